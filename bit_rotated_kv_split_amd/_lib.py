@@ -1,0 +1,197 @@
+"""ctypes binding of liboscar.so (the C ABI declared in include/oscar.h).
+
+Argument marshalling only: every computation runs in the HIP library.  The
+functions carry the C names and raise :class:`OscarError` on a non-zero
+return code.  Tensors are torch tensors on the GPU (or raw device addresses
+as ints); the library neither keeps nor frees them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liboscar.so")
+
+OSCAR_OK = 0
+OSCAR_EINVAL = 1
+OSCAR_EUNSUPPORTED = 2
+OSCAR_EHIP = 3
+
+HEAD_DIM = 128
+PAGE = 64
+SINK = 64
+RECENT = 256
+
+
+class OscarError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"oscar error {code}: {msg}")
+        self.code = code
+
+
+class OscarDims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("sink_len", ctypes.c_int32),
+                ("recent_len", ctypes.c_int32)]
+
+
+class OscarRotation(ctypes.Structure):
+    _fields_ = [("r_k", ctypes.c_void_p), ("r_v", ctypes.c_void_p),
+                ("clip_k", ctypes.c_void_p), ("clip_v", ctypes.c_void_p)]
+
+
+class OscarCache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p),
+                ("recent_k", ctypes.c_void_p), ("recent_v", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("max_pages_per_req", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("batch", ctypes.c_int32)]
+
+
+# (name, restype, argtypes) of every exported function
+_P = ctypes.POINTER
+_SIGS = [
+    ("oscar_block_bytes", ctypes.c_size_t, [ctypes.c_int32]),
+    ("oscar_kv_demote", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_kv_fill_history", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_history_splits", ctypes.c_int32, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
+    ("oscar_decode_workspace_bytes", ctypes.c_size_t, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
+    ("oscar_decode_attn", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
+    ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
+    ("oscar_set_history_events", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_last_error", ctypes.c_char_p, []),
+]
+EXPORTED = [s[0] for s in _SIGS]
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise OscarError(OSCAR_EHIP, f"{LIB_PATH} is missing; run "
+                                 "`python -m bit_rotated_kv_split_amd.build` first")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, res, args in _SIGS:
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+        return _lib
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != OSCAR_OK:
+        raise OscarError(rc, lib().oscar_last_error().decode())
+
+
+# ------------------------------------------------------------------ structs
+
+def make_dims(num_q_heads: int, num_kv_heads: int, group_size: int, head_dim: int = HEAD_DIM,
+              page_size: int = PAGE, sink_len: int = SINK, recent_len: int = RECENT) -> OscarDims:
+    return OscarDims(num_q_heads, num_kv_heads, head_dim, group_size, page_size, sink_len, recent_len)
+
+
+def make_rotation(r_k, r_v, clip_k, clip_v) -> OscarRotation:
+    rot = OscarRotation(_ptr(r_k), _ptr(r_v), _ptr(clip_k), _ptr(clip_v))
+    rot._keep = (r_k, r_v, clip_k, clip_v)
+    return rot
+
+
+def make_cache(pages, n_pages: int, sink_k, sink_v, recent_k, recent_v, page_table,
+               max_pages_per_req: int, seq_lens, batch: int) -> OscarCache:
+    c = OscarCache(_ptr(pages), n_pages, _ptr(sink_k), _ptr(sink_v), _ptr(recent_k),
+                   _ptr(recent_v), _ptr(page_table), max_pages_per_req, _ptr(seq_lens), batch)
+    c._keep = (pages, sink_k, sink_v, recent_k, recent_v, page_table, seq_lens)
+    return c
+
+
+# ------------------------------------------------------------- entry points
+
+def oscar_block_bytes(group_size: int) -> int:
+    return lib().oscar_block_bytes(group_size)
+
+
+def oscar_kv_demote(dims, rot, cache, k_new, v_new, stream=None) -> None:
+    _check(lib().oscar_kv_demote(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
+                                 _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def oscar_kv_fill_history(dims, rot, cache, request: int, hist_begin: int, n_tokens: int,
+                          k_tokens, v_tokens, stream=None) -> None:
+    _check(lib().oscar_kv_fill_history(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
+                                       request, hist_begin, n_tokens, _ptr(k_tokens),
+                                       _ptr(v_tokens), _stream(stream)))
+
+
+def oscar_history_splits(dims, batch: int, max_seq_len: int) -> int:
+    return lib().oscar_history_splits(ctypes.byref(dims), batch, max_seq_len)
+
+
+def oscar_decode_workspace_bytes(dims, batch: int, max_seq_len: int) -> int:
+    return lib().oscar_decode_workspace_bytes(ctypes.byref(dims), batch, max_seq_len)
+
+
+def oscar_decode_attn(dims, rot, cache, q, max_seq_len: int, workspace, workspace_bytes: int,
+                      stream=None) -> None:
+    _check(lib().oscar_decode_attn(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
+                                   _ptr(q), max_seq_len, _ptr(workspace), workspace_bytes,
+                                   _stream(stream)))
+
+
+def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspace_bytes: int,
+                    out, lse_out=None, stream=None) -> None:
+    _check(lib().oscar_merge_lse(ctypes.byref(dims), ctypes.byref(rot), batch, max_seq_len,
+                                 _ptr(workspace), workspace_bytes, _ptr(out), _ptr(lse_out),
+                                 _stream(stream)))
+
+
+def oscar_set_history_kernel(kind: int) -> int:
+    prev = lib().oscar_set_history_kernel(kind)
+    if prev < 0:
+        raise OscarError(OSCAR_EINVAL, f"invalid history kernel {kind}")
+    return prev
+
+
+def oscar_set_history_events(before, after) -> None:
+    b = None if before is None else before.cuda_event if hasattr(before, "cuda_event") else before
+    a = None if after is None else after.cuda_event if hasattr(after, "cuda_event") else after
+    _check(lib().oscar_set_history_events(b, a))
+
+
+def oscar_last_error() -> str:
+    return lib().oscar_last_error().decode()

@@ -1,0 +1,241 @@
+// C ABI entry points of the OSCAR decode path: argument checks, workspace
+// layout and launch order.  Every compute step runs in the HIP kernels of
+// demote.hip, decode.hip and decode_mfma.hip.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+#include <string>
+
+#include "oscar_device.h"
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+thread_local std::string g_error;
+thread_local void* g_ev_before = nullptr;
+thread_local void* g_ev_after = nullptr;
+std::atomic<int> g_hist_kernel{0};
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(OSCAR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_dims(const oscar_dims* d) {
+  if (d == nullptr) return fail(OSCAR_EINVAL, "dims is NULL");
+  if (d->head_dim != kDim) return fail(OSCAR_EUNSUPPORTED, "head_dim %d unsupported (128 only)", d->head_dim);
+  if (d->page_size != kPage) return fail(OSCAR_EUNSUPPORTED, "page_size %d unsupported (64 only)", d->page_size);
+  if (d->sink_len != kSink || d->recent_len != kRecent)
+    return fail(OSCAR_EUNSUPPORTED, "sink/recent %d/%d unsupported (64/256 only)", d->sink_len, d->recent_len);
+  if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128)
+    return fail(OSCAR_EUNSUPPORTED, "group_size %d unsupported (32, 64, 128)", d->group_size);
+  if (d->num_kv_heads <= 0 || d->num_q_heads <= 0)
+    return fail(OSCAR_EINVAL, "head counts must be positive (%d q, %d kv)", d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(OSCAR_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads, d->num_kv_heads);
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g > 8) return fail(OSCAR_EUNSUPPORTED, "query heads per KV head %d unsupported (<= 8)", g);
+  return OSCAR_OK;
+}
+
+int check_rot(const oscar_rotation* r) {
+  if (r == nullptr) return fail(OSCAR_EINVAL, "rotation is NULL");
+  if (!r->r_k || !r->r_v || !r->clip_k || !r->clip_v)
+    return fail(OSCAR_EINVAL, "rotation has a NULL pointer");
+  return OSCAR_OK;
+}
+
+int check_cache(const oscar_cache* c, bool need_pages) {
+  if (c == nullptr) return fail(OSCAR_EINVAL, "cache is NULL");
+  if (c->batch < 0) return fail(OSCAR_EINVAL, "batch %d < 0", c->batch);
+  if (c->batch == 0) return OSCAR_OK;
+  if (!c->sink_k || !c->sink_v || !c->recent_k || !c->recent_v || !c->seq_lens)
+    return fail(OSCAR_EINVAL, "cache has a NULL sink/recent/seq_lens pointer");
+  if (need_pages) {
+    if (!c->pages || !c->page_table) return fail(OSCAR_EINVAL, "cache has a NULL pages/page_table pointer");
+    if (c->max_pages_per_req <= 0 || c->n_pages <= 0)
+      return fail(OSCAR_EINVAL, "max_pages_per_req %d / n_pages %lld must be positive",
+                  c->max_pages_per_req, static_cast<long long>(c->n_pages));
+  }
+  return OSCAR_OK;
+}
+
+int pages_for(int32_t max_seq_len) {
+  const int n_hist = max_seq_len > kBf16Tokens ? max_seq_len - kBf16Tokens : 0;
+  return (n_hist + kPage - 1) / kPage;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len) {
+  WsLayout w;
+  const int pages = pages_for(max_seq_len);
+  const int pairs = batch * d.num_kv_heads;
+  // Enough workgroups to fill 256 compute units several times over, without
+  // making a split shorter than 8 pages.
+  constexpr int kTargetWorkgroups = 2048;
+  int splits = 1;
+  if (pages > 0 && pairs > 0) {
+    splits = (kTargetWorkgroups + pairs - 1) / pairs;
+    const int max_splits = (pages + 7) / 8;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    const int pps = (pages + splits - 1) / splits;
+    splits = (pages + pps - 1) / pps;
+    w.pages_per_split = pps;
+  }
+  w.splits = splits;
+  const size_t heads = static_cast<size_t>(batch) * d.num_q_heads;
+  size_t off = 0;
+  w.off_qrot = off;
+  off = align256(off + heads * kDim * sizeof(float));
+  w.off_qsum = off;
+  off = align256(off + heads * 4 * sizeof(float));
+  w.off_qpack = off;
+  off = align256(off + static_cast<size_t>(batch) * d.num_kv_heads * kQPackBytes);
+  w.off_po = off;
+  off = align256(off + heads * (splits + 1) * kDim * sizeof(float));
+  w.off_plse = off;
+  off = align256(off + heads * (splits + 1) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+}  // namespace oscar
+
+using namespace oscar;
+
+extern "C" {
+
+size_t oscar_block_bytes(int32_t group_size) {
+  if (group_size != 32 && group_size != 64 && group_size != 128) return 0;
+  return static_cast<size_t>(block_bytes(group_size));
+}
+
+const char* oscar_last_error(void) { return g_error.c_str(); }
+
+int oscar_set_history_kernel(int kind) {
+  if (kind < 0 || kind > 2) return -1;
+  return g_hist_kernel.exchange(kind);
+}
+
+int oscar_set_history_events(void* before, void* after) {
+  g_ev_before = before;
+  g_ev_after = after;
+  return OSCAR_OK;
+}
+
+int oscar_kv_demote(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                    const uint16_t* k_new, const uint16_t* v_new, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(OSCAR_EINVAL, "k_new and v_new must both be set or both be NULL");
+  if (cache->batch == 0) return OSCAR_OK;
+  const hipError_t e = launch_demote(*dims, *rot, *cache, k_new, v_new, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "demote launch");
+  return OSCAR_OK;
+}
+
+int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
+                          const oscar_cache* cache, int32_t request, int32_t hist_begin,
+                          int32_t n_tokens, const uint16_t* k_tokens, const uint16_t* v_tokens,
+                          void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
+  if (request < 0 || request >= cache->batch)
+    return fail(OSCAR_EINVAL, "request %d outside batch %d", request, cache->batch);
+  if (hist_begin < 0 || n_tokens < 0)
+    return fail(OSCAR_EINVAL, "hist_begin %d / n_tokens %d must be >= 0", hist_begin, n_tokens);
+  if (n_tokens == 0) return OSCAR_OK;
+  if (k_tokens == nullptr || v_tokens == nullptr) return fail(OSCAR_EINVAL, "token pointers are NULL");
+  const int64_t last_page = (static_cast<int64_t>(hist_begin) + n_tokens - 1) / kPage;
+  if (last_page >= cache->max_pages_per_req)
+    return fail(OSCAR_EINVAL, "history index %lld beyond max_pages_per_req %d",
+                static_cast<long long>(hist_begin) + n_tokens - 1, cache->max_pages_per_req);
+  const hipError_t e = launch_fill(*dims, *rot, *cache, request, hist_begin, n_tokens, k_tokens,
+                                   v_tokens, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  return OSCAR_OK;
+}
+
+int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims) || batch < 0 || max_seq_len < 0) return -1;
+  return workspace_layout(*dims, batch, max_seq_len).splits;
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims) || batch < 0 || max_seq_len < 0) return 0;
+  return workspace_layout(*dims, batch, max_seq_len).total;
+}
+
+int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                      const uint16_t* q, int32_t max_seq_len, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (cache->batch == 0) return OSCAR_OK;
+  if (q == nullptr || workspace == nullptr) return fail(OSCAR_EINVAL, "q or workspace is NULL");
+  if (pages_for(max_seq_len) > cache->max_pages_per_req)
+    return fail(OSCAR_EINVAL, "max_seq_len %d needs %d pages > max_pages_per_req %d", max_seq_len,
+                pages_for(max_seq_len), cache->max_pages_per_req);
+  const WsLayout lay = workspace_layout(*dims, cache->batch, max_seq_len);
+  if (workspace_bytes < lay.total)
+    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
+  hipError_t e = launch_qrot(a, s);
+  if (e != hipSuccess) return hip_fail(e, "query rotation launch");
+  const int kind = g_hist_kernel.load();
+  const bool use_mfma = kind == 2 || (kind == 0 && hist_mfma_supported(*dims));
+  if (kind == 2 && !hist_mfma_supported(*dims))
+    return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
+  const bool timed = g_ev_before != nullptr && g_ev_after != nullptr;
+  if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(g_ev_before), s)) != hipSuccess)
+    return hip_fail(e, "event record");
+  e = use_mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
+  if (e != hipSuccess) return hip_fail(e, "history launch");
+  if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(g_ev_after), s)) != hipSuccess)
+    return hip_fail(e, "event record");
+  e = launch_bf16(a, s);
+  if (e != hipSuccess) return hip_fail(e, "bf16 launch");
+  return OSCAR_OK;
+}
+
+int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,
+                    int32_t max_seq_len, const void* workspace, size_t workspace_bytes, float* out,
+                    float* lse_out, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_rot(rot))) return rc;
+  if (batch < 0 || max_seq_len < 1) return fail(OSCAR_EINVAL, "batch %d / max_seq_len %d invalid", batch, max_seq_len);
+  if (batch == 0) return OSCAR_OK;
+  if (workspace == nullptr || out == nullptr) return fail(OSCAR_EINVAL, "workspace or out is NULL");
+  const WsLayout lay = workspace_layout(*dims, batch, max_seq_len);
+  if (workspace_bytes < lay.total)
+    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  const hipError_t e = launch_merge(*dims, *rot, batch, static_cast<const uint8_t*>(workspace), lay,
+                                    out, lse_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return OSCAR_OK;
+}
+
+}  // extern "C"

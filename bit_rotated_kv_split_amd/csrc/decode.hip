@@ -1,0 +1,583 @@
+// Decode attention kernels over the three-region cache (page
+// "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务", section
+// "OSCAR的另一个关键点是": an INT2 kernel over history, a bf16 kernel over
+// sink and recent, and an online-softmax merge of the two).
+//
+//   qrot_kernel      q . R_K per (request, head), pre-scaled by log2(e)/sqrt(d),
+//                    plus the per-group sums the zero-point term needs and
+//                    the int8 limb operands of the matrix-core kernel.
+//   hist_valu_kernel split-K over history pages on the vector ALU: lane =
+//                    token for q.k, lane = channel pair for p.v.
+//   bf16_kernel      sink + recent tokens with the unrotated query.
+//   merge_kernel     LSE merge of the history splits, . R_V^T, merge with the
+//                    bf16 partial.
+//
+// The factored score of a history token is
+//   q_rot . k_hat = sum_groups ( scale * (q_rot . code) + zero * sum(q_rot) )
+// and the value side accumulates (p * scale) * code plus (p * zero) per group,
+// so dequantized values are never formed element by element.
+#include <math.h>
+
+#include "oscar_device.h"
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+// Largest magnitude of the int8-limb fixed-point query: three signed base-256
+// digits represent every integer of magnitude <= 2^23 - 2^17 with digit 2 in
+// [-127, 126].
+constexpr float kQFixMax = 8257536.0f;
+
+template <int GQ>
+__global__ void __launch_bounds__(128)
+qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int hq, int hkv, int G,
+            float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int k = threadIdx.x;
+  __shared__ float qs[GQ][kDim];
+  __shared__ float qr[GQ][kDim];
+  __shared__ float qmax[GQ];
+  const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) qs[h][k] = bf16_to_f32(q[(head0 + h) * kDim + k]);
+  __syncthreads();
+  const float* r = r_k + static_cast<size_t>(kvh) * kDim * kDim;
+  float acc[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
+  for (int i = 0; i < kDim; ++i) {
+    const float rik = r[i * kDim + k];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) acc[h] = __builtin_fmaf(qs[h][i], rik, acc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const float v = acc[h] * kScoreScaleLog2;
+    qr[h][k] = v;
+    qrot[(head0 + h) * kDim + k] = v;
+  }
+  __syncthreads();
+  // per-group sums (thread k < GQ*4 handles (head, group of the 4 possible))
+  if (k < GQ * 4) {
+    const int h = k >> 2, gi = k & 3;
+    const int ng = kDim / G;
+    float s = 0.f;
+    if (gi < ng)
+      for (int j = 0; j < G; ++j) s += qr[h][gi * G + j];
+    qsum[(head0 + h) * 4 + gi] = s;
+  }
+  if (k < GQ) {
+    float m = 0.f;
+    for (int j = 0; j < kDim; ++j) m = fmaxf(m, fabsf(qr[k][j]));
+    qmax[k] = m;
+  }
+  __syncthreads();
+  // int8 limb operands: row = 4*h + limb (limb 3 = zero pad), 32 rows; for
+  // channel half hf and lane group kg, byte e = 4*j + b2 of the row holds
+  // channel 16*(4*hf + kg) + 4*b2 + j.
+  uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
+  for (int idx = k; idx < 2 * 4 * kQPackRows * 16; idx += kDim) {
+    const int e = idx & 15;
+    const int row = (idx >> 4) & (kQPackRows - 1);
+    const int kg = (idx >> 9) & 3;
+    const int hf = idx >> 11;
+    const int h = row >> 2, limb = row & 3;
+    int8_t val = 0;
+    if (h < GQ && limb < 3) {
+      const int ch = 16 * (4 * hf + kg) + 4 * (e & 3) + (e >> 2);
+      const float sc = qmax[h] > 0.f ? qmax[h] / kQFixMax : 1.f;
+      const int qi = static_cast<int>(rintf(qr[h][ch] / sc));
+      const int d0 = ((qi + 128) & 255) - 128;
+      const int q1 = (qi - d0) >> 8;
+      const int d1 = ((q1 + 128) & 255) - 128;
+      const int d2 = (q1 - d1) >> 8;
+      val = static_cast<int8_t>(limb == 0 ? d0 : (limb == 1 ? d1 : d2));
+    }
+    qp[idx] = static_cast<uint8_t>(val);
+  }
+  if (k < 8) {
+    float* sc = reinterpret_cast<float*>(qp + kQPackOperandBytes);
+    sc[k] = (k < GQ && qmax[k] > 0.f) ? qmax[k] / kQFixMax : 0.f;
+  }
+}
+
+struct HistParams {
+  const uint8_t* pages;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const float* qrot;
+  const float* qsum;
+  float* po;
+  float* plse;
+  int32_t max_pages;
+  int32_t hkv;
+  int32_t hq;
+  int32_t splits;
+  int32_t pages_per_split;
+};
+
+// Vector-ALU history kernel.  Workgroup = (split, KV head, request), four
+// waves; wave w takes pages p0+w, p0+w+4, ... of the split with its own
+// online-softmax state, and the four states are merged at the end.
+template <int GQ, int G>
+__global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
+  constexpr int NG = kDim / G;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float q_s[GQ][kDim];
+  __shared__ float qsum_s[GQ][4];
+  __shared__ float w_s[4][GQ][NG][kPage];
+  __shared__ float st_m[4][GQ], st_l[4][GQ];
+  __shared__ float st_acc[4][GQ][kDim];
+
+  const int L = a.seq_lens[b];
+  const int n_hist = max(0, L - kBf16Tokens);
+  const int n_pages = (n_hist + kPage - 1) / kPage;
+  const int p0 = split * a.pages_per_split;
+  const int p1 = min(p0 + a.pages_per_split, n_pages);
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * GQ;
+  for (int i = tid; i < GQ * kDim; i += 256) q_s[i / kDim][i % kDim] = a.qrot[head0 * kDim + i];
+  if (tid < GQ * 4) qsum_s[tid >> 2][tid & 3] = a.qsum[head0 * 4 + tid];
+  __syncthreads();
+
+  float m[GQ], l[GQ], acc0[GQ], acc1[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+    acc0[h] = 0.f;
+    acc1[h] = 0.f;
+  }
+  const int c0 = lane, c1 = lane + 64;
+  for (int p = p0 + wave; p < p1; p += 4) {
+    const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + p];
+    const uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.hkv + kvh) * block_bytes(G);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(blk);
+    const uint16_t* szk = reinterpret_cast<const uint16_t*>(blk + kCodesBytes);
+    const uint16_t* szv = szk + kPage * NG * 2;
+    const int t = lane;
+    const bool valid = p * kPage + t < n_hist;
+    const int qo = qk_order(t);
+
+    // scores: lane = token slot t
+    float dot[GQ][NG];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) dot[h][gi] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t w = words[d * 64 + qo];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float code = static_cast<float>((w >> (2 * i)) & 3u);
+        const int ch = 16 * d + i;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) dot[h][ch / G] = __builtin_fmaf(q_s[h][ch], code, dot[h][ch / G]);
+      }
+    }
+    float sc[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const float ks = bf16_to_f32(szk[(qo * NG + gi) * 2]);
+        const float kz = bf16_to_f32(szk[(qo * NG + gi) * 2 + 1]);
+        s += ks * dot[h][gi] + kz * qsum_s[h][gi];
+      }
+      sc[h] = valid ? s : -INFINITY;
+    }
+    // online softmax over the page
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float pm = wave_max(sc[h]);
+      const float mn = fmaxf(m[h], pm);
+      const float alpha = exp2f(m[h] - mn);
+      const float pr = valid ? exp2f(sc[h] - mn) : 0.f;
+      l[h] = l[h] * alpha + wave_sum(pr);
+      m[h] = mn;
+      acc0[h] *= alpha;
+      acc1[h] *= alpha;
+      sc[h] = pr;
+    }
+    // value weights: p * scale per (head, group, token); zero-point sums
+    float u[GQ][NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float vs = valid ? bf16_to_f32(szv[(qo * NG + gi) * 2]) : 0.f;
+      const float vz = valid ? bf16_to_f32(szv[(qo * NG + gi) * 2 + 1]) : 0.f;
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        w_s[wave][h][gi][t] = sc[h] * vs;
+        u[h][gi] = wave_sum(sc[h] * vz);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // p . v: lane owns channels c0 and c1
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = half ? c1 : c0;
+      const int gi = c / G;
+      float accv[GQ];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) accv[h] = 0.f;
+#pragma unroll
+      for (int wq = 0; wq < 4; ++wq) {
+        const uint32_t w = words[512 + v_word_index(c, wq)];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float code = static_cast<float>((w >> (2 * i)) & 3u);
+#pragma unroll
+          for (int h = 0; h < GQ; ++h)
+            accv[h] = __builtin_fmaf(w_s[wave][h][gi][16 * wq + i], code, accv[h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        if (half) acc1[h] += accv[h] + u[h][gi];
+        else acc0[h] += accv[h] + u[h][gi];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // merge the four wave states
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    if (lane == 0) {
+      st_m[wave][h] = m[h];
+      st_l[wave][h] = l[h];
+    }
+    st_acc[wave][h][c0] = acc0[h];
+    st_acc[wave][h][c1] = acc1[h];
+  }
+  __syncthreads();
+  for (int job = tid; job < GQ * kDim; job += 256) {
+    const int h = job / kDim, c = job % kDim;
+    float mx = -INFINITY;
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, st_m[w][h]);
+    float lt = 0.f, at = 0.f;
+    if (mx != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        if (st_m[w][h] == -INFINITY) continue;
+        const float f = exp2f(st_m[w][h] - mx);
+        lt += st_l[w][h] * f;
+        at += st_acc[w][h][c] * f;
+      }
+    }
+    const size_t pidx = (head0 + h) * (a.splits + 1) + split;
+    a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
+    if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+struct Bf16Params {
+  const uint16_t* q;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  const uint16_t* recent_k;
+  const uint16_t* recent_v;
+  const int32_t* seq_lens;
+  float* po;
+  float* plse;
+  int32_t hkv;
+  int32_t hq;
+  int32_t splits;
+};
+
+// Sink + recent: 320 virtual slots (64 sink, 256 ring) in five chunks of 64;
+// wave w takes chunks w and w+4.  Lane = token for q.k, lane = channel pair
+// for p.v.
+template <int GQ>
+__global__ void __launch_bounds__(256) bf16_kernel(Bf16Params a) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float q_s[GQ][kDim];
+  __shared__ float p_s[4][GQ][kPage];
+  __shared__ float st_m[4][GQ], st_l[4][GQ];
+  __shared__ float st_acc[4][GQ][kDim];
+  const int L = a.seq_lens[b];
+  const int n_sink = min(L, kSink);
+  const int n_recent = min(max(L - kSink, 0), kRecent);
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * GQ;
+  for (int i = tid; i < GQ * kDim; i += 256)
+    q_s[i / kDim][i % kDim] = bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2;
+  __syncthreads();
+  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
+  const uint16_t* sk = a.sink_k + kv0 * kSink * kDim;
+  const uint16_t* sv = a.sink_v + kv0 * kSink * kDim;
+  const uint16_t* rk = a.recent_k + kv0 * kRecent * kDim;
+  const uint16_t* rv = a.recent_v + kv0 * kRecent * kDim;
+  float m[GQ], l[GQ], acc0[GQ], acc1[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+    acc0[h] = 0.f;
+    acc1[h] = 0.f;
+  }
+  for (int chunk = wave; chunk < 5; chunk += 4) {
+    const bool is_sink = chunk == 0;
+    const int n_valid = is_sink ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
+    if (n_valid == 0) continue;   // uniform across the wave
+    const uint16_t* kb = is_sink ? sk : rk + (chunk - 1) * kPage * kDim;
+    const uint16_t* vb = is_sink ? sv : rv + (chunk - 1) * kPage * kDim;
+    const int t = lane;
+    const bool valid = t < n_valid;
+    float sc[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
+    if (valid) {
+      const uint4* row = reinterpret_cast<const uint4*>(kb + t * kDim);
+#pragma unroll 4
+      for (int v8 = 0; v8 < kDim / 8; ++v8) {
+        const uint4 w = row[v8];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = __uint_as_float(ws[j] << 16);
+          const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
+          const int ch = v8 * 8 + 2 * j;
+#pragma unroll
+          for (int h = 0; h < GQ; ++h) {
+            sc[h] = __builtin_fmaf(q_s[h][ch], lo, sc[h]);
+            sc[h] = __builtin_fmaf(q_s[h][ch + 1], hi, sc[h]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float s = valid ? sc[h] : -INFINITY;
+      const float pm = wave_max(s);
+      const float mn = fmaxf(m[h], pm);
+      const float alpha = exp2f(m[h] - mn);
+      const float pr = valid ? exp2f(s - mn) : 0.f;
+      l[h] = l[h] * alpha + wave_sum(pr);
+      m[h] = mn;
+      acc0[h] *= alpha;
+      acc1[h] *= alpha;
+      p_s[wave][h][t] = pr;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int tt = 0; tt < n_valid; ++tt) {
+      const float v0 = bf16_to_f32(vb[tt * kDim + lane]);
+      const float v1 = bf16_to_f32(vb[tt * kDim + lane + 64]);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        acc0[h] = __builtin_fmaf(p_s[wave][h][tt], v0, acc0[h]);
+        acc1[h] = __builtin_fmaf(p_s[wave][h][tt], v1, acc1[h]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    if (lane == 0) {
+      st_m[wave][h] = m[h];
+      st_l[wave][h] = l[h];
+    }
+    st_acc[wave][h][lane] = acc0[h];
+    st_acc[wave][h][lane + 64] = acc1[h];
+  }
+  __syncthreads();
+  for (int job = tid; job < GQ * kDim; job += 256) {
+    const int h = job / kDim, c = job % kDim;
+    float mx = -INFINITY;
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, st_m[w][h]);
+    float lt = 0.f, at = 0.f;
+    if (mx != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        if (st_m[w][h] == -INFINITY) continue;
+        const float f = exp2f(st_m[w][h] - mx);
+        lt += st_l[w][h] * f;
+        at += st_acc[w][h][c] * f;
+      }
+    }
+    const size_t pidx = (head0 + h) * (a.splits + 1) + a.splits;
+    a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
+    if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// LSE merge: workgroup = (KV head, request), thread = channel.
+template <int GQ>
+__global__ void __launch_bounds__(128)
+merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
+             const float* __restrict__ r_v, int hq, int splits, float* __restrict__ out,
+             float* __restrict__ lse_out) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int k = threadIdx.x;
+  __shared__ float orot[GQ][kDim];
+  __shared__ float lse_h[GQ];
+  const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const size_t base = (head0 + h) * (splits + 1);
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, plse[base + s]);
+    float den = 0.f, o = 0.f;
+    if (mx != -INFINITY) {
+      for (int s = 0; s < splits; ++s) {
+        const float ls = plse[base + s];
+        if (ls == -INFINITY) continue;
+        const float w = expf(ls - mx);
+        den += w;
+        o += w * po[(base + s) * kDim + k];
+      }
+    }
+    orot[h][k] = den > 0.f ? o / den : 0.f;
+    if (k == 0) lse_h[h] = den > 0.f ? mx + logf(den) : -INFINITY;
+  }
+  __syncthreads();
+  // history output back to the model domain: x_i = sum_k y_k R_V[i][k]
+  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + k) * kDim);
+  float oh[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) oh[h] = 0.f;
+#pragma unroll 2
+  for (int c4 = 0; c4 < kDim / 4; ++c4) {
+    const float4 rr = rrow[c4];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 0], rr.x, oh[h]);
+      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 1], rr.y, oh[h]);
+      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 2], rr.z, oh[h]);
+      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 3], rr.w, oh[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const size_t pb = (head0 + h) * (splits + 1) + splits;
+    const float lb = plse[pb];
+    const float ob = po[pb * kDim + k];
+    const float lh = lse_h[h];
+    const float mx = fmaxf(lh, lb);
+    const float wh = lh == -INFINITY ? 0.f : expf(lh - mx);
+    const float wb = lb == -INFINITY ? 0.f : expf(lb - mx);
+    const float den = wh + wb;
+    out[(head0 + h) * kDim + k] = den > 0.f ? (wh * oh[h] + wb * ob) / den : 0.f;
+    if (lse_out != nullptr && k == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
+  }
+}
+
+template <template <int> class F, typename... Args>
+hipError_t dispatch_gq(int gq, Args... args) {
+  switch (gq) {
+    case 1: return F<1>::run(args...);
+    case 2: return F<2>::run(args...);
+    case 3: return F<3>::run(args...);
+    case 4: return F<4>::run(args...);
+    case 5: return F<5>::run(args...);
+    case 6: return F<6>::run(args...);
+    case 7: return F<7>::run(args...);
+    default: return F<8>::run(args...);
+  }
+}
+
+template <int GQ>
+struct QrotRun {
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    const oscar_dims& d = *a.dims;
+    const dim3 grid(d.num_kv_heads, a.cache->batch);
+    qrot_kernel<GQ><<<grid, 128, 0, s>>>(
+        a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
+        reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
+        a.ws + a.lay.off_qpack);
+    return hipGetLastError();
+  }
+};
+
+template <int GQ>
+struct HistValuRun {
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    const oscar_dims& d = *a.dims;
+    HistParams p;
+    p.pages = a.cache->pages;
+    p.page_table = a.cache->page_table;
+    p.seq_lens = a.cache->seq_lens;
+    p.qrot = reinterpret_cast<const float*>(a.ws + a.lay.off_qrot);
+    p.qsum = reinterpret_cast<const float*>(a.ws + a.lay.off_qsum);
+    p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
+    p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+    p.max_pages = a.cache->max_pages_per_req;
+    p.hkv = d.num_kv_heads;
+    p.hq = d.num_q_heads;
+    p.splits = a.lay.splits;
+    p.pages_per_split = a.lay.pages_per_split;
+    const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
+    switch (d.group_size) {
+      case 32: hist_valu_kernel<GQ, 32><<<grid, 256, 0, s>>>(p); break;
+      case 64: hist_valu_kernel<GQ, 64><<<grid, 256, 0, s>>>(p); break;
+      default: hist_valu_kernel<GQ, 128><<<grid, 256, 0, s>>>(p); break;
+    }
+    return hipGetLastError();
+  }
+};
+
+template <int GQ>
+struct Bf16Run {
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) {
+    const oscar_dims& d = *a.dims;
+    Bf16Params p;
+    p.q = a.q;
+    p.sink_k = a.cache->sink_k;
+    p.sink_v = a.cache->sink_v;
+    p.recent_k = a.cache->recent_k;
+    p.recent_v = a.cache->recent_v;
+    p.seq_lens = a.cache->seq_lens;
+    p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
+    p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+    p.hkv = d.num_kv_heads;
+    p.hq = d.num_q_heads;
+    p.splits = a.lay.splits;
+    const dim3 grid(d.num_kv_heads, a.cache->batch);
+    bf16_kernel<GQ><<<grid, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
+};
+
+template <int GQ>
+struct MergeRun {
+  static hipError_t run(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
+                        const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
+                        hipStream_t s) {
+    const dim3 grid(d.num_kv_heads, batch);
+    merge_kernel<GQ><<<grid, 128, 0, s>>>(reinterpret_cast<const float*>(ws + lay.off_po),
+                                          reinterpret_cast<const float*>(ws + lay.off_plse),
+                                          rot.r_v, d.num_q_heads, lay.splits, out, lse_out);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
+
+hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s) {
+  return dispatch_gq<QrotRun>(a.dims->num_q_heads / a.dims->num_kv_heads, a, s);
+}
+
+hipError_t launch_hist_valu(const DecodeArgs& a, hipStream_t s) {
+  return dispatch_gq<HistValuRun>(a.dims->num_q_heads / a.dims->num_kv_heads, a, s);
+}
+
+hipError_t launch_bf16(const DecodeArgs& a, hipStream_t s) {
+  return dispatch_gq<Bf16Run>(a.dims->num_q_heads / a.dims->num_kv_heads, a, s);
+}
+
+hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
+                        const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
+                        hipStream_t s) {
+  return dispatch_gq<MergeRun>(d.num_q_heads / d.num_kv_heads, d, rot, batch, ws, lay, out,
+                               lse_out, s);
+}
+
+}  // namespace oscar

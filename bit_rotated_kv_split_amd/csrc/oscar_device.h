@@ -1,0 +1,59 @@
+// Device helpers shared by the OSCAR HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kDim = 128;        // head dimension
+constexpr int kPage = 64;        // history slots per page
+constexpr int kSink = 64;        // bf16 sink tokens
+constexpr int kRecent = 256;     // bf16 recent window
+constexpr int kBf16Tokens = kSink + kRecent;
+constexpr int kKWordsBytes = 2048;   // key words of one block
+constexpr int kCodesBytes = 4096;    // key + value words of one block
+
+__host__ __device__ constexpr int block_bytes(int G) { return kCodesBytes + 512 * (kDim / G); }
+
+// Position of slot t in the key-word rows and in the scale/zero tables:
+// the order in which the matrix-core history kernel's lanes consume tokens.
+__host__ __device__ __forceinline__ int qk_order(int t) {
+  return 16 * (t >> 4) + 4 * (t & 3) + ((t >> 2) & 3);
+}
+
+// Word index (within the value words) of channel c, token group w (16 slots).
+__host__ __device__ __forceinline__ int v_word_index(int c, int w) {
+  return (c >> 6) * 256 + (w * 16 + (c & 15)) * 4 + ((c >> 4) & 3);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16_rne(x)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// log2(e) / sqrt(128): scores are kept in base-2 units inside the kernels.
+constexpr float kScoreScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace oscar

@@ -1,0 +1,67 @@
+// Host-side declarations shared between the OSCAR entry points and the
+// kernel launchers.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/oscar.h"
+
+namespace oscar {
+
+// Workspace layout of one decode call (offsets in bytes, 256-aligned).
+struct WsLayout {
+  int32_t splits = 1;           // history splits S
+  int32_t pages_per_split = 0;  // pages one split covers
+  size_t off_qrot = 0;          // float [B][Hq][128]: R_K-rotated query * log2(e)/sqrt(128)
+  size_t off_qsum = 0;          // float [B][Hq][4]: per-group sums of that query
+  size_t off_qpack = 0;         // matrix-core operands, kQPackBytes per (b, kv head)
+  size_t off_po = 0;            // float [B][Hq][S+1][128] partial outputs (S = bf16 partial)
+  size_t off_plse = 0;          // float [B][Hq][S+1] partial log-sum-exp (natural log)
+  size_t total = 0;
+};
+
+// Matrix-core query operand of one (request, KV head): for each channel half
+// (64 channels) and lane group, 32 rows x 16 int8 limb bytes, then per-head
+// dequantization scales.
+constexpr int kQPackRows = 32;
+constexpr size_t kQPackOperandBytes = 2 * 4 * kQPackRows * 16;  // 4096
+constexpr size_t kQPackBytes = kQPackOperandBytes + 256;
+
+WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len);
+
+struct DemoteArgs {
+  const float* r;        // [Hkv][128][128], K or V per blockIdx.z
+  const float* clip;
+  uint8_t* pages;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t hkv;
+};
+
+hipError_t launch_demote(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
+                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
+hipError_t launch_fill(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
+                       int32_t request, int32_t hist_begin, int32_t n_tokens,
+                       const uint16_t* k_tokens, const uint16_t* v_tokens, hipStream_t s);
+
+struct DecodeArgs {
+  const oscar_dims* dims;
+  const oscar_rotation* rot;
+  const oscar_cache* cache;
+  const uint16_t* q;
+  uint8_t* ws;
+  WsLayout lay;
+};
+
+hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_hist_valu(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s);
+bool hist_mfma_supported(const oscar_dims& d);
+hipError_t launch_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
+                        const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
+                        hipStream_t s);
+
+}  // namespace oscar

@@ -1,0 +1,186 @@
+/*
+ * oscar.h - C ABI of the OSCAR INT2 KV-cache decode path on MI355X (gfx950).
+ *
+ * OSCAR keeps each request's KV cache in three regions (page "Together AI
+ * 开源 OSCAR：一种面向长上下文 LLM 服务的注意力感知 2 位 KV 缓存量化系统",
+ * section "服务系统：混合精度缓存布局"; page "超越TurboQuant：Together AI把
+ * 2-bit KV Cache推向真实服务", section "OSCAR的另一个关键点是"):
+ *   - sink:    the first 64 tokens, bf16, unrotated;
+ *   - history: every token between, stored rotated (key as k.R_K, value as
+ *              v.R_V), clipped and quantized to 2-bit codes with a bf16 scale
+ *              and zero point per group of G channels, 4 codes per byte;
+ *   - recent:  the last 256 tokens, bf16, unrotated.
+ * A decode step appends the new token to the recent window, demotes the
+ * oldest recent token into history, runs attention over history and over
+ * the bf16 regions separately, and merges the partial results with an
+ * online-softmax (log-sum-exp) merge (same section of the second page).
+ *
+ * Conventions common to every call:
+ *   - head_dim is 128; rotations are row-vector maps: stored = x . R, with
+ *     R row-major [128][128] in float32.
+ *   - "device" pointers are HIP device memory owned by the caller; the
+ *     library never allocates, frees or keeps pointers after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns without synchronising; buffers must
+ *     stay valid until that work completes.  Calls on one stream run in
+ *     order; calls that touch the same cache on different streams race.
+ *   - Return value: OSCAR_OK, or an error code with a message available
+ *     from oscar_last_error() (thread-local).  Arguments are checked on the
+ *     host before anything is enqueued; an error leaves device memory
+ *     untouched.  Device-resident values (seq_lens, page_table) are trusted:
+ *     the caller keeps them within the documented ranges.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_OK 0
+#define OSCAR_EINVAL 1        /* null/inconsistent argument, workspace too small */
+#define OSCAR_EUNSUPPORTED 2  /* a shape this build does not implement */
+#define OSCAR_EHIP 3          /* a HIP runtime call or kernel launch failed */
+
+/* Model and cache geometry.  Supported: head_dim 128, page_size 64,
+ * sink_len 64, recent_len 256, group_size in {32, 64, 128},
+ * num_q_heads a multiple of num_kv_heads with 1 <= Hq/Hkv <= 8. */
+typedef struct oscar_dims {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t group_size;
+  int32_t page_size;
+  int32_t sink_len;
+  int32_t recent_len;
+} oscar_dims;
+
+/* Fixed per-layer rotations and clip thresholds, built offline from the
+ * query covariance and the score-weighted value covariance
+ * (R = U . Hadamard . bit-reversal; first page, section "OSCAR 的不同之处").
+ * All device, float32, read only. */
+typedef struct oscar_rotation {
+  const float* r_k;     /* [Hkv][128][128] */
+  const float* r_v;     /* [Hkv][128][128] */
+  const float* clip_k;  /* [Hkv][128], thresholds in the rotated domain, > 0 */
+  const float* clip_v;  /* [Hkv][128] */
+} oscar_rotation;
+
+/* One layer's cache for a batch of requests (all device memory).
+ *
+ * pages:       [n_pages][Hkv][oscar_block_bytes(G)] bytes.  One block holds
+ *              64 history slots of one KV head, keys and values, laid out as:
+ *                bytes [0, 2048): key words; word d*64 + qk(t) holds the 2-bit
+ *                  codes of channels 16d..16d+15 of slot t (d = 0..7);
+ *                bytes [2048, 4096): value words; word
+ *                  (c/64)*256 + ((w*16 + c%16)*4 + (c/16)%4) holds the codes
+ *                  of slots 16w..16w+15 of channel c (w = 0..3);
+ *                then key scale/zero, then value scale/zero: entry qk(t) is
+ *                  128/G pairs {scale, zero} of bf16.
+ *              Words are 32-bit little endian; element i of a word sits at
+ *              bits 2i..2i+1.  qk(t) = 16*(t/16) + 4*(t%4) + (t/4)%4.
+ *              The stored channel index is the rotated one (after . R).
+ * sink_k/v:    bf16 [B][Hkv][64][128]; position p < 64 at slot p.
+ * recent_k/v:  bf16 [B][Hkv][256][128]; position p >= 64 at slot (p-64) % 256.
+ * page_table:  int32 [B][max_pages_per_req]; history index j = p - 64 of
+ *              request b lives in page page_table[b][j/64], slot j % 64.
+ * seq_lens:    int32 [B]; L_b = tokens held by request b, including the
+ *              current one (1 <= L_b <= max_seq_len of the call).
+ * Request b holds min(L_b,64) sink, max(0,L_b-320) history and
+ * min(max(L_b-64,0),256) recent tokens. */
+typedef struct oscar_cache {
+  uint8_t* pages;
+  int64_t n_pages;
+  uint16_t* sink_k;
+  uint16_t* sink_v;
+  uint16_t* recent_k;
+  uint16_t* recent_v;
+  const int32_t* page_table;
+  int32_t max_pages_per_req;
+  const int32_t* seq_lens;
+  int32_t batch;
+} oscar_cache;
+
+/* Bytes of one (page, KV head) block for group size G: 4096 + 512*(128/G);
+ * 0 for an unsupported G. */
+size_t oscar_block_bytes(int32_t group_size);
+
+/* Append + demote, one decode step (second page, section
+ * "OSCAR的另一个关键点是": the oldest recent token is rotated, clipped,
+ * quantized and packed into history).  seq_lens already count the new token.
+ * For each request with L > 320 and each KV head, the token at position
+ * L-257 is read from its recent slot, stored as y = x . R (float32), clipped
+ * to [-c, c] per channel, quantized per group of G channels (zero = bf16(min),
+ * scale = bf16((max-min)/3), code = clamp(rint((y-zero)/scale), 0, 3), code 0
+ * when scale = 0) and packed into history index L-321 (key and value).
+ * Then the new token k_new/v_new (bf16 [B][Hkv][128]) is written to its sink
+ * or recent slot, which for L > 320 is the slot just freed.  k_new and v_new
+ * may both be NULL (demote only).  The page holding index L-321 must be
+ * allocated in page_table and owned by this request alone. */
+int oscar_kv_demote(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                    const uint16_t* k_new, const uint16_t* v_new, void* stream);
+
+/* Bulk form of the demotion for filling history in one launch (a prefill
+ * of a long prompt): quantize n_tokens bf16 tokens k_tokens/v_tokens
+ * [n_tokens][Hkv][128] (device) into history indices hist_begin ..
+ * hist_begin+n_tokens-1 of request `request`, with exactly the per-token
+ * arithmetic of oscar_kv_demote.  Other slots of the touched pages keep
+ * their contents. */
+int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
+                          const oscar_cache* cache, int32_t request, int32_t hist_begin,
+                          int32_t n_tokens, const uint16_t* k_tokens,
+                          const uint16_t* v_tokens, void* stream);
+
+/* Number of history splits the decode uses for (batch, max_seq_len). */
+int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len);
+
+/* Workspace bytes oscar_decode_attn / oscar_merge_lse need (device memory,
+ * 256-byte aligned, owned by the caller; no initialisation required). */
+size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32_t max_seq_len);
+
+/* Decode attention over the three regions (second page, section
+ * "OSCAR的另一个关键点是": an INT2 kernel for history with unpacking and
+ * scale/zero dequantization, a bf16 kernel for sink and recent).
+ * q: bf16 [B][Hq][128] (unrotated).  Query head h reads KV head h/(Hq/Hkv).
+ * The query is rotated by R_K once per (request, head) (third page, method
+ * paragraphs: the online overhead lives inside the decode kernels); the
+ * history is split into oscar_history_splits() ranges and each produces a
+ * partial output (in the rotated value domain) and its log-sum-exp; the
+ * sink and recent tokens produce one more partial with the unrotated query.
+ * Scores use scale 1/sqrt(128).  Results go to `workspace` for
+ * oscar_merge_lse.  max_seq_len >= every L_b. */
+int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot,
+                      const oscar_cache* cache, const uint16_t* q, int32_t max_seq_len,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Log-sum-exp merge: combine the history partials, rotate the history
+ * output back by R_V^T, merge it with the sink/recent partial and write
+ * out: float32 [B][Hq][128].  lse_out (may be NULL): float32 [B][Hq], the
+ * natural-log log-sum-exp of all scores.  batch and max_seq_len must equal
+ * those given to oscar_decode_attn for this workspace. */
+int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,
+                    int32_t max_seq_len, const void* workspace, size_t workspace_bytes,
+                    float* out, float* lse_out, void* stream);
+
+/* Which history kernel oscar_decode_attn launches: 0 = default (MFMA where
+ * available), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
+ * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
+int oscar_set_history_kernel(int kind);
+
+/* Optional timing hook: when both are non-NULL, oscar_decode_attn records
+ * hipEvent_t `before` immediately before and `after` immediately after the
+ * history kernel launch on its stream.  Thread-local; NULL clears it. */
+int oscar_set_history_events(void* before, void* after);
+
+/* Thread-local text of the last error ("" if none). */
+const char* oscar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

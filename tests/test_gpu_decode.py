@@ -1,0 +1,191 @@
+"""GPU parity of decode attention (query rotation, INT2 history split-K,
+bf16 sink/recent, LSE merge) against the oracle's single-softmax attention.
+
+Each cache is filled on the GPU from the seeded generator through the
+library's bulk demotion; the oracle regenerates the same tokens on the host,
+demotes them itself and attends in float64.  Bar: 2e-3 max-abs and 1e-3
+relative L2 on the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_split_amd as ok
+from bit_rotated_kv_split_amd import workload as W
+from bit_rotated_kv_split_amd.kvcache import DecodeWorkspace, Rotation, decode_step
+from synth import configs
+
+from gpu_helpers import assert_close, oracle_calibration, oracle_request
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = {"valu": 1, "mfma": 2}
+
+
+def run_decode(cache, rot, q, max_len, kind):
+    prev = ok.oscar_set_history_kernel(kind)
+    try:
+        ws = DecodeWorkspace(cache.dims, cache.batch, max_len)
+        out = torch.empty((cache.batch, cache.num_q_heads, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((cache.batch, cache.num_q_heads), dtype=torch.float32, device="cuda")
+        c = cache.struct()
+        ok.oscar_decode_attn(cache.dims, rot.struct, c, q, max_len, ws.buf, ws.nbytes)
+        ok.oscar_merge_lse(cache.dims, rot.struct, cache.batch, max_len, ws.buf, ws.nbytes, out, lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+    finally:
+        ok.oscar_set_history_kernel(prev)
+
+
+_CAL = {}
+
+
+def setup(w, lens=None, extra=0):
+    layout = W.Layout(w, lens, extra)
+    model = W.SyntheticModel(w)
+    key = (w.name, w.num_q_heads, w.num_kv_heads, w.seed)
+    if key not in _CAL:
+        _CAL[key] = oracle_calibration(model)
+    cal = _CAL[key]
+    rot = Rotation(cal["r_k32"], cal["r_v32"], cal["clip_k"], cal["clip_v"])
+    cache = W.build_cache(w, layout, model, rot)
+    return layout, model, cal, rot, cache
+
+
+def check_all(layout, model, cal, out, lse, q_bits, requests=None, what=""):
+    w = model.w
+    for b in (range(w.batch) if requests is None else requests):
+        L = int(layout.lens[b])
+        ref, ref_lse = oracle_request(model, layout, cal, q_bits[b], b, L)
+        assert_close(out[b], ref, f"{what} b={b} L={L}")
+        assert np.abs(lse[b] - ref_lse).max() < 2e-3, f"{what} lse b={b}"
+
+
+def small(name, seed, hq, hkv, group, lens, paged=True, shared=False, aniso=True):
+    return configs.Workload(name, seed, hq, hkv, group, len(lens), tuple(lens), paged=paged,
+                            shared_prefix=shared, anisotropic_q=aniso)
+
+
+def _run_case(w, kind, lens=None):
+    layout, model, cal, rot, cache = setup(w, lens)
+    q_bits = model.queries(0, w.batch)
+    q = W.queries_tensor(model, 0, w.batch)
+    max_len = int(layout.lens.max())
+    try:
+        out, lse = run_decode(cache, rot, q, max_len, kind)
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(f"history kernel {kind} unsupported: {e}")
+        raise
+    check_all(layout, model, cal, out, lse, q_bits, what=w.name)
+    return out
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_tiny_config(kernel):
+    """1 q head, 1 KV head, G = 32, L = 1024 = 64 | 704 | 256."""
+    _run_case(configs.tiny(), KERNELS[kernel])
+
+
+EDGE_LENS = [1, 30, 64, 65, 200, 320, 321, 322, 384, 385, 448, 1000, 2047, 4000]
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_ragged_edges_gqa4(kernel, group):
+    w = small(f"edges-g{group}", 21, 8, 2, group, EDGE_LENS)
+    _run_case(w, KERNELS[kernel])
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("gqa", [1, 2, 8])
+def test_gqa_widths(kernel, gqa):
+    w = small(f"gqa{gqa}", 30 + gqa, 2 * gqa, 2, 128, [333, 1500, 3333, 6000])
+    _run_case(w, KERNELS[kernel])
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_shared_prefix_gqa8(kernel):
+    """Half of each request's history pages map to one shared physical chain."""
+    lens = [9000, 4500, 7100, 12345]
+    w = small("shared", 40, 16, 2, 128, lens, shared=True)
+    _run_case(w, KERNELS[kernel])
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_contiguous_isotropic(kernel):
+    w = small("contig", 50, 4, 1, 64, [2500, 700], paged=False, aniso=False)
+    _run_case(w, KERNELS[kernel])
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_deterministic_and_split_independent(kernel):
+    w = small("det", 60, 8, 2, 128, [5000, 3000, 800])
+    layout, model, cal, rot, cache = setup(w, extra=55_000)
+    q = W.queries_tensor(model, 0, w.batch)
+    try:
+        a, la = run_decode(cache, rot, q, 5000, KERNELS[kernel])
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(str(e))
+        raise
+    b, lb = run_decode(cache, rot, q, 5000, KERNELS[kernel])
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # a larger max_seq_len changes the split layout, not the result
+    assert ok.oscar_history_splits(cache.dims, 3, 5000) != ok.oscar_history_splits(cache.dims, 3, 60000)
+    c, lc = run_decode(cache, rot, q, 60000, KERNELS[kernel])
+    assert_close(c, a, "split layouts", atol=1e-5, rel_l2=1e-5)
+
+
+def test_valu_and_mfma_agree():
+    w = small("agree", 70, 8, 2, 128, [7000, 321, 2000])
+    layout, model, cal, rot, cache = setup(w)
+    q = W.queries_tensor(model, 0, w.batch)
+    a, _ = run_decode(cache, rot, q, 7000, KERNELS["valu"])
+    try:
+        b, _ = run_decode(cache, rot, q, 7000, KERNELS["mfma"])
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(str(e))
+        raise
+    assert_close(b, a, "valu vs mfma", atol=1e-4, rel_l2=1e-4)
+
+
+def test_full_step_sequence_matches_oracle():
+    """Decode steps with append + demotion (the bench's step) from L = 2000,
+    checked against the oracle after several steps."""
+    w = small("steps", 80, 8, 2, 128, [2000, 1100], paged=True)
+    steps = 40
+    layout, model, cal, rot, cache = setup(w, extra=steps)
+    ws = DecodeWorkspace(cache.dims, w.batch, int(layout.lens.max()) + steps)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    lens = layout.lens.copy()
+    for s in range(1, steps + 1):
+        lens = lens + 1
+        cache.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        kn = W.new_tokens_tensor(model, layout, lens, "k")
+        vn = W.new_tokens_tensor(model, layout, lens, "v")
+        q = W.queries_tensor(model, s, w.batch)
+        decode_step(cache, rot, ws, q, out, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    q_bits = model.queries(steps, w.batch)
+    layout.lens = lens
+    for b in range(w.batch):
+        ref, _ = oracle_request(model, layout, cal, q_bits[b], b, int(lens[b]))
+        assert_close(got[b], ref, f"after {steps} steps b={b}")
+
+
+@pytest.mark.slow
+def test_full_size_batch32_100k_sampled():
+    """The benchmark's workload at full size (32 requests x 100K tokens,
+    32 q / 8 kv heads, G = 128, paged) in its launch configuration; outputs
+    of sampled requests checked against the oracle."""
+    w = configs.qwen3_8b_b32(128)
+    layout, model, cal, rot, cache = setup(w)
+    q_bits = model.queries(0, w.batch)
+    q = W.queries_tensor(model, 0, w.batch)
+    for kind in (0,):
+        out, lse = run_decode(cache, rot, q, 100_000, kind)
+        assert np.isfinite(out).all()
+        check_all(layout, model, cal, out, lse, q_bits, requests=[0, 31], what="full-size")

@@ -1,0 +1,236 @@
+"""GPU parity of the demotion (rotate -> clip -> quantize -> pack) against the
+oracle: bit-exact packed bytes and bf16 scale/zero given identical rotated
+values, and the append/demote state machine of a decode step."""
+import numpy as np
+import pytest
+import torch
+
+import bit_rotated_kv_split_amd as ok
+from bit_rotated_kv_split_amd.kvcache import PagedKVCache, Rotation
+from oracle import oscar as O
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def bits_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def tensor_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def random_tokens(rng, n, hkv, outlier=True):
+    x = rng.standard_normal((n, hkv, 128)).astype(np.float32)
+    if outlier:
+        x[:, :, [5, 77]] *= 20
+    return gen.bf16_bits(x)
+
+
+def signed_permutation(rng):
+    p = O.bit_reversal_matrix(128)
+    return (p * rng.choice([-1.0, 1.0], size=128)[None, :]).astype(np.float32)
+
+
+def make_rot(kind, hkv, rng):
+    if kind == "identity":
+        rk = np.stack([np.eye(128, dtype=np.float32)] * hkv)
+        rv = rk.copy()
+    else:
+        rk = np.stack([signed_permutation(rng) for _ in range(hkv)])
+        rv = np.stack([signed_permutation(rng) for _ in range(hkv)])
+    ck = (1.5 + rng.random((hkv, 128))).astype(np.float32) * 2
+    cv = (1.0 + rng.random((hkv, 128))).astype(np.float32) * 2
+    return rk, rv, ck, cv
+
+
+def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid):
+    """Oracle bytes of one page block whose first n_valid slots hold tokens."""
+    ng = 128 // group
+    codes_k = np.zeros((64, 128), dtype=np.uint8)
+    codes_v = np.zeros((64, 128), dtype=np.uint8)
+    sk = np.zeros((64, ng), np.float32)
+    zk = np.zeros((64, ng), np.float32)
+    sv = np.zeros((64, ng), np.float32)
+    zv = np.zeros((64, ng), np.float32)
+    if n_valid:
+        c, s, z = O.demote(k_bits[:n_valid], rk, ck, group)
+        codes_k[:n_valid], sk[:n_valid], zk[:n_valid] = c, s, z
+        c, s, z = O.demote(v_bits[:n_valid], rv, cv, group)
+        codes_v[:n_valid], sv[:n_valid], zv[:n_valid] = c, s, z
+    return O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("kind", ["identity", "signed_perm"])
+def test_fill_bit_exact(group, kind):
+    rng = np.random.default_rng(group + (7 if kind == "identity" else 9))
+    B, hkv, hq = 2, 2, 4
+    n_hist = [150, 64]
+    max_pages = 3
+    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8)
+    pt = np.array([[5, 0, 3], [7, 2, 6]], dtype=np.int32)
+    cache.page_table.copy_(torch.from_numpy(pt))
+    cache.seq_lens.copy_(torch.tensor([320 + n for n in n_hist], dtype=torch.int32))
+    rk, rv, ck, cv = make_rot(kind, hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    toks = [(random_tokens(rng, n, hkv), random_tokens(rng, n, hkv)) for n in n_hist]
+    for b in range(B):
+        kb, vb = toks[b]
+        cuts = [0, 37, 100, n_hist[b]] if n_hist[b] > 100 else [0, n_hist[b]]
+        for a, e in zip(cuts[:-1], cuts[1:]):
+            ok.oscar_kv_fill_history(cache.dims, rot.struct, cache.struct(), b, a, e - a,
+                                     bits_tensor(kb[a:e]), bits_tensor(vb[a:e]))
+    torch.cuda.synchronize()
+    pages = cache.pages.cpu().numpy()
+    for b in range(B):
+        kb, vb = toks[b]
+        for p in range(max_pages):
+            n_valid = max(0, min(64, n_hist[b] - 64 * p))
+            if n_valid == 0:
+                continue
+            for j in range(hkv):
+                exp = expected_block(kb[64 * p:64 * p + n_valid, j], vb[64 * p:64 * p + n_valid, j],
+                                     rk[j], rv[j], ck[j], cv[j], group, n_valid)
+                got = pages[pt[b, p], j]
+                assert np.array_equal(got, exp), f"b={b} page={p} kvh={j}"
+    # pages no request uses stay zero
+    used = set(pt[0, :3].tolist()) | set(pt[1, :1].tolist())
+    for q in range(8):
+        if q not in used:
+            assert not pages[q].any()
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_fill_calibrated_rotation_codes(group):
+    """With a calibrated (dense) rotation the GPU rotates in float32 and the
+    oracle rounds an exact sum once, so the rotated values can differ in the
+    last bit.  Scale/zero must agree except where that moves a bf16 rounding,
+    and codes except within 1e-5 (relative) of a level boundary."""
+    from synth import configs
+    from bit_rotated_kv_split_amd.workload import SyntheticModel
+    w = configs.qwen3_8b_b32(group)
+    model = SyntheticModel(w)
+    q, k, v = model.calibration()
+    cal = O.calibrate(q[:, :8], k[:, :2], v[:, :2], w.clip_pct)
+    hkv, n = 2, 512
+    rng = np.random.default_rng(3)
+    cache = PagedKVCache(8, hkv, group, 1, 8, 8)
+    cache.page_table.copy_(torch.arange(8, dtype=torch.int32)[None])
+    rot = Rotation(cal["r_k32"], cal["r_v32"], cal["clip_k"], cal["clip_v"])
+    kb = np.stack([gen.kv_tokens_bf16(w.seed, "k", 0, j, 64, n, model.k_scale[j]) for j in range(hkv)], 1)
+    vb = np.stack([gen.kv_tokens_bf16(w.seed, "v", 0, j, 64, n, model.v_scale[j]) for j in range(hkv)], 1)
+    del rng
+    ok.oscar_kv_fill_history(cache.dims, rot.struct, cache.struct(), 0, 0, n, bits_tensor(kb), bits_tensor(vb))
+    torch.cuda.synchronize()
+    pages = cache.pages.cpu().numpy()
+    sz_mismatch = code_mismatch = 0
+    total_groups = 0
+    for j in range(hkv):
+        for which, bits, r, c in (("k", kb, cal["r_k32"][j], cal["clip_k"][j]),
+                                  ("v", vb, cal["r_v32"][j], cal["clip_v"][j])):
+            y = O.clip(O.rotate(O.bf16_value(bits[:, j]), r), c)
+            codes, s, z = O.quantize_groups(y, group)
+            for p in range(n // 64):
+                ck_, sk_, zk_, cv_, sv_, zv_ = O.unpack_block(pages[p, j], group)
+                gc, gs, gz = (ck_, sk_, zk_) if which == "k" else (cv_, sv_, zv_)
+                sl = slice(64 * p, 64 * p + 64)
+                bad_g = (gs != s[sl]) | (gz != z[sl])
+                sz_mismatch += int(bad_g.sum())
+                total_groups += bad_g.size
+                # scale/zero within one bf16 step when they differ
+                assert np.all(np.abs(gs - s[sl]) <= np.abs(s[sl]) * 2 ** -7)
+                assert np.all(np.abs(gz - z[sl]) <= np.abs(z[sl]) * 2 ** -7 + 1e-30)
+                ng = 128 // group
+                same_g = np.repeat(~bad_g, group, axis=1).reshape(64, 128)
+                diff = (gc != codes[sl]) & same_g
+                t = (y[sl].astype(np.float64) - np.repeat(z[sl], group, axis=1)) / np.repeat(s[sl], group, axis=1)
+                near = np.abs(t - np.floor(t) - 0.5) <= 1e-5 * np.maximum(np.abs(t), 1)
+                assert not (diff & ~near).any(), f"kvh={j} {which} page={p}"
+                code_mismatch += int(diff.sum())
+    assert sz_mismatch <= max(2, total_groups // 500), (sz_mismatch, total_groups)
+
+
+def ring_expect(L, k_all):
+    """Expected recent ring [256][128] bits for a request holding L tokens."""
+    ring = np.zeros((256, 128), dtype=np.uint16)
+    n_r = min(max(L - 64, 0), 256)
+    for p in range(L - n_r, L):
+        ring[(p - 64) % 256] = k_all[p]
+    return ring
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_decode_steps_append_and_demote(group):
+    """A sequence of decode steps (append + demote) from L = 60 to L = 480
+    crosses every region boundary and two page boundaries; the GPU state after
+    the last step equals the oracle's: sink and ring bits, packed pages."""
+    rng = np.random.default_rng(11 + group)
+    B, hkv, hq = 2, 2, 4
+    L0, L1 = 60, 480
+    start = [L0, L0 + 37]
+    total = max(start) + (L1 - L0)
+    k_all = random_tokens(rng, total, hkv).reshape(total, hkv, 128)
+    k_all = np.stack([k_all, random_tokens(rng, total, hkv)], axis=0)   # [K/V][pos][kvh][128]
+    v_all = k_all[1]
+    k_all = k_all[0]
+    rk, rv, ck, cv = make_rot("signed_perm", hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    max_pages = 4
+    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8)
+    pt = np.array([[4, 1, 2, 6], [0, 5, 3, 7]], dtype=np.int32)
+    cache.page_table.copy_(torch.from_numpy(pt))
+    # initial state: positions < start[b] as the state machine leaves them
+    for b in range(B):
+        L = start[b]
+        sink = np.zeros((hkv, 64, 128), np.uint16)
+        n_s = min(L, 64)
+        sink[:, :n_s] = k_all[:n_s].transpose(1, 0, 2)
+        cache.sink_k[b] = bits_tensor(sink)
+        sink[:, :n_s] = v_all[:n_s].transpose(1, 0, 2)
+        cache.sink_v[b] = bits_tensor(sink)
+        cache.recent_k[b] = bits_tensor(np.stack([ring_expect(L, k_all[:, j]) for j in range(hkv)]))
+        cache.recent_v[b] = bits_tensor(np.stack([ring_expect(L, v_all[:, j]) for j in range(hkv)]))
+    lens = np.array(start)
+    for step in range(L1 - L0):
+        lens = lens + 1
+        cache.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        kn = np.stack([k_all[lens[b] - 1] for b in range(B)])
+        vn = np.stack([v_all[lens[b] - 1] for b in range(B)])
+        ok.oscar_kv_demote(cache.dims, rot.struct, cache.struct(), bits_tensor(kn), bits_tensor(vn))
+    torch.cuda.synchronize()
+    pages = cache.pages.cpu().numpy()
+    for b in range(B):
+        L = int(lens[b])
+        assert np.array_equal(tensor_bits(cache.recent_k[b]),
+                              np.stack([ring_expect(L, k_all[:, j]) for j in range(hkv)]))
+        assert np.array_equal(tensor_bits(cache.recent_v[b]),
+                              np.stack([ring_expect(L, v_all[:, j]) for j in range(hkv)]))
+        assert np.array_equal(tensor_bits(cache.sink_k[b]), k_all[:64].transpose(1, 0, 2))
+        n_hist = L - 320
+        for p in range((n_hist + 63) // 64):
+            n_valid = min(64, n_hist - 64 * p)
+            for j in range(hkv):
+                sl = slice(64 + 64 * p, 64 + 64 * p + n_valid)
+                exp = expected_block(k_all[sl, j], v_all[sl, j], rk[j], rv[j], ck[j], cv[j], group, n_valid)
+                assert np.array_equal(pages[pt[b, p], j], exp), f"b={b} page={p} kvh={j}"
+
+
+def test_demote_only_leaves_ring_alone():
+    rng = np.random.default_rng(5)
+    hkv = 1
+    cache = PagedKVCache(1, hkv, 64, 1, 2, 2)
+    cache.page_table.copy_(torch.tensor([[1, 0]], dtype=torch.int32))
+    ring = random_tokens(rng, 256, hkv).reshape(256, 128)
+    cache.recent_k[0, 0] = bits_tensor(ring)
+    cache.recent_v[0, 0] = bits_tensor(ring)
+    cache.seq_lens.fill_(321)
+    rk, rv, ck, cv = make_rot("identity", hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    ok.oscar_kv_demote(cache.dims, rot.struct, cache.struct(), None, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensor_bits(cache.recent_k[0, 0]), ring)
+    slot = (320 - 256 - 64) % 256   # position 64 -> slot 0
+    exp = expected_block(ring[slot:slot + 1], ring[slot:slot + 1], rk[0], rv[0], ck[0], cv[0], 64, 1)
+    assert np.array_equal(cache.pages[1, 0].cpu().numpy(), exp)

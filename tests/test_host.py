@@ -1,0 +1,136 @@
+"""Host-side checks that need no GPU: the library loads, exports every
+function include/oscar.h declares, and rejects bad arguments before it
+enqueues anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_rotated_kv_split_amd as ok
+from bit_rotated_kv_split_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ok.lib()
+    decl = declared_functions()
+    assert len(decl) >= 10
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(_lib.EXPORTED) == decl
+
+
+def test_block_bytes():
+    assert ok.oscar_block_bytes(128) == 4608
+    assert ok.oscar_block_bytes(64) == 5120
+    assert ok.oscar_block_bytes(32) == 6144
+    assert ok.oscar_block_bytes(16) == 0
+
+
+def test_workspace_and_splits():
+    d = ok.make_dims(32, 8, 128)
+    s = ok.oscar_history_splits(d, 32, 100_000)
+    assert 1 <= s <= 1558
+    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= 32 * 32 * (s + 1) * 129 * 4
+    assert ok.oscar_history_splits(d, 1, 300) == 1          # no history
+    bad = ok.make_dims(32, 8, 128, head_dim=64)
+    assert ok.oscar_decode_workspace_bytes(bad, 1, 1000) == 0
+    assert ok.oscar_history_splits(bad, 1, 1000) == -1
+
+
+def _cache(batch=1):
+    fake = 0x1000
+    return ok.make_cache(fake, 4, fake, fake, fake, fake, fake, 4, fake, batch)
+
+
+def _rot():
+    fake = 0x1000
+    return ok.make_rotation(fake, fake, fake, fake)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, ok.OSCAR_EUNSUPPORTED),
+    ("group_size", 16, ok.OSCAR_EUNSUPPORTED),
+    ("page_size", 32, ok.OSCAR_EUNSUPPORTED),
+    ("sink_len", 32, ok.OSCAR_EUNSUPPORTED),
+    ("recent_len", 128, ok.OSCAR_EUNSUPPORTED),
+    ("num_kv_heads", 0, ok.OSCAR_EINVAL),
+    ("num_q_heads", 12, ok.OSCAR_EINVAL),     # not a multiple of 8
+])
+def test_invalid_dims_rejected(field, value, code):
+    d = ok.make_dims(32, 8, 128)
+    setattr(d, field, value)
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_kv_demote(d, _rot(), _cache(), None, None, 0)
+    assert e.value.code == code
+    assert ok.oscar_last_error() != ""
+
+
+def test_too_many_query_heads_per_kv_head():
+    d = ok.make_dims(72, 8, 128)
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode_attn(d, _rot(), _cache(), 0x1000, 1000, 0x1000, 1 << 30, 0)
+    assert e.value.code == ok.OSCAR_EUNSUPPORTED
+
+
+def test_null_and_inconsistent_arguments():
+    d = ok.make_dims(4, 2, 64)
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_kv_demote(d, _rot(), _cache(), 0x1000, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL
+    with pytest.raises(ok.OscarError):
+        ok.oscar_decode_attn(d, ok.make_rotation(0, 0x1000, 0x1000, 0x1000), _cache(), 0x1000, 100,
+                             0x1000, 1 << 30, 0)
+    # workspace too small
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode_attn(d, _rot(), _cache(), 0x1000, 100, 0x1000, 16, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "workspace" in ok.oscar_last_error()
+    # misaligned workspace
+    with pytest.raises(ok.OscarError):
+        ok.oscar_decode_attn(d, _rot(), _cache(), 0x1000, 100, 0x1008, 1 << 30, 0)
+    # history longer than the page table allows (4 pages = 256 history tokens)
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode_attn(d, _rot(), _cache(), 0x1000, 320 + 257, 0x1000, 1 << 30, 0)
+    assert "max_pages_per_req" in ok.oscar_last_error()
+    # fill outside the batch or beyond the page table
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_fill_history(d, _rot(), _cache(), 1, 0, 10, 0x1000, 0x1000, 0)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 250, 10, 0x1000, 0x1000, 0)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_merge_lse(d, _rot(), 1, 100, None, 1 << 30, 0x1000, None, 0)
+
+
+def test_empty_batch_and_zero_tokens_are_no_ops():
+    d = ok.make_dims(4, 2, 64)
+    ok.oscar_kv_demote(d, _rot(), _cache(batch=0), None, None, 0)
+    ok.oscar_decode_attn(d, _rot(), _cache(batch=0), None, 100, None, 0, 0)
+    ok.oscar_merge_lse(d, _rot(), 0, 100, None, 0, None, None, 0)
+    ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 0, 0, None, None, 0)
+
+
+def test_history_kernel_selector():
+    prev = ok.oscar_set_history_kernel(1)
+    assert ok.oscar_set_history_kernel(prev) == 1
+    with pytest.raises(ok.OscarError):
+        ok.oscar_set_history_kernel(7)
+
+
+def test_last_error_is_thread_local():
+    import threading
+    d = ok.make_dims(32, 8, 128, head_dim=64)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_demote(d, _rot(), _cache(), None, None, 0)
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(ok.oscar_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""] and "head_dim" in ok.oscar_last_error()
