@@ -24,8 +24,12 @@ from ._lib import (  # noqa: F401
     make_dims,
     make_rotation,
     oscar_block_bytes,
+    oscar_calibrate,
+    oscar_calibrate_max_tokens,
+    oscar_calibrate_workspace_bytes,
     oscar_decode_attn,
     oscar_decode_workspace_bytes,
+    oscar_history_kernel_for,
     oscar_history_splits,
     oscar_kv_demote,
     oscar_kv_fill_history,

@@ -68,7 +68,15 @@ _SIGS = [
     ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_calibrate_max_tokens", ctypes.c_int32, []),
+    ("oscar_calibrate_workspace_bytes", ctypes.c_size_t, [_P(OscarDims), ctypes.c_int32]),
+    ("oscar_calibrate", ctypes.c_int, [_P(OscarDims), ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
+    ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims)]),
     ("oscar_set_history_events", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_last_error", ctypes.c_char_p, []),
 ]
@@ -180,11 +188,39 @@ def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspac
                                  _stream(stream)))
 
 
+def oscar_calibrate_max_tokens() -> int:
+    return lib().oscar_calibrate_max_tokens()
+
+
+def oscar_calibrate_workspace_bytes(dims, n_tokens: int) -> int:
+    return lib().oscar_calibrate_workspace_bytes(ctypes.byref(dims), n_tokens)
+
+
+def oscar_calibrate(dims, n_tokens: int, q, k, v, clip_percentile: float, r_k, r_v, clip_k, clip_v,
+                    r_k_host=None, r_v_host=None, workspace=None, workspace_bytes: int = 0,
+                    stream=None) -> None:
+    """Device outputs r_k/r_v/clip_k/clip_v; optional host float64 outputs
+    given as numpy arrays (written in place)."""
+    def host(a):
+        if a is None:
+            return None
+        assert a.dtype.name == "float64" and a.flags["C_CONTIGUOUS"]
+        return a.ctypes.data
+    _check(lib().oscar_calibrate(ctypes.byref(dims), n_tokens, _ptr(q), _ptr(k), _ptr(v),
+                                 clip_percentile, _ptr(r_k), _ptr(r_v), _ptr(clip_k), _ptr(clip_v),
+                                 host(r_k_host), host(r_v_host), _ptr(workspace), workspace_bytes,
+                                 _stream(stream)))
+
+
 def oscar_set_history_kernel(kind: int) -> int:
     prev = lib().oscar_set_history_kernel(kind)
     if prev < 0:
         raise OscarError(OSCAR_EINVAL, f"invalid history kernel {kind}")
     return prev
+
+
+def oscar_history_kernel_for(dims) -> int:
+    return lib().oscar_history_kernel_for(ctypes.byref(dims))
 
 
 def oscar_set_history_events(before, after) -> None:

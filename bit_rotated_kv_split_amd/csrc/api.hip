@@ -127,9 +127,48 @@ size_t oscar_block_bytes(int32_t group_size) {
 
 const char* oscar_last_error(void) { return g_error.c_str(); }
 
+int32_t oscar_calibrate_max_tokens(void) { return calibrate_max_tokens(); }
+
+size_t oscar_calibrate_workspace_bytes(const oscar_dims* dims, int32_t n_tokens) {
+  if (check_dims(dims) || n_tokens < 2 || n_tokens > calibrate_max_tokens()) return 0;
+  return calibrate_workspace_bytes(*dims, n_tokens);
+}
+
+int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, const float* k,
+                    const float* v, double clip_percentile, float* r_k, float* r_v, float* clip_k,
+                    float* clip_v, double* r_k_host, double* r_v_host, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims))) return rc;
+  if (n_tokens < 2 || n_tokens > calibrate_max_tokens())
+    return fail(OSCAR_EUNSUPPORTED, "n_tokens %d outside 2..%d", n_tokens, calibrate_max_tokens());
+  if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))
+    return fail(OSCAR_EINVAL, "clip_percentile %g outside (0, 100]", clip_percentile);
+  if (!q || !k || !v || !r_k || !r_v || !clip_k || !clip_v || !workspace)
+    return fail(OSCAR_EINVAL, "calibration has a NULL device pointer");
+  if (workspace_bytes < calibrate_workspace_bytes(*dims, n_tokens))
+    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes,
+                calibrate_workspace_bytes(*dims, n_tokens));
+  const hipError_t e = run_calibration(*dims, n_tokens, q, k, v, clip_percentile, r_k, r_v, clip_k,
+                                       clip_v, r_k_host, r_v_host, workspace,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "calibration");
+  return OSCAR_OK;
+}
+
 int oscar_set_history_kernel(int kind) {
   if (kind < 0 || kind > 2) return -1;
   return g_hist_kernel.exchange(kind);
+}
+
+int oscar_history_kernel_for(const oscar_dims* dims) {
+  if (check_dims(dims)) return -1;
+  const int kind = g_hist_kernel.load();
+  const bool mfma_ok = hist_mfma_supported(*dims);
+  if (kind == 2) return mfma_ok ? 2 : -1;
+  if (kind == 1) return 1;
+  return mfma_ok ? 2 : 1;
 }
 
 int oscar_set_history_events(void* before, void* after) {

@@ -64,4 +64,11 @@ hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t 
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
                         hipStream_t s);
 
+size_t calibrate_workspace_bytes(const oscar_dims& d, int32_t n_tokens);
+int32_t calibrate_max_tokens();
+hipError_t run_calibration(const oscar_dims& d, int32_t n, const float* q, const float* k,
+                           const float* v, double pct, float* r_k, float* r_v, float* clip_k,
+                           float* clip_v, double* r_k_host, double* r_v_host, void* workspace,
+                           hipStream_t s);
+
 }  // namespace oscar

@@ -166,10 +166,47 @@ int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t b
                     int32_t max_seq_len, const void* workspace, size_t workspace_bytes,
                     float* out, float* lse_out, void* stream);
 
+/* Largest calibration sequence oscar_calibrate accepts (tokens). */
+int32_t oscar_calibrate_max_tokens(void);
+
+/* Device workspace bytes oscar_calibrate needs for n_tokens tokens; 0 on
+ * invalid arguments. */
+size_t oscar_calibrate_workspace_bytes(const oscar_dims* dims, int32_t n_tokens);
+
+/* Offline calibration of one layer (first page, section "OSCAR 的不同之处";
+ * second page, section "OSCAR把旋转对准attention"; third page, method
+ * paragraphs).  Input: a calibration sequence of n_tokens positions,
+ * device float32 q [N][Hq][128], k and v [N][Hkv][128].  For each KV head j
+ * with query group G_j = {h : h / (Hq/Hkv) == j}:
+ *   C_Q = mean over n and h in G_j of q_{n,h}^T q_{n,h};
+ *   C_S = mean over n and h in G_j of o_{n,h}^T o_{n,h}, o_{n,h} = sum_{t<=n}
+ *         softmax_t(q_{n,h} . k_t / sqrt(128)) v_t (= V^T S^T S V / N with
+ *         causal attention probabilities S);
+ *   R_K = U_Q . H . P_br, R_V = U_S . H . P_br, U the eigenvectors of C in
+ *         descending eigenvalue order, each signed so that its entry of
+ *         largest magnitude (lowest index on ties) is positive; H the
+ *         normalised Sylvester Hadamard matrix; (x . P_br)_k = x_bitrev7(k);
+ *   clip_K[c] = clip_percentile-th percentile (linear interpolation) of
+ *         |k_n . R_K[:, c]| over n, likewise clip_V with v and R_V.
+ * Statistics are float64.  Outputs: r_k, r_v device float32 [Hkv][128][128];
+ * clip_k, clip_v device float32 [Hkv][128]; r_k_host, r_v_host (optional,
+ * may be NULL) host float64 [Hkv][128][128].  2 <= n_tokens <=
+ * oscar_calibrate_max_tokens(); 0 < clip_percentile <= 100.  This call is
+ * synchronous: it waits for `stream` (the eigen-decompositions run on the
+ * host between kernels) and returns when every output is written. */
+int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, const float* k,
+                    const float* v, double clip_percentile, float* r_k, float* r_v, float* clip_k,
+                    float* clip_v, double* r_k_host, double* r_v_host, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Which history kernel oscar_decode_attn launches: 0 = default (MFMA where
  * available), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
  * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
 int oscar_set_history_kernel(int kind);
+
+/* History kernel the current selection launches for dims: 1 = vector-ALU,
+ * 2 = matrix-core; -1 for invalid dims or an unsupported forced choice. */
+int oscar_history_kernel_for(const oscar_dims* dims);
 
 /* Optional timing hook: when both are non-NULL, oscar_decode_attn records
  * hipEvent_t `before` immediately before and `after` immediately after the

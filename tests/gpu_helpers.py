@@ -42,6 +42,24 @@ def oracle_request(model, layout, cal, q_bits_b, b: int, L: int, heads=None):
                                cal["clip_v"], model.w.group_size)
 
 
+def oracle_request_heads(model, layout, cal, q_bits_b, b: int, L: int, kv_heads):
+    """Oracle output of the query groups of the listed KV heads of request b:
+    {kv head: (out [g][128], lse [g])}."""
+    w = model.w
+    g = w.gqa
+    res = {}
+    for j in kv_heads:
+        k = np.zeros((L, 1, 128), dtype=np.uint16)
+        v = np.zeros_like(k)
+        for src, p0, n in layout.src_ranges(b, 0, L):
+            k[p0:p0 + n, 0] = gen.kv_tokens_bf16(w.seed, "k", src, j, p0, n, model.k_scale[j])
+            v[p0:p0 + n, 0] = gen.kv_tokens_bf16(w.seed, "v", src, j, p0, n, model.v_scale[j])
+        res[j] = O.request_attention(q_bits_b[j * g:(j + 1) * g], k, v, cal["r_k32"][j:j + 1],
+                                     cal["r_v32"][j:j + 1], cal["clip_k"][j:j + 1],
+                                     cal["clip_v"][j:j + 1], w.group_size)
+    return res
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, what: str = "", atol: float = ATOL,
                  rel_l2: float = REL_L2) -> None:
     got = np.asarray(got, dtype=np.float64)

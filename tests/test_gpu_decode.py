@@ -179,13 +179,18 @@ def test_full_step_sequence_matches_oracle():
 @pytest.mark.slow
 def test_full_size_batch32_100k_sampled():
     """The benchmark's workload at full size (32 requests x 100K tokens,
-    32 q / 8 kv heads, G = 128, paged) in its launch configuration; outputs
-    of sampled requests checked against the oracle."""
+    32 q / 8 kv heads, G = 128, paged) in its launch configuration (default
+    history kernel, max_seq_len 100K); sampled (request, KV head) groups
+    checked against the oracle, every output checked finite."""
+    from gpu_helpers import oracle_request_heads
     w = configs.qwen3_8b_b32(128)
     layout, model, cal, rot, cache = setup(w)
     q_bits = model.queries(0, w.batch)
     q = W.queries_tensor(model, 0, w.batch)
-    for kind in (0,):
-        out, lse = run_decode(cache, rot, q, 100_000, kind)
-        assert np.isfinite(out).all()
-        check_all(layout, model, cal, out, lse, q_bits, requests=[0, 31], what="full-size")
+    out, lse = run_decode(cache, rot, q, 100_000, 0)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    g = w.gqa
+    for b, j in ((0, 0), (31, 7), (17, 3)):
+        ref = oracle_request_heads(model, layout, cal, q_bits[b], b, 100_000, [j])[j]
+        assert_close(out[b, j * g:(j + 1) * g], ref[0], f"full-size b={b} kvh={j}")
+        assert np.abs(lse[b, j * g:(j + 1) * g] - ref[1]).max() < 2e-3
