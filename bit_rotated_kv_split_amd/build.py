@@ -18,6 +18,8 @@ ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # keep MFMA accumulators in VGPRs (no accvgpr copies)
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
 
 

@@ -90,7 +90,8 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
   int splits = 1;
   if (pages > 0 && pairs > 0) {
     splits = (kTargetWorkgroups + pairs - 1) / pairs;
-    const int max_splits = (pages + 7) / 8;
+    int max_splits = (pages + 7) / 8;
+    if (max_splits > kMaxSplits) max_splits = kMaxSplits;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     const int pps = (pages + splits - 1) / splits;
@@ -98,6 +99,7 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
     w.pages_per_split = pps;
   }
   w.splits = splits;
+  w.parts = splits + kBf16Parts;
   const size_t heads = static_cast<size_t>(batch) * d.num_q_heads;
   size_t off = 0;
   w.off_qrot = off;
@@ -107,9 +109,9 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
   w.off_qpack = off;
   off = align256(off + static_cast<size_t>(batch) * d.num_kv_heads * kQPackBytes);
   w.off_po = off;
-  off = align256(off + heads * (splits + 1) * kDim * sizeof(float));
+  off = align256(off + heads * w.parts * kDim * sizeof(float));
   w.off_plse = off;
-  off = align256(off + heads * (splits + 1) * sizeof(float));
+  off = align256(off + heads * w.parts * sizeof(float));
   w.total = off;
   return w;
 }

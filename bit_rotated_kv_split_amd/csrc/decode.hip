@@ -30,54 +30,63 @@ namespace {
 constexpr float kQFixMax = 8257536.0f;
 
 template <int GQ>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int hq, int hkv, int G,
             float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int k = threadIdx.x;
+  const int tid = threadIdx.x, k = tid & (kDim - 1), half = tid >> 7;
+  const int wave = tid >> 6, lane = tid & 63;
   __shared__ float qs[GQ][kDim];
+  __shared__ float part[2][GQ][kDim];
   __shared__ float qr[GQ][kDim];
-  __shared__ float qmax[GQ];
+  __shared__ float qinv[GQ];
   const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) qs[h][k] = bf16_to_f32(q[(head0 + h) * kDim + k]);
+  for (int i = tid; i < GQ * kDim; i += 256) qs[i / kDim][i % kDim] = bf16_to_f32(q[head0 * kDim + i]);
   __syncthreads();
+  // q . R_K: thread (k, half) sums rows i of its half
   const float* r = r_k + static_cast<size_t>(kvh) * kDim * kDim;
   float acc[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
-  for (int i = 0; i < kDim; ++i) {
+#pragma unroll 8
+  for (int i = 64 * half; i < 64 * half + 64; ++i) {
     const float rik = r[i * kDim + k];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) acc[h] = __builtin_fmaf(qs[h][i], rik, acc[h]);
   }
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const float v = acc[h] * kScoreScaleLog2;
-    qr[h][k] = v;
-    qrot[(head0 + h) * kDim + k] = v;
+  for (int h = 0; h < GQ; ++h) part[half][h][k] = acc[h];
+  __syncthreads();
+  for (int i = tid; i < GQ * kDim; i += 256) {
+    const int h = i / kDim, c = i % kDim;
+    const float v = (part[0][h][c] + part[1][h][c]) * kScoreScaleLog2;
+    qr[h][c] = v;
+    qrot[(head0 + h) * kDim + c] = v;
   }
   __syncthreads();
-  // per-group sums (thread k < GQ*4 handles (head, group of the 4 possible))
-  if (k < GQ * 4) {
-    const int h = k >> 2, gi = k & 3;
-    const int ng = kDim / G;
-    float s = 0.f;
-    if (gi < ng)
-      for (int j = 0; j < G; ++j) s += qr[h][gi * G + j];
-    qsum[(head0 + h) * 4 + gi] = s;
-  }
-  if (k < GQ) {
-    float m = 0.f;
-    for (int j = 0; j < kDim; ++j) m = fmaxf(m, fabsf(qr[k][j]));
-    qmax[k] = m;
+  // per-group sums and the largest magnitude, one wave per head
+  for (int h = wave; h < GQ; h += 4) {
+    const float v0 = qr[h][lane], v1 = qr[h][lane + 64];
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    if (lane == 0) qinv[h] = mx > 0.f ? kQFixMax / mx : 0.f;
+    for (int gi = 0; gi < 4; ++gi) {
+      const int lo = gi * G, hi = lo + G;
+      float sgi = (lane >= lo && lane < hi ? v0 : 0.f) + (lane + 64 >= lo && lane + 64 < hi ? v1 : 0.f);
+      sgi = wave_sum(sgi);
+      if (lane == 0) qsum[(head0 + h) * 4 + gi] = gi * G < kDim ? sgi : 0.f;
+    }
+    if (lane == 0) {
+      float* sc = reinterpret_cast<float*>(qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes +
+                                           kQPackOperandBytes);
+      sc[h] = mx > 0.f ? mx / kQFixMax : 0.f;
+    }
   }
   __syncthreads();
   // int8 limb operands: row = 4*h + limb (limb 3 = zero pad), 32 rows; for
   // channel half hf and lane group kg, byte e = 4*j + b2 of the row holds
   // channel 16*(4*hf + kg) + 4*b2 + j.
   uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
-  for (int idx = k; idx < 2 * 4 * kQPackRows * 16; idx += kDim) {
+  for (int idx = tid; idx < 2 * 4 * kQPackRows * 16; idx += 256) {
     const int e = idx & 15;
     const int row = (idx >> 4) & (kQPackRows - 1);
     const int kg = (idx >> 9) & 3;
@@ -86,8 +95,7 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     int8_t val = 0;
     if (h < GQ && limb < 3) {
       const int ch = 16 * (4 * hf + kg) + 4 * (e & 3) + (e >> 2);
-      const float sc = qmax[h] > 0.f ? qmax[h] / kQFixMax : 1.f;
-      const int qi = static_cast<int>(rintf(qr[h][ch] / sc));
+      const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h]));
       const int d0 = ((qi + 128) & 255) - 128;
       const int q1 = (qi - d0) >> 8;
       const int d1 = ((q1 + 128) & 255) - 128;
@@ -96,9 +104,9 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     }
     qp[idx] = static_cast<uint8_t>(val);
   }
-  if (k < 8) {
+  if (tid >= GQ && tid < 8) {
     float* sc = reinterpret_cast<float*>(qp + kQPackOperandBytes);
-    sc[k] = (k < GQ && qmax[k] > 0.f) ? qmax[k] / kQFixMax : 0.f;
+    sc[tid] = 0.f;
   }
 }
 
@@ -114,6 +122,7 @@ struct HistParams {
   int32_t hkv;
   int32_t hq;
   int32_t splits;
+  int32_t parts;
   int32_t pages_per_split;
 };
 
@@ -270,7 +279,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
         at += st_acc[w][h][c] * f;
       }
     }
-    const size_t pidx = (head0 + h) * (a.splits + 1) + split;
+    const size_t pidx = (head0 + h) * a.parts + split;
     a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
     if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
   }
@@ -287,186 +296,191 @@ struct Bf16Params {
   float* plse;
   int32_t hkv;
   int32_t hq;
-  int32_t splits;
+  int32_t parts;        // partials per head (history splits + bf16 chunks)
+  int32_t first_part;   // index of this kernel's first partial
 };
 
-// Sink + recent: 320 virtual slots (64 sink, 256 ring) in five chunks of 64;
-// wave w takes chunks w and w+4.  Lane = token for q.k, lane = channel pair
-// for p.v.
+// Sink + recent: five 64-slot chunks (the sink, then the ring in quarters),
+// one wave each, each writing its own partial (output, LSE).  q . k: lane =
+// token, reading its 256-byte key row; p . v: lane = (8-channel group, token
+// residue mod 4), 16-byte loads coalesced across a row, reduced across the
+// four residues at the end.
 template <int GQ>
-__global__ void __launch_bounds__(256) bf16_kernel(Bf16Params a) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
   __shared__ float q_s[GQ][kDim];
-  __shared__ float p_s[4][GQ][kPage];
-  __shared__ float st_m[4][GQ], st_l[4][GQ];
-  __shared__ float st_acc[4][GQ][kDim];
+  __shared__ float p_s[GQ][kPage];
   const int L = a.seq_lens[b];
   const int n_sink = min(L, kSink);
   const int n_recent = min(max(L - kSink, 0), kRecent);
+  const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
   const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * GQ;
-  for (int i = tid; i < GQ * kDim; i += 256)
-    q_s[i / kDim][i % kDim] = bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2;
-  __syncthreads();
-  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
-  const uint16_t* sk = a.sink_k + kv0 * kSink * kDim;
-  const uint16_t* sv = a.sink_v + kv0 * kSink * kDim;
-  const uint16_t* rk = a.recent_k + kv0 * kRecent * kDim;
-  const uint16_t* rv = a.recent_v + kv0 * kRecent * kDim;
-  float m[GQ], l[GQ], acc0[GQ], acc1[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-    acc0[h] = 0.f;
-    acc1[h] = 0.f;
+  const size_t part0 = static_cast<size_t>(a.first_part + chunk);
+  if (n_valid == 0) {   // uniform across the wave
+    for (int i = lane; i < GQ * kDim; i += 64)
+      a.po[((head0 + i / kDim) * a.parts + part0) * kDim + i % kDim] = 0.f;
+    if (lane < GQ) a.plse[(head0 + lane) * a.parts + part0] = -INFINITY;
+    return;
   }
-  for (int chunk = wave; chunk < 5; chunk += 4) {
-    const bool is_sink = chunk == 0;
-    const int n_valid = is_sink ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
-    if (n_valid == 0) continue;   // uniform across the wave
-    const uint16_t* kb = is_sink ? sk : rk + (chunk - 1) * kPage * kDim;
-    const uint16_t* vb = is_sink ? sv : rv + (chunk - 1) * kPage * kDim;
-    const int t = lane;
-    const bool valid = t < n_valid;
-    float sc[GQ];
+  for (int i = lane; i < GQ * kDim; i += 64)
+    q_s[i / kDim][i % kDim] = bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2;
+  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
+  const uint16_t* kb = chunk == 0 ? a.sink_k + kv0 * kSink * kDim
+                                  : a.recent_k + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  const uint16_t* vb = chunk == 0 ? a.sink_v + kv0 * kSink * kDim
+                                  : a.recent_v + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool valid = lane < n_valid;
+  float sc[GQ];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
-    if (valid) {
-      const uint4* row = reinterpret_cast<const uint4*>(kb + t * kDim);
+  for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
+  if (valid) {
+    const uint4* row = reinterpret_cast<const uint4*>(kb + lane * kDim);
 #pragma unroll 4
-      for (int v8 = 0; v8 < kDim / 8; ++v8) {
-        const uint4 w = row[v8];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int v8 = 0; v8 < kDim / 8; ++v8) {
+      const uint4 w = row[v8];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = __uint_as_float(ws[j] << 16);
-          const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
-          const int ch = v8 * 8 + 2 * j;
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(ws[j] << 16);
+        const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
+        const int ch = v8 * 8 + 2 * j;
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) {
-            sc[h] = __builtin_fmaf(q_s[h][ch], lo, sc[h]);
-            sc[h] = __builtin_fmaf(q_s[h][ch + 1], hi, sc[h]);
-          }
+        for (int h = 0; h < GQ; ++h) {
+          sc[h] = __builtin_fmaf(q_s[h][ch], lo, sc[h]);
+          sc[h] = __builtin_fmaf(q_s[h][ch + 1], hi, sc[h]);
         }
       }
     }
+  }
+  float mx[GQ], lsum[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const float s = valid ? sc[h] : -INFINITY;
+    mx[h] = wave_max(s);
+    const float pr = valid ? exp2f(s - mx[h]) : 0.f;
+    lsum[h] = wave_sum(pr);
+    p_s[h][lane] = pr;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int cg = lane & 15, res = lane >> 4;
+  float acc[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int t = res; t < n_valid; t += 4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(vb + t * kDim + cg * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      const float s = valid ? sc[h] : -INFINITY;
-      const float pm = wave_max(s);
-      const float mn = fmaxf(m[h], pm);
-      const float alpha = exp2f(m[h] - mn);
-      const float pr = valid ? exp2f(s - mn) : 0.f;
-      l[h] = l[h] * alpha + wave_sum(pr);
-      m[h] = mn;
-      acc0[h] *= alpha;
-      acc1[h] *= alpha;
-      p_s[wave][h][t] = pr;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int tt = 0; tt < n_valid; ++tt) {
-      const float v0 = bf16_to_f32(vb[tt * kDim + lane]);
-      const float v1 = bf16_to_f32(vb[tt * kDim + lane + 64]);
+      const float pt = p_s[h][t];
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        acc0[h] = __builtin_fmaf(p_s[wave][h][tt], v0, acc0[h]);
-        acc1[h] = __builtin_fmaf(p_s[wave][h][tt], v1, acc1[h]);
+      for (int j = 0; j < 4; ++j) {
+        acc[h][2 * j] = __builtin_fmaf(pt, __uint_as_float(ws[j] << 16), acc[h][2 * j]);
+        acc[h][2 * j + 1] = __builtin_fmaf(pt, __uint_as_float(ws[j] & 0xFFFF0000u), acc[h][2 * j + 1]);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    if (lane == 0) {
-      st_m[wave][h] = m[h];
-      st_l[wave][h] = l[h];
+    const float inv = 1.f / lsum[h];
+    const size_t pidx = (head0 + h) * a.parts + part0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (res == 0) a.po[pidx * kDim + cg * 8 + e] = v * inv;
     }
-    st_acc[wave][h][lane] = acc0[h];
-    st_acc[wave][h][lane + 64] = acc1[h];
-  }
-  __syncthreads();
-  for (int job = tid; job < GQ * kDim; job += 256) {
-    const int h = job / kDim, c = job % kDim;
-    float mx = -INFINITY;
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, st_m[w][h]);
-    float lt = 0.f, at = 0.f;
-    if (mx != -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
-        if (st_m[w][h] == -INFINITY) continue;
-        const float f = exp2f(st_m[w][h] - mx);
-        lt += st_l[w][h] * f;
-        at += st_acc[w][h][c] * f;
-      }
-    }
-    const size_t pidx = (head0 + h) * (a.splits + 1) + a.splits;
-    a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
-    if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
+    if (lane == 0) a.plse[pidx] = (mx[h] + log2f(lsum[h])) * kLn2;
   }
 }
 
-// LSE merge: workgroup = (KV head, request), thread = channel.
+// LSE merge: workgroup = (KV head, request), 256 threads.  The history
+// splits are merged per head into the rotated value domain, rotated back by
+// R_V^T, and merged with the bf16 partials.
 template <int GQ>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
-             const float* __restrict__ r_v, int hq, int splits, float* __restrict__ out,
+             const float* __restrict__ r_v, int hq, int splits, int parts, float* __restrict__ out,
              float* __restrict__ lse_out) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int k = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float wts[GQ][kMaxParts];
+  __shared__ float lse_s[GQ][2];      // history LSE, bf16 LSE
   __shared__ float orot[GQ][kDim];
-  __shared__ float lse_h[GQ];
   const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
+  for (int i = tid; i < GQ * parts; i += 256) wts[i / parts][i % parts] = plse[(head0 + i / parts) * parts + i % parts];
+  __syncthreads();
+  // per head: normalised weights of the history splits and of the bf16 partials
+  for (int h = wave; h < GQ; h += 4) {
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const size_t base = (head0 + h) * (splits + 1);
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, plse[base + s]);
-    float den = 0.f, o = 0.f;
-    if (mx != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const float ls = plse[base + s];
-        if (ls == -INFINITY) continue;
-        const float w = expf(ls - mx);
-        den += w;
-        o += w * po[(base + s) * kDim + k];
-      }
+    for (int side = 0; side < 2; ++side) {
+      const int s0 = side ? splits : 0, s1 = side ? parts : splits;
+      float mx = -INFINITY;
+      for (int s = s0 + lane; s < s1; s += 64) mx = fmaxf(mx, wts[h][s]);
+      mx = wave_max(mx);
+      float den = 0.f;
+      for (int s = s0 + lane; s < s1; s += 64) den += mx == -INFINITY ? 0.f : expf(wts[h][s] - mx);
+      den = wave_sum(den);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int s = s0 + lane; s < s1; s += 64) wts[h][s] = den > 0.f ? expf(wts[h][s] - mx) / den : 0.f;
+      if (lane == 0) lse_s[h][side] = den > 0.f ? mx + logf(den) : -INFINITY;
     }
-    orot[h][k] = den > 0.f ? o / den : 0.f;
-    if (k == 0) lse_h[h] = den > 0.f ? mx + logf(den) : -INFINITY;
   }
   __syncthreads();
-  // history output back to the model domain: x_i = sum_k y_k R_V[i][k]
-  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + k) * kDim);
-  float oh[GQ];
+  for (int i = tid; i < GQ * kDim; i += 256) {
+    const int h = i / kDim, k = i % kDim;
+    const float* base = po + ((head0 + h) * parts) * kDim + k;
+    float o = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < splits; ++s) o = __builtin_fmaf(wts[h][s], base[static_cast<size_t>(s) * kDim], o);
+    orot[h][k] = o;
+  }
+  __syncthreads();
+  // history output back to the model domain: x_i = sum_k y_k R_V[i][k];
+  // thread (i, half) covers heads of one parity
+  const int i = tid & (kDim - 1), half = tid >> 7;
+  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim);
+  float oh[(GQ + 1) / 2];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) oh[h] = 0.f;
+  for (int j = 0; j < (GQ + 1) / 2; ++j) oh[j] = 0.f;
 #pragma unroll 2
   for (int c4 = 0; c4 < kDim / 4; ++c4) {
     const float4 rr = rrow[c4];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 0], rr.x, oh[h]);
-      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 1], rr.y, oh[h]);
-      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 2], rr.z, oh[h]);
-      oh[h] = __builtin_fmaf(orot[h][4 * c4 + 3], rr.w, oh[h]);
+    for (int j = 0; j < (GQ + 1) / 2; ++j) {
+      const int h = 2 * j + half;
+      if (h < GQ) {
+        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 0], rr.x, oh[j]);
+        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 1], rr.y, oh[j]);
+        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 2], rr.z, oh[j]);
+        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 3], rr.w, oh[j]);
+      }
     }
   }
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const size_t pb = (head0 + h) * (splits + 1) + splits;
-    const float lb = plse[pb];
-    const float ob = po[pb * kDim + k];
-    const float lh = lse_h[h];
+  for (int j = 0; j < (GQ + 1) / 2; ++j) {
+    const int h = 2 * j + half;
+    if (h >= GQ) continue;
+    const float* bb = po + ((head0 + h) * parts) * kDim + i;
+    float ob = 0.f;
+    for (int s = splits; s < parts; ++s) ob = __builtin_fmaf(wts[h][s], bb[static_cast<size_t>(s) * kDim], ob);
+    const float lh = lse_s[h][0], lb = lse_s[h][1];
     const float mx = fmaxf(lh, lb);
     const float wh = lh == -INFINITY ? 0.f : expf(lh - mx);
     const float wb = lb == -INFINITY ? 0.f : expf(lb - mx);
     const float den = wh + wb;
-    out[(head0 + h) * kDim + k] = den > 0.f ? (wh * oh[h] + wb * ob) / den : 0.f;
-    if (lse_out != nullptr && k == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
+    out[(head0 + h) * kDim + i] = den > 0.f ? (wh * oh[j] + wb * ob) / den : 0.f;
+    if (lse_out != nullptr && i == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
   }
 }
 
@@ -489,7 +503,7 @@ struct QrotRun {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const oscar_dims& d = *a.dims;
     const dim3 grid(d.num_kv_heads, a.cache->batch);
-    qrot_kernel<GQ><<<grid, 128, 0, s>>>(
+    qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
         a.ws + a.lay.off_qpack);
@@ -513,6 +527,7 @@ struct HistValuRun {
     p.hkv = d.num_kv_heads;
     p.hq = d.num_q_heads;
     p.splits = a.lay.splits;
+    p.parts = a.lay.parts;
     p.pages_per_split = a.lay.pages_per_split;
     const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
     switch (d.group_size) {
@@ -539,9 +554,10 @@ struct Bf16Run {
     p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
     p.hkv = d.num_kv_heads;
     p.hq = d.num_q_heads;
-    p.splits = a.lay.splits;
-    const dim3 grid(d.num_kv_heads, a.cache->batch);
-    bf16_kernel<GQ><<<grid, 256, 0, s>>>(p);
+    p.parts = a.lay.parts;
+    p.first_part = a.lay.splits;
+    const dim3 grid(kBf16Parts, d.num_kv_heads, a.cache->batch);
+    bf16_kernel<GQ><<<grid, 64, 0, s>>>(p);
     return hipGetLastError();
   }
 };
@@ -552,9 +568,9 @@ struct MergeRun {
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
                         hipStream_t s) {
     const dim3 grid(d.num_kv_heads, batch);
-    merge_kernel<GQ><<<grid, 128, 0, s>>>(reinterpret_cast<const float*>(ws + lay.off_po),
+    merge_kernel<GQ><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(ws + lay.off_po),
                                           reinterpret_cast<const float*>(ws + lay.off_plse),
-                                          rot.r_v, d.num_q_heads, lay.splits, out, lse_out);
+                                          rot.r_v, d.num_q_heads, lay.splits, lay.parts, out, lse_out);
     return hipGetLastError();
   }
 };

@@ -1,11 +1,412 @@
-// Matrix-core (MFMA) history kernel: not built yet; the vector-ALU kernel
-// serves every shape until it is.
+// Matrix-core history kernel: split-K decode attention over INT2 history
+// pages (page "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务",
+// section "OSCAR的另一个关键点是": unpack, scale/zero dequantization and
+// float accumulation of the INT2 history), built on v_mfma_i32_16x16x64_i8.
+//
+// The vector-ALU form needs ~1000 fp32 FMAs per history token and KV head
+// (q.k and p.v for four query heads), twice what the vector ALU can retire
+// while HBM streams the 72 bytes that token costs.  Both contractions are
+// exact integer products here:
+//   q . code   A = the rotated query as 3-digit signed base-256 fixed point
+//              (rows = head x digit), B = 2-bit codes as int8 (0..3);
+//   P' . code  A = p * value-scale per token as 4 unsigned base-128 digits
+//              (rows = head x digit), B = value codes as int8.
+// Codes become int8 operands with one shift + one mask per four of them.
+//
+// Softmax bookkeeping is amortised over pages.  Each head keeps a reference
+// maximum m and a fixed-point unit u; tokens use p = 2^(score - m) and
+// digits of p * scale / u, so the P' . code products of many pages add up
+// exactly in the MFMA's int32 accumulator, and l = sum p and the zero-point
+// sum p * zero stay per-lane partial sums.  A head "re-bases" (its int32
+// accumulator is folded into float, everything rescaled by 2^(m_old - m_new),
+// and a new unit taken from the current page) only when a score exceeds m by
+// more than kSlack or a value would overflow the digits; that branch is
+// uniform across the wave and rare once the first page has set m.
+//
+// One wave per workgroup; the workgroup owns (history split, KV head,
+// request).  Per 64-token page a lane loads 4 x 16 B of codes and the
+// scale/zero entries of its tokens (the page layout puts each lane's MFMA
+// operands in one 16-byte load); the loads of page p+1 are in flight while
+// page p is processed (two register buffers, no copies).  Query heads are
+// handled in blocks of four (16 MFMA rows = 4 heads x 4 digit rows; the
+// query uses three of them).
+#include <math.h>
+
+#include "oscar_device.h"
 #include "oscar_internal.h"
 
 namespace oscar {
+namespace {
 
-bool hist_mfma_supported(const oscar_dims&) { return false; }
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-hipError_t launch_hist_mfma(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
+constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
+constexpr float kDigitMax = 268435455.0f;      // 4 unsigned base-128 digits: x < 2^28
+
+// Codes at positions 4b+j of a 16-code word -> byte b of result j.
+__device__ __forceinline__ v4i unpack16(uint32_t w) {
+  v4i r;
+  r.x = static_cast<int>(w & 0x03030303u);
+  r.y = static_cast<int>((w >> 2) & 0x03030303u);
+  r.z = static_cast<int>((w >> 4) & 0x03030303u);
+  r.w = static_cast<int>((w >> 6) & 0x03030303u);
+  return r;
+}
+
+// value of the signed base-256 digit rows of q . code
+__device__ __forceinline__ float q_digits(const v4i& d) {
+  const int lo = d.x + (d.y << 8);   // |d.y| <= 49152: fits
+  return static_cast<float>(lo) + 65536.f * static_cast<float>(d.z);
+}
+
+// value of the unsigned base-128 digit rows of P' . code (accumulated)
+__device__ __forceinline__ float p_digits(const v4i& d) {
+  return static_cast<float>(d.x) + 128.f * static_cast<float>(d.y) + 16384.f * static_cast<float>(d.z) +
+         2097152.f * static_cast<float>(d.w);
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+template <typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  int x = __float_as_int(v);
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
+  return __int_as_float(x);
+}
+
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+struct MfmaParams {
+  const uint8_t* pages;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const uint8_t* qpack;
+  const float* qsum;
+  float* po;
+  float* plse;
+  int32_t max_pages;
+  int32_t hkv;
+  int32_t hq;
+  int32_t gq;
+  int32_t splits;
+  int32_t parts;
+  int32_t pages_per_split;
+};
+
+template <int G>
+struct PageRegs {
+  static constexpr int NG = kDim / G;
+  v4i kw[2];              // key words: half hf, word m -> token tau(m, n), word d = 4 hf + lane group
+  v4i vw[2];              // value words: load r, word m -> channel block 4 r + m
+  uint32_t ksz[4 * NG];   // (scale, zero) bf16 pairs of tokens tau(m, n), [m][group]
+  uint32_t vsz[4 * NG];
+};
+
+template <int G>
+__device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ blk, int lane) {
+  constexpr int NG = kDim / G;
+  const int n = lane & 15;
+  r.kw[0] = *reinterpret_cast<const v4i*>(blk + lane * 16);
+  r.kw[1] = *reinterpret_cast<const v4i*>(blk + 1024 + lane * 16);
+  r.vw[0] = *reinterpret_cast<const v4i*>(blk + 2048 + lane * 16);
+  r.vw[1] = *reinterpret_cast<const v4i*>(blk + 3072 + lane * 16);
+  const uint32_t* ks = reinterpret_cast<const uint32_t*>(blk + kCodesBytes) + n * 4 * NG;
+  const uint32_t* vs = reinterpret_cast<const uint32_t*>(blk + kCodesBytes + kPage * NG * 4) + n * 4 * NG;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const v4i a = reinterpret_cast<const v4i*>(ks)[i];
+    const v4i b = reinterpret_cast<const v4i*>(vs)[i];
+    r.ksz[4 * i + 0] = a.x; r.ksz[4 * i + 1] = a.y; r.ksz[4 * i + 2] = a.z; r.ksz[4 * i + 3] = a.w;
+    r.vsz[4 * i + 0] = b.x; r.vsz[4 * i + 1] = b.y; r.vsz[4 * i + 2] = b.z; r.vsz[4 * i + 3] = b.w;
+  }
+}
+
+template <int NHB, int G>
+struct WaveState {
+  static constexpr int NG = kDim / G;
+  v4i qa[NHB][2];          // query digit operands
+  float qs[NHB];           // query fixed-point unit of this lane's head
+  float qz[NHB][NG];       // per-group query sums (zero-point term of the score)
+  float m_ref[NHB];        // reference maximum (log2 units)
+  float unit[NHB][NG];     // P' fixed-point unit
+  float inv[NHB][NG];      // 1 / unit
+  v4i dacc[NHB][8];        // int32 digit accumulators of P' . code, channel block cb
+  float accf[NHB][8];      // folded float accumulators
+  float ls[NHB];           // per-lane partial sum of p
+  float zs[NHB][NG];       // per-lane partial sum of p * value zero
+};
+
+// Fold the int32 accumulators of flagged heads into float, rescale to the
+// new reference max and take a new P' unit from the current page.
+template <int NHB, int G>
+__device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[NHB][4],
+                                    const PageRegs<G>& cur, const bool (&need)[NHB]) {
+  constexpr int NG = kDim / G;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float pm = row_reduce(fmaxf(fmaxf(sc[hb][0], sc[hb][1]), fmaxf(sc[hb][2], sc[hb][3])), MaxOp());
+    const float m_new = need[hb] ? fmaxf(st.m_ref[hb], pm) : st.m_ref[hb];
+    const float alpha = need[hb] ? exp2f(st.m_ref[hb] - m_new) : 1.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const int gi = (16 * cb) / G;
+      const float folded = (st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb])) * alpha;
+      st.accf[hb][cb] = need[hb] ? folded : st.accf[hb][cb];
+      const v4i z = {0, 0, 0, 0};
+      st.dacc[hb][cb] = need[hb] ? z : st.dacc[hb][cb];
+    }
+    st.ls[hb] *= alpha;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      st.zs[hb][gi] *= alpha;
+      float wmax = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float p = exp2f(sc[hb][m] - m_new);
+        wmax = fmaxf(wmax, p * __uint_as_float(cur.vsz[m * NG + gi] << 16));
+      }
+      wmax = row_reduce(wmax, MaxOp());
+      const float u = fmaxf(wmax, 1e-30f) * (kHeadroom / kDigitMax);
+      st.unit[hb][gi] = need[hb] ? u : st.unit[hb][gi];
+      st.inv[hb][gi] = need[hb] ? 1.f / u : st.inv[hb][gi];
+    }
+    st.m_ref[hb] = m_new;
+  }
+}
+
+template <int NHB, int G>
+__device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
+                                             int n_hist, int lane, int32_t (*pop)[16][16]) {
+  constexpr int NG = kDim / G;
+  const int n = lane & 15, lg = lane >> 4;
+  // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n
+  float sc[NHB][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const v4i b0 = unpack16(static_cast<uint32_t>(cur.kw[0][m]));
+    const v4i b1 = unpack16(static_cast<uint32_t>(cur.kw[1][m]));
+    const bool valid = tok_base + 16 * (n >> 2) + 4 * m + (n & 3) < n_hist;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const v4i zero = {0, 0, 0, 0};
+      float s;
+      if constexpr (NG == 1) {
+        v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
+        const uint32_t sz = cur.ksz[m];
+        s = __builtin_fmaf(__uint_as_float(sz << 16) * st.qs[hb], q_digits(d),
+                           __uint_as_float(sz & 0xFFFF0000u) * st.qz[hb][0]);
+      } else {
+        const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+        const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
+        const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
+        s = __builtin_fmaf(__uint_as_float(s0 << 16) * st.qs[hb], q_digits(d0),
+                           __uint_as_float(s0 & 0xFFFF0000u) * st.qz[hb][0]) +
+            __builtin_fmaf(__uint_as_float(s1 << 16) * st.qs[hb], q_digits(d1),
+                           __uint_as_float(s1 & 0xFFFF0000u) * st.qz[hb][1]);
+      }
+      sc[hb][m] = valid ? s : -INFINITY;
+    }
+  }
+  // ---- p against the reference max, P' in units of the head's fixed point
+  float pr[NHB][4], xv[NHB][NG][4];
+  bool flag = false;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      pr[hb][m] = exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
+      flag |= sc[hb][m] > st.m_ref[hb] + kSlack;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
+        flag |= xv[hb][gi][m] > kDigitMax;
+      }
+    }
+  // ---- re-base the heads that need a new reference max or unit (rare)
+  const uint64_t mask = __ballot(flag);
+  if (mask != 0) {
+    bool need[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) need[hb] = ((mask >> (16 * lg)) & 0xFFFFull) != 0;
+    rebase<NHB, G>(st, sc, cur, need);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        pr[hb][m] = exp2f(sc[hb][m] - st.m_ref[hb]);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
+      }
+  }
+  // ---- P' digits into the operand rows, l and zero-point partial sums
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.ls[hb] += pr[hb][m];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      uint32_t dig0 = 0, dig1 = 0, dig2 = 0, dig3 = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t sz = cur.vsz[m * NG + gi];
+        st.zs[hb][gi] = __builtin_fmaf(pr[hb][m], __uint_as_float(sz & 0xFFFF0000u), st.zs[hb][gi]);
+        const uint32_t x = static_cast<uint32_t>(xv[hb][gi][m] + 0.5f);
+        dig0 |= (x & 127u) << (8 * m);
+        dig1 |= ((x >> 7) & 127u) << (8 * m);
+        dig2 |= ((x >> 14) & 127u) << (8 * m);
+        dig3 |= (x >> 21) << (8 * m);
+      }
+      // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
+      pop[hb * NG + gi][4 * lg + 0][n] = static_cast<int32_t>(dig0);
+      pop[hb * NG + gi][4 * lg + 1][n] = static_cast<int32_t>(dig1);
+      pop[hb * NG + gi][4 * lg + 2][n] = static_cast<int32_t>(dig2);
+      pop[hb * NG + gi][4 * lg + 3][n] = static_cast<int32_t>(dig3);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- P' . code accumulated in int32: column n = channel 16 cb + n, rows = head x digit
+  v4i pa[NHB][NG];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&pop[hb * NG + gi][n][lg * 4]);
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int gi = (16 * cb) / G;
+    const v4i bv = unpack16(static_cast<uint32_t>(cur.vw[cb >> 2][cb & 3]));
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      st.dacc[hb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], bv, st.dacc[hb][cb], 0, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NHB, int G>
+__global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
+  constexpr int NG = kDim / G;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
+  // P' operand rows: [head block x group][row = 4 h + digit][16 dwords]
+  __shared__ int32_t pop[NHB * NG][16][16];
+
+  const int L = a.seq_lens[b];
+  const int n_hist = max(0, L - kBf16Tokens);
+  const int n_pages = (n_hist + kPage - 1) / kPage;
+  const int p0 = split * a.pages_per_split;
+  const int p1 = min(p0 + a.pages_per_split, n_pages);
+
+  WaveState<NHB, G> st;
+  const uint8_t* qp = a.qpack + (static_cast<size_t>(b) * a.hkv + kvh) * kQPackBytes;
+  const float* qscale = reinterpret_cast<const float*>(qp + kQPackOperandBytes);
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * a.gq;
+  bool head_ok[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + ((hf * 4 + lg) * kQPackRows + hb * 16 + n) * 16);
+    const int h = 4 * hb + lg;
+    head_ok[hb] = h < a.gq;
+    st.qs[hb] = qscale[h];
+    st.m_ref[hb] = -INFINITY;
+    st.ls[hb] = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      st.qz[hb][gi] = head_ok[hb] ? a.qsum[(head0 + h) * 4 + gi] : 0.f;
+      st.unit[hb][gi] = 0.f;
+      st.inv[hb][gi] = 0.f;
+      st.zs[hb][gi] = 0.f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      st.dacc[hb][cb] = v4i{0, 0, 0, 0};
+      st.accf[hb][cb] = 0.f;
+    }
+  }
+  const size_t pt_row = static_cast<size_t>(b) * a.max_pages;
+  const size_t blk_stride = static_cast<size_t>(a.hkv) * block_bytes(G);
+  const uint8_t* base = a.pages + static_cast<size_t>(kvh) * block_bytes(G);
+  PageRegs<G> ra, rb;
+  if (p0 < p1) load_page<G>(ra, base + a.page_table[pt_row + p0] * blk_stride, lane);
+  for (int p = p0; p < p1; p += 2) {
+    if (p + 1 < p1) load_page<G>(rb, base + a.page_table[pt_row + p + 1] * blk_stride, lane);
+    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, pop);
+    if (p + 1 >= p1) break;
+    if (p + 2 < p1) load_page<G>(ra, base + a.page_table[pt_row + p + 2] * blk_stride, lane);
+    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, pop);
+  }
+
+  // ---- partial output of this split (rotated value domain)
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float l = row_reduce(st.ls[hb], AddOp());
+    float zsum[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) zsum[gi] = row_reduce(st.zs[hb][gi], AddOp());
+    if (!head_ok[hb]) continue;
+    const int h = 4 * hb + lg;
+    const size_t pidx = (head0 + h) * a.parts + split;
+    const bool any = l > 0.f;
+    const float inv_l = any ? 1.f / l : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const int gi = (16 * cb) / G;
+      const float o = st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb]) + zsum[gi];
+      a.po[pidx * kDim + 16 * cb + n] = o * inv_l;
+    }
+    if (n == 0) a.plse[pidx] = any ? (st.m_ref[hb] + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int NHB, int G>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  const oscar_dims& d = *a.dims;
+  MfmaParams p;
+  p.pages = a.cache->pages;
+  p.page_table = a.cache->page_table;
+  p.seq_lens = a.cache->seq_lens;
+  p.qpack = a.ws + a.lay.off_qpack;
+  p.qsum = reinterpret_cast<const float*>(a.ws + a.lay.off_qsum);
+  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
+  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+  p.max_pages = a.cache->max_pages_per_req;
+  p.hkv = d.num_kv_heads;
+  p.hq = d.num_q_heads;
+  p.gq = d.num_q_heads / d.num_kv_heads;
+  p.splits = a.lay.splits;
+  p.parts = a.lay.parts;
+  p.pages_per_split = a.lay.pages_per_split;
+  const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
+  hist_mfma_kernel<NHB, G><<<grid, 64, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool hist_mfma_supported(const oscar_dims& d) {
+  const int g = d.num_q_heads / d.num_kv_heads;
+  return (d.group_size == 64 || d.group_size == 128) && g >= 1 && g <= 8;
+}
+
+hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s) {
+  const int g = a.dims->num_q_heads / a.dims->num_kv_heads;
+  const bool two = g > 4;
+  if (a.dims->group_size == 64) return two ? launch_t<2, 64>(a, s) : launch_t<1, 64>(a, s);
+  return two ? launch_t<2, 128>(a, s) : launch_t<1, 128>(a, s);
+}
 
 }  // namespace oscar

@@ -10,10 +10,13 @@
 //
 // A workgroup has 128 threads, thread k owning stored channel k.  The
 // rotation is a 128x128 GEMV per token with the rotation row read once per
-// workgroup and reused across its tokens; accumulation order is i = 0..127
-// with fused multiply-add.  Quantization uses IEEE float32 subtraction and
-// division (no fast-math) and round-half-even, so the codes and the bf16
-// scale/zero are a deterministic function of the rotated values.
+// workgroup and reused across its tokens.  A bf16 x float32 product is exact
+// in float64, so the GEMV accumulates in float64 and rounds once to float32:
+// the stored value is the rounded exact dot product except where the
+// float64 rounding of the sum lands within ~2^-22 ulp of a float32 tie.
+// Quantization uses IEEE float32 subtraction and division (no fast-math)
+// and round-half-even, so the codes and the bf16 scale/zero are a
+// deterministic function of the rotated values.
 #include "oscar_device.h"
 #include "oscar_internal.h"
 
@@ -37,47 +40,73 @@ struct QuantSmem {
 template <int G, int NT>
 __device__ void quantize_tokens(QuantSmem<G, NT>& sm, int nt, const float* __restrict__ r,
                                 const float* __restrict__ clipv) {
-  constexpr int NG = kDim / G;
-  const int k = threadIdx.x;
-  float acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-  for (int i = 0; i < kDim; ++i) {
-    const float rik = r[i * kDim + k];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(sm.x[t][i], rik, acc[t]);
-  }
-  const float c = clipv[k];
+  constexpr int WG = G < 64 ? G : 64;   // group lanes inside one wave
+  const int k = threadIdx.x, lane = k & 63, wave = k >> 6;
+  __shared__ float xw[2][NT][2];        // per-wave (min, max) when a group spans both waves
+  double acc[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    if (t < nt) sm.y[t][k] = fminf(fmaxf(acc[t], -c), c);
-  __syncthreads();
-  for (int job = k; job < nt * NG; job += kDim) {
-    const int t = job / NG, gi = job % NG;
-    float mn = sm.y[t][gi * G], mx = mn;
-    for (int j = 1; j < G; ++j) {
-      const float v = sm.y[t][gi * G + j];
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
+  for (int i = 0; i < kDim; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double rik = static_cast<double>(r[(i + u) * kDim + k]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
     }
-    const float range = mx - mn;
-    sm.scale[t][gi] = bf16_round(range / 3.0f);
-    sm.zero[t][gi] = bf16_round(mn);
   }
-  __syncthreads();
+  const float c = clipv[k];
+  float y[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (t < nt) {
-      const float s = sm.scale[t][k / G];
-      const float z = sm.zero[t][k / G];
-      int code = 0;
-      if (s != 0.f) {
-        const float diff = sm.y[t][k] - z;
-        const float q = rintf(diff / s);
-        code = static_cast<int>(fminf(fmaxf(q, 0.f), 3.f));
-      }
-      sm.code[t][k] = static_cast<uint8_t>(code);
+    const double sum = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
+    y[t] = fminf(fmaxf(static_cast<float>(sum), -c), c);
+    sm.y[t][k] = y[t];
+  }
+  // group min / max across the G lanes of a group
+  float mn[NT], mx[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    mn[t] = y[t];
+    mx[t] = y[t];
+#pragma unroll
+    for (int off = 1; off < WG; off <<= 1) {
+      mn[t] = fminf(mn[t], __shfl_xor(mn[t], off, 64));
+      mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], off, 64));
     }
+  }
+  if constexpr (G == 128) {
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        xw[wave][t][0] = mn[t];
+        xw[wave][t][1] = mx[t];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      mn[t] = fminf(xw[0][t][0], xw[1][t][0]);
+      mx[t] = fmaxf(xw[0][t][1], xw[1][t][1]);
+    }
+  }
+  const int gi = k / G;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float range = mx[t] - mn[t];
+    const float s = bf16_round(range / 3.0f);
+    const float z = bf16_round(mn[t]);
+    if (k % G == 0 && t < nt) {
+      sm.scale[t][gi] = s;
+      sm.zero[t][gi] = z;
+    }
+    int code = 0;
+    if (s != 0.f) {
+      const float diff = y[t] - z;
+      const float q = rintf(diff / s);
+      code = static_cast<int>(fminf(fmaxf(q, 0.f), 3.f));
+    }
+    if (t < nt) sm.code[t][k] = static_cast<uint8_t>(code);
   }
   __syncthreads();
 }

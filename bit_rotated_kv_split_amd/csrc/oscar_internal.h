@@ -10,15 +10,22 @@
 
 namespace oscar {
 
+// Partials per (request, query head): S history splits, then the bf16
+// sink/recent chunks (the sink and four quarters of the ring).
+constexpr int kBf16Parts = 5;
+constexpr int kMaxSplits = 251;
+constexpr int kMaxParts = kMaxSplits + kBf16Parts;
+
 // Workspace layout of one decode call (offsets in bytes, 256-aligned).
 struct WsLayout {
   int32_t splits = 1;           // history splits S
+  int32_t parts = 1 + kBf16Parts;
   int32_t pages_per_split = 0;  // pages one split covers
   size_t off_qrot = 0;          // float [B][Hq][128]: R_K-rotated query * log2(e)/sqrt(128)
   size_t off_qsum = 0;          // float [B][Hq][4]: per-group sums of that query
   size_t off_qpack = 0;         // matrix-core operands, kQPackBytes per (b, kv head)
-  size_t off_po = 0;            // float [B][Hq][S+1][128] partial outputs (S = bf16 partial)
-  size_t off_plse = 0;          // float [B][Hq][S+1] partial log-sum-exp (natural log)
+  size_t off_po = 0;            // float [B][Hq][parts][128] partial outputs
+  size_t off_plse = 0;          // float [B][Hq][parts] partial log-sum-exp (natural log)
   size_t total = 0;
 };
 

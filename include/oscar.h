@@ -113,7 +113,8 @@ size_t oscar_block_bytes(int32_t group_size);
  * "OSCAR的另一个关键点是": the oldest recent token is rotated, clipped,
  * quantized and packed into history).  seq_lens already count the new token.
  * For each request with L > 320 and each KV head, the token at position
- * L-257 is read from its recent slot, stored as y = x . R (float32), clipped
+ * L-257 is read from its recent slot, stored as y = x . R (exact products,
+ * float64 accumulation, rounded once to float32), clipped
  * to [-c, c] per channel, quantized per group of G channels (zero = bf16(min),
  * scale = bf16((max-min)/3), code = clamp(rint((y-zero)/scale), 0, 3), code 0
  * when scale = 0) and packed into history index L-321 (key and value).

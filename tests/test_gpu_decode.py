@@ -148,7 +148,7 @@ def test_valu_and_mfma_agree():
         if e.code == ok.OSCAR_EUNSUPPORTED:
             pytest.skip(str(e))
         raise
-    assert_close(b, a, "valu vs mfma", atol=1e-4, rel_l2=1e-4)
+    assert_close(b, a, "valu vs mfma", atol=2e-4, rel_l2=2e-5)
 
 
 def test_full_step_sequence_matches_oracle():
