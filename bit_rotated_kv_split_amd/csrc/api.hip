@@ -84,9 +84,15 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
   WsLayout w;
   const int pages = pages_for(max_seq_len);
   const int pairs = batch * d.num_kv_heads;
-  // Enough workgroups to fill 256 compute units several times over, without
-  // making a split shorter than 8 pages.
-  constexpr int kTargetWorkgroups = 2048;
+  // About as many workgroups as the history kernel keeps resident (256
+  // compute units x 4 SIMDs x 2 waves), without making a split shorter than
+  // 8 pages.
+#ifndef OSCAR_TARGET_WORKGROUPS
+#define OSCAR_TARGET_WORKGROUPS 2048
+#endif
+  // the eight-head history kernel keeps one wave per SIMD resident
+  const int kTargetWorkgroups =
+      d.num_q_heads / d.num_kv_heads > 4 ? OSCAR_TARGET_WORKGROUPS / 2 : OSCAR_TARGET_WORKGROUPS;
   int splits = 1;
   if (pages > 0 && pairs > 0) {
     splits = (kTargetWorkgroups + pairs - 1) / pairs;
@@ -249,13 +255,12 @@ int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const o
   const bool use_mfma = kind == 2 || (kind == 0 && hist_mfma_supported(*dims));
   if (kind == 2 && !hist_mfma_supported(*dims))
     return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
-  const bool timed = g_ev_before != nullptr && g_ev_after != nullptr;
-  if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(g_ev_before), s)) != hipSuccess)
-    return hip_fail(e, "event record");
+  if (g_ev_before != nullptr && g_ev_after != nullptr) {
+    a.ev_start = static_cast<hipEvent_t>(g_ev_before);
+    a.ev_stop = static_cast<hipEvent_t>(g_ev_after);
+  }
   e = use_mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
   if (e != hipSuccess) return hip_fail(e, "history launch");
-  if (timed && (e = hipEventRecord(static_cast<hipEvent_t>(g_ev_after), s)) != hipSuccess)
-    return hip_fail(e, "event record");
   e = launch_bf16(a, s);
   if (e != hipSuccess) return hip_fail(e, "bf16 launch");
   return OSCAR_OK;

@@ -5,7 +5,7 @@
 //
 //   qrot_kernel      q . R_K per (request, head), pre-scaled by log2(e)/sqrt(d),
 //                    plus the per-group sums the zero-point term needs and
-//                    the int8 limb operands of the matrix-core kernel.
+//                    the int8 digit operands of the matrix-core kernel.
 //   hist_valu_kernel split-K over history pages on the vector ALU: lane =
 //                    token for q.k, lane = channel pair for p.v.
 //   bf16_kernel      sink + recent tokens with the unrotated query.
@@ -16,6 +16,7 @@
 //   q_rot . k_hat = sum_groups ( scale * (q_rot . code) + zero * sum(q_rot) )
 // and the value side accumulates (p * scale) * code plus (p * zero) per group,
 // so dequantized values are never formed element by element.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "oscar_device.h"
@@ -24,10 +25,9 @@
 namespace oscar {
 namespace {
 
-// Largest magnitude of the int8-limb fixed-point query: three signed base-256
-// digits represent every integer of magnitude <= 2^23 - 2^17 with digit 2 in
-// [-127, 126].
-constexpr float kQFixMax = 8257536.0f;
+// Fixed-point range of the matrix-core query operand: q * 2^26 / max|q|,
+// held as four signed base-256 digits.
+constexpr float kQFixMax = 67108864.0f;
 
 template <int GQ>
 __global__ void __launch_bounds__(256)
@@ -82,25 +82,31 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     }
   }
   __syncthreads();
-  // int8 limb operands: row = 4*h + limb (limb 3 = zero pad), 32 rows; for
-  // channel half hf and lane group kg, byte e = 4*j + b2 of the row holds
-  // channel 16*(4*hf + kg) + 4*b2 + j.
+  // int8 digit operands: row = 4*h + digit, 32 rows; for channel half hf and
+  // lane group kg, byte e = 4*j + b2 of the row holds channel
+  // 16*(4*hf + kg) + 4*b2 + j.  The matrix-core kernel feeds that channel's
+  // 2-bit code masked in place, i.e. multiplied by 4^j for j < 3, so the
+  // operand holds q / 4^j for those slots (rounded on its own, coarser grid).
   uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
   for (int idx = tid; idx < 2 * 4 * kQPackRows * 16; idx += 256) {
     const int e = idx & 15;
     const int row = (idx >> 4) & (kQPackRows - 1);
     const int kg = (idx >> 9) & 3;
     const int hf = idx >> 11;
-    const int h = row >> 2, limb = row & 3;
+    const int h = row >> 2, digit = row & 3;
     int8_t val = 0;
-    if (h < GQ && limb < 3) {
-      const int ch = 16 * (4 * hf + kg) + 4 * (e & 3) + (e >> 2);
-      const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h]));
+    if (h < GQ) {
+      const int j = e >> 2;
+      const int ch = 16 * (4 * hf + kg) + 4 * (e & 3) + j;
+      const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : 1.f);
+      const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h] * slot));
       const int d0 = ((qi + 128) & 255) - 128;
       const int q1 = (qi - d0) >> 8;
       const int d1 = ((q1 + 128) & 255) - 128;
-      const int d2 = (q1 - d1) >> 8;
-      val = static_cast<int8_t>(limb == 0 ? d0 : (limb == 1 ? d1 : d2));
+      const int q2 = (q1 - d1) >> 8;
+      const int d2 = ((q2 + 128) & 255) - 128;
+      const int d3 = (q2 - d2) >> 8;
+      val = static_cast<int8_t>(digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3)));
     }
     qp[idx] = static_cast<uint8_t>(val);
   }
@@ -530,12 +536,20 @@ struct HistValuRun {
     p.parts = a.lay.parts;
     p.pages_per_split = a.lay.pages_per_split;
     const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
+    const bool timed = a.ev_start != nullptr && a.ev_stop != nullptr;
     switch (d.group_size) {
-      case 32: hist_valu_kernel<GQ, 32><<<grid, 256, 0, s>>>(p); break;
-      case 64: hist_valu_kernel<GQ, 64><<<grid, 256, 0, s>>>(p); break;
-      default: hist_valu_kernel<GQ, 128><<<grid, 256, 0, s>>>(p); break;
+      case 32: launch(hist_valu_kernel<GQ, 32>, grid, timed, a, p, s); break;
+      case 64: launch(hist_valu_kernel<GQ, 64>, grid, timed, a, p, s); break;
+      default: launch(hist_valu_kernel<GQ, 128>, grid, timed, a, p, s); break;
     }
     return hipGetLastError();
+  }
+  template <typename K>
+  static void launch(K kernel, dim3 grid, bool timed, const DecodeArgs& a, const HistParams& p, hipStream_t s) {
+    if (timed)
+      hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, p);
+    else
+      kernel<<<grid, 256, 0, s>>>(p);
   }
 };
 

@@ -7,11 +7,15 @@
 // (q.k and p.v for four query heads), twice what the vector ALU can retire
 // while HBM streams the 72 bytes that token costs.  Both contractions are
 // exact integer products here:
-//   q . code   A = the rotated query as 3-digit signed base-256 fixed point
-//              (rows = head x digit), B = 2-bit codes as int8 (0..3);
+//   q . code   A = the rotated query as 4-digit signed base-256 fixed point
+//              (rows = head x digit), B = 2-bit codes as int8;
 //   P' . code  A = p * value-scale per token as 4 unsigned base-128 digits
 //              (rows = head x digit), B = value codes as int8.
-// Codes become int8 operands with one shift + one mask per four of them.
+// A word of sixteen 2-bit codes gives the four int8 operand registers as
+// w & 0x03030303 << 2j (j = 0, 1, 2: the code times 4^j, masked in place)
+// and (w >> 6) & 0x03030303, five operations; the A operand of those slots
+// carries the matching 4^-j (query digits are rounded on that grid, P'
+// digits are computed from floats and lose nothing).
 //
 // Softmax bookkeeping is amortised over pages.  Each head keeps a reference
 // maximum m and a fixed-point unit u; tokens use p = 2^(score - m) and
@@ -26,11 +30,12 @@
 // One wave per workgroup; the workgroup owns (history split, KV head,
 // request).  Per 64-token page a lane loads 4 x 16 B of codes and the
 // scale/zero entries of its tokens (the page layout puts each lane's MFMA
-// operands in one 16-byte load); the loads of page p+1 are in flight while
-// page p is processed (two register buffers, no copies).  Query heads are
-// handled in blocks of four (16 MFMA rows = 4 heads x 4 digit rows; the
-// query uses three of them).
+// operands in one 16-byte load); the loads of pages p+1 and p+2 are in
+// flight while page p is processed (three register buffers, no copies).  Query heads are
+// handled in blocks of four (16 MFMA rows = 4 heads x 4 digit rows).
 #include <math.h>
+
+#include <hip/hip_ext.h>
 
 #include "oscar_device.h"
 #include "oscar_internal.h"
@@ -40,24 +45,31 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// Launch-shape knob (compile-time): register page buffers per wave for the
+// four-head, G = 128 variant (2 or 3); the larger variants use 2.
+#ifndef OSCAR_HIST_BUFFERS
+#define OSCAR_HIST_BUFFERS 3
+#endif
+
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
 constexpr float kDigitMax = 268435455.0f;      // 4 unsigned base-128 digits: x < 2^28
 
-// Codes at positions 4b+j of a 16-code word -> byte b of result j.
+// Codes at positions 4b+j of a 16-code word -> byte b of result j, times
+// 4^j for j < 3.
 __device__ __forceinline__ v4i unpack16(uint32_t w) {
   v4i r;
   r.x = static_cast<int>(w & 0x03030303u);
-  r.y = static_cast<int>((w >> 2) & 0x03030303u);
-  r.z = static_cast<int>((w >> 4) & 0x03030303u);
+  r.y = static_cast<int>(w & 0x0C0C0C0Cu);
+  r.z = static_cast<int>(w & 0x30303030u);
   r.w = static_cast<int>((w >> 6) & 0x03030303u);
   return r;
 }
 
 // value of the signed base-256 digit rows of q . code
 __device__ __forceinline__ float q_digits(const v4i& d) {
-  const int lo = d.x + (d.y << 8);   // |d.y| <= 49152: fits
-  return static_cast<float>(lo) + 65536.f * static_cast<float>(d.z);
+  const int lo = d.x + (d.y << 8);   // |d.x|, |d.y| <= 128 * 128 * 48: fits
+  return static_cast<float>(lo) + 65536.f * static_cast<float>(d.z) + 16777216.f * static_cast<float>(d.w);
 }
 
 // value of the unsigned base-128 digit rows of P' . code (accumulated)
@@ -137,7 +149,7 @@ struct WaveState {
   float qz[NHB][NG];       // per-group query sums (zero-point term of the score)
   float m_ref[NHB];        // reference maximum (log2 units)
   float unit[NHB][NG];     // P' fixed-point unit
-  float inv[NHB][NG];      // 1 / unit
+  float inv[NHB][NG];      // 4^-j / unit for this lane's token residue j
   v4i dacc[NHB][8];        // int32 digit accumulators of P' . code, channel block cb
   float accf[NHB][8];      // folded float accumulators
   float ls[NHB];           // per-lane partial sum of p
@@ -150,6 +162,10 @@ template <int NHB, int G>
 __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[NHB][4],
                                     const PageRegs<G>& cur, const bool (&need)[NHB]) {
   constexpr int NG = kDim / G;
+  // P' of this lane's tokens (residue j = n % 4 in the K-slot order) meets
+  // codes masked in place, i.e. times 4^j for j < 3: carry 4^-j here
+  const int jr = threadIdx.x & 3;
+  const float slot = jr == 1 ? 0.25f : (jr == 2 ? 0.0625f : 1.f);
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float pm = row_reduce(fmaxf(fmaxf(sc[hb][0], sc[hb][1]), fmaxf(sc[hb][2], sc[hb][3])), MaxOp());
@@ -176,7 +192,7 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
       wmax = row_reduce(wmax, MaxOp());
       const float u = fmaxf(wmax, 1e-30f) * (kHeadroom / kDigitMax);
       st.unit[hb][gi] = need[hb] ? u : st.unit[hb][gi];
-      st.inv[hb][gi] = need[hb] ? 1.f / u : st.inv[hb][gi];
+      st.inv[hb][gi] = need[hb] ? slot / u : st.inv[hb][gi];
     }
     st.m_ref[hb] = m_new;
   }
@@ -223,7 +239,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      pr[hb][m] = exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
+      pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
       flag |= sc[hb][m] > st.m_ref[hb] + kSlack;
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
@@ -242,7 +258,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        pr[hb][m] = exp2f(sc[hb][m] - st.m_ref[hb]);
+        pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
           xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
@@ -295,7 +311,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NHB, int G>
+template <int NHB, int G, int BUF>
 __global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
   constexpr int NG = kDim / G;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -337,17 +353,48 @@ __global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
       st.accf[hb][cb] = 0.f;
     }
   }
-  const size_t pt_row = static_cast<size_t>(b) * a.max_pages;
+  // Page-table entries of the split, 64 at a time in one register (lane i
+  // holds entry base + i) and broadcast with readlane: page addresses need
+  // no dependent load inside the loop.
+  const int32_t* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
   const size_t blk_stride = static_cast<size_t>(a.hkv) * block_bytes(G);
   const uint8_t* base = a.pages + static_cast<size_t>(kvh) * block_bytes(G);
-  PageRegs<G> ra, rb;
-  if (p0 < p1) load_page<G>(ra, base + a.page_table[pt_row + p0] * blk_stride, lane);
-  for (int p = p0; p < p1; p += 2) {
-    if (p + 1 < p1) load_page<G>(rb, base + a.page_table[pt_row + p + 1] * blk_stride, lane);
+  int pt_base = p0;
+  int pt_reg = p0 + lane < p1 ? pt[p0 + lane] : 0;
+  auto page_ptr = [&](int p) -> const uint8_t* {
+    if (p - pt_base >= 64) {   // uniform: every lane sees the same p
+      pt_base += 64;
+      pt_reg = pt_base + lane < p1 ? pt[pt_base + lane] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(pt_reg, p - pt_base);
+    return base + static_cast<size_t>(phys) * blk_stride;
+  };
+  if constexpr (BUF == 3) {
+  // three register buffers: pages p+1 and p+2 are in flight while p is processed
+  PageRegs<G> ra, rb, rc;
+  if (p0 < p1) load_page<G>(ra, page_ptr(p0), lane);
+  if (p0 + 1 < p1) load_page<G>(rb, page_ptr(p0 + 1), lane);
+  for (int p = p0; p < p1; p += 3) {
+    if (p + 2 < p1) load_page<G>(rc, page_ptr(p + 2), lane);
     process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, pop);
     if (p + 1 >= p1) break;
-    if (p + 2 < p1) load_page<G>(ra, base + a.page_table[pt_row + p + 2] * blk_stride, lane);
+    if (p + 3 < p1) load_page<G>(ra, page_ptr(p + 3), lane);
     process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, pop);
+    if (p + 2 >= p1) break;
+    if (p + 4 < p1) load_page<G>(rb, page_ptr(p + 4), lane);
+    process_page<NHB, G>(st, rc, (p + 2) * kPage, n_hist, lane, pop);
+  }
+  } else {
+  // two register buffers: page p+1 is in flight while p is processed
+  PageRegs<G> ra, rb;
+  if (p0 < p1) load_page<G>(ra, page_ptr(p0), lane);
+  for (int p = p0; p < p1; p += 2) {
+    if (p + 1 < p1) load_page<G>(rb, page_ptr(p + 1), lane);
+    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, pop);
+    if (p + 1 >= p1) break;
+    if (p + 2 < p1) load_page<G>(ra, page_ptr(p + 2), lane);
+    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, pop);
+  }
   }
 
   // ---- partial output of this split (rotated value domain)
@@ -374,6 +421,7 @@ __global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
 
 template <int NHB, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int BUF = (NHB == 1 && G == 128) ? OSCAR_HIST_BUFFERS : 2;
   const oscar_dims& d = *a.dims;
   MfmaParams p;
   p.pages = a.cache->pages;
@@ -391,7 +439,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.parts = a.lay.parts;
   p.pages_per_split = a.lay.pages_per_split;
   const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
-  hist_mfma_kernel<NHB, G><<<grid, 64, 0, s>>>(p);
+  if (a.ev_start != nullptr && a.ev_stop != nullptr)
+    hipExtLaunchKernelGGL(hist_mfma_kernel<NHB, G, BUF>, grid, dim3(64), 0, s, a.ev_start, a.ev_stop, 0, p);
+  else
+    hist_mfma_kernel<NHB, G, BUF><<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
 

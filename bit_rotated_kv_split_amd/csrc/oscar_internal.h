@@ -60,6 +60,8 @@ struct DecodeArgs {
   const uint16_t* q;
   uint8_t* ws;
   WsLayout lay;
+  hipEvent_t ev_start = nullptr;   // when both set, the history kernel is launched
+  hipEvent_t ev_stop = nullptr;    // with these as its start/stop timestamps
 };
 
 hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);

@@ -209,9 +209,10 @@ int oscar_set_history_kernel(int kind);
  * 2 = matrix-core; -1 for invalid dims or an unsupported forced choice. */
 int oscar_history_kernel_for(const oscar_dims* dims);
 
-/* Optional timing hook: when both are non-NULL, oscar_decode_attn records
- * hipEvent_t `before` immediately before and `after` immediately after the
- * history kernel launch on its stream.  Thread-local; NULL clears it. */
+/* Optional timing hook: when both are non-NULL, oscar_decode_attn launches
+ * the history kernel with hipEvent_t `before` and `after` as its start and
+ * stop events (hipExtLaunchKernelGGL), so their elapsed time is that
+ * kernel's execution.  Thread-local; NULL clears it. */
 int oscar_set_history_events(void* before, void* after);
 
 /* Thread-local text of the last error ("" if none). */
