@@ -17,7 +17,6 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -65,15 +64,6 @@ def step_bytes(lens: np.ndarray, hkv: int, hq: int, group: int) -> tuple[int, in
     return hist, hist + bf16 + qo + demoted + appended
 
 
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "bit_rotated_kv_split_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.startswith("decode"):
-            h.update(open(os.path.join(d, name), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per history-kernel launch from the committed rocprofv3 PMC
     summary, or None when absent or taken on other kernel sources."""
@@ -84,48 +74,58 @@ def load_traffic(workload: str, kernel: str):
         rec = json.load(open(path)).get(f"{workload}/{kernel}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_sha():
+    from bit_rotated_kv_split_amd.profiling import source_sha
+    if not rec or rec.get("source_sha") != source_sha(ROOT):
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(model, layout, cal_host, lens, n_heads: int):
-    """Time the oracle (as it stands) on request 0 of the same workload at the
-    final length, for n_heads KV heads, scaled to GB/s of the same
-    algorithmic bytes.  The sample's tokens come from the GPU twin of the
-    seeded generator (bit-identical to synth.gen; not timed)."""
+def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 10.0):
+    """Time the oracle (as it stands) on whole requests of the same workload
+    at their final length, request 0 first, until about budget_s seconds of
+    oracle work; scaled to GB/s of the same algorithmic bytes.  The sample's
+    tokens come from the GPU twin of the seeded generator (bit-identical to
+    synth.gen; not timed)."""
     import torch
     from oracle import oscar as O
     from synth import gpu as synth_gpu
     w = model.w
-    L = int(lens[0])
     g = w.gqa
     stream = torch.cuda.current_stream().cuda_stream
-    host = {}
-    for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
-        buf = torch.empty((L, n_heads, 128), dtype=torch.int16, device="cuda")
-        sc = torch.from_numpy(np.ascontiguousarray(scale[:n_heads])).cuda()
-        for src, p0, n in layout.src_ranges(0, 0, L):
-            synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * n_heads * 128, n, n_heads, n_heads * 128, 128,
-                              w.seed, which, src, p0, sc, stream)
-        torch.cuda.synchronize()
-        host[which] = buf.cpu().numpy().view(np.uint16)
-        del buf
-    q = model.queries(0, 1)[0][: n_heads * g]
-    t0 = time.perf_counter()
-    O.request_attention(q, host["k"], host["v"], cal_host["r_k32"][:n_heads], cal_host["r_v32"][:n_heads],
-                        cal_host["clip_k"][:n_heads], cal_host["clip_v"][:n_heads], w.group_size)
-    dt = time.perf_counter() - t0
-    _, sbytes = step_bytes(np.array([L]), n_heads, n_heads * g, w.group_size)
+    spent = 0.0
+    done_bytes = 0
+    reqs = 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        host = {}
+        for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
+            buf = torch.empty((L, n_heads, 128), dtype=torch.int16, device="cuda")
+            sc = torch.from_numpy(np.ascontiguousarray(scale[:n_heads])).cuda()
+            for src, p0, n in layout.src_ranges(b, 0, L):
+                synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * n_heads * 128, n, n_heads, n_heads * 128, 128,
+                                  w.seed, which, src, p0, sc, stream)
+            torch.cuda.synchronize()
+            host[which] = buf.cpu().numpy().view(np.uint16)
+            del buf
+        q = model.queries(0, w.batch)[b][: n_heads * g]
+        t0 = time.perf_counter()
+        O.request_attention(q, host["k"], host["v"], cal_host["r_k32"][:n_heads], cal_host["r_v32"][:n_heads],
+                            cal_host["clip_k"][:n_heads], cal_host["clip_v"][:n_heads], w.group_size)
+        spent += time.perf_counter() - t0
+        done_bytes += step_bytes(np.array([L]), n_heads, n_heads * g, w.group_size)[1]
+        reqs += 1
+        if spent >= budget_s:
+            break
     try:
         from threadpoolctl import threadpool_info
         cores = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
     except Exception:
         cores = 1
-    return {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"request 0 of {w.batch}, {n_heads} of {w.num_kv_heads} KV heads, L={L}: "
-                      f"the oracle demotes that history and attends in float64 (numpy)"}
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seconds": round(spent, 3),
+            "sample": f"requests 0..{reqs - 1} of {w.batch}, {n_heads} of {w.num_kv_heads} KV heads each, "
+                      f"at their final lengths: the oracle demotes each history and attends in float64 "
+                      f"(numpy); {done_bytes / 1e9:.3f} GB of the step's algorithmic bytes"}
 
 
 def main() -> int:

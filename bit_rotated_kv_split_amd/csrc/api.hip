@@ -259,10 +259,13 @@ int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const o
     a.ev_start = static_cast<hipEvent_t>(g_ev_before);
     a.ev_stop = static_cast<hipEvent_t>(g_ev_after);
   }
+  // the matrix-core launch also runs the bf16 sink/recent chunks
   e = use_mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
   if (e != hipSuccess) return hip_fail(e, "history launch");
-  e = launch_bf16(a, s);
-  if (e != hipSuccess) return hip_fail(e, "bf16 launch");
+  if (!use_mfma) {
+    e = launch_bf16(a, s);
+    if (e != hipSuccess) return hip_fail(e, "bf16 launch");
+  }
   return OSCAR_OK;
 }
 

@@ -19,6 +19,7 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include "decode_bf16.h"
 #include "oscar_device.h"
 #include "oscar_internal.h"
 
@@ -48,12 +49,13 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   float acc[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
-#pragma unroll 8
-  for (int i = 64 * half; i < 64 * half + 64; ++i) {
-    const float rik = r[i * kDim + k];
+  float rv[64];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h] = __builtin_fmaf(qs[h][i], rik, acc[h]);
-  }
+  for (int i = 0; i < 64; ++i) rv[i] = r[(64 * half + i) * kDim + k];
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) acc[h] = __builtin_fmaf(qs[h][64 * half + i], rv[i], acc[h]);
 #pragma unroll
   for (int h = 0; h < GQ; ++h) part[half][h][k] = acc[h];
   __syncthreads();
@@ -88,27 +90,31 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   // 2-bit code masked in place, i.e. multiplied by 4^j for j < 3, so the
   // operand holds q / 4^j for those slots (rounded on its own, coarser grid).
   uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
-  for (int idx = tid; idx < 2 * 4 * kQPackRows * 16; idx += 256) {
-    const int e = idx & 15;
-    const int row = (idx >> 4) & (kQPackRows - 1);
-    const int kg = (idx >> 9) & 3;
-    const int hf = idx >> 11;
+  uint32_t* qpw = reinterpret_cast<uint32_t*>(qp);
+  for (int widx = tid; widx < 2 * 4 * kQPackRows * 4; widx += 256) {
+    const int j = widx & 3;                     // dword j = bytes 4j .. 4j+3 of the row
+    const int row = (widx >> 2) & (kQPackRows - 1);
+    const int kg = (widx >> 7) & 3;
+    const int hf = widx >> 9;
     const int h = row >> 2, digit = row & 3;
-    int8_t val = 0;
+    uint32_t word = 0;
     if (h < GQ) {
-      const int j = e >> 2;
-      const int ch = 16 * (4 * hf + kg) + 4 * (e & 3) + j;
       const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : 1.f);
-      const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h] * slot));
-      const int d0 = ((qi + 128) & 255) - 128;
-      const int q1 = (qi - d0) >> 8;
-      const int d1 = ((q1 + 128) & 255) - 128;
-      const int q2 = (q1 - d1) >> 8;
-      const int d2 = ((q2 + 128) & 255) - 128;
-      const int d3 = (q2 - d2) >> 8;
-      val = static_cast<int8_t>(digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3)));
+#pragma unroll
+      for (int b2 = 0; b2 < 4; ++b2) {
+        const int ch = 16 * (4 * hf + kg) + 4 * b2 + j;
+        const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h] * slot));
+        const int d0 = ((qi + 128) & 255) - 128;
+        const int q1 = (qi - d0) >> 8;
+        const int d1 = ((q1 + 128) & 255) - 128;
+        const int q2 = (q1 - d1) >> 8;
+        const int d2 = ((q2 + 128) & 255) - 128;
+        const int d3 = (q2 - d2) >> 8;
+        const int dv = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
+        word |= static_cast<uint32_t>(dv & 255) << (8 * b2);
+      }
     }
-    qp[idx] = static_cast<uint8_t>(val);
+    qpw[widx] = word;
   }
   if (tid >= GQ && tid < 8) {
     float* sc = reinterpret_cast<float*>(qp + kQPackOperandBytes);
@@ -291,126 +297,18 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
   }
 }
 
-struct Bf16Params {
-  const uint16_t* q;
-  const uint16_t* sink_k;
-  const uint16_t* sink_v;
-  const uint16_t* recent_k;
-  const uint16_t* recent_v;
-  const int32_t* seq_lens;
-  float* po;
-  float* plse;
-  int32_t hkv;
-  int32_t hq;
-  int32_t parts;        // partials per head (history splits + bf16 chunks)
-  int32_t first_part;   // index of this kernel's first partial
-};
-
-// Sink + recent: five 64-slot chunks (the sink, then the ring in quarters),
-// one wave each, each writing its own partial (output, LSE).  q . k: lane =
-// token, reading its 256-byte key row; p . v: lane = (8-channel group, token
-// residue mod 4), 16-byte loads coalesced across a row, reduced across the
-// four residues at the end.
+// Sink + recent as a standalone launch (the matrix-core path runs the same
+// chunks inside the history launch).
 template <int GQ>
 __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
-  __shared__ float q_s[GQ][kDim];
-  __shared__ float p_s[GQ][kPage];
-  const int L = a.seq_lens[b];
-  const int n_sink = min(L, kSink);
-  const int n_recent = min(max(L - kSink, 0), kRecent);
-  const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
-  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * GQ;
-  const size_t part0 = static_cast<size_t>(a.first_part + chunk);
-  if (n_valid == 0) {   // uniform across the wave
-    for (int i = lane; i < GQ * kDim; i += 64)
-      a.po[((head0 + i / kDim) * a.parts + part0) * kDim + i % kDim] = 0.f;
-    if (lane < GQ) a.plse[(head0 + lane) * a.parts + part0] = -INFINITY;
-    return;
-  }
-  for (int i = lane; i < GQ * kDim; i += 64)
-    q_s[i / kDim][i % kDim] = bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2;
-  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
-  const uint16_t* kb = chunk == 0 ? a.sink_k + kv0 * kSink * kDim
-                                  : a.recent_k + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
-  const uint16_t* vb = chunk == 0 ? a.sink_v + kv0 * kSink * kDim
-                                  : a.recent_v + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const bool valid = lane < n_valid;
-  float sc[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
-  if (valid) {
-    const uint4* row = reinterpret_cast<const uint4*>(kb + lane * kDim);
-#pragma unroll 4
-    for (int v8 = 0; v8 < kDim / 8; ++v8) {
-      const uint4 w = row[v8];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(ws[j] << 16);
-        const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
-        const int ch = v8 * 8 + 2 * j;
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          sc[h] = __builtin_fmaf(q_s[h][ch], lo, sc[h]);
-          sc[h] = __builtin_fmaf(q_s[h][ch + 1], hi, sc[h]);
-        }
-      }
-    }
-  }
-  float mx[GQ], lsum[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const float s = valid ? sc[h] : -INFINITY;
-    mx[h] = wave_max(s);
-    const float pr = valid ? exp2f(s - mx[h]) : 0.f;
-    lsum[h] = wave_sum(pr);
-    p_s[h][lane] = pr;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int cg = lane & 15, res = lane >> 4;
-  float acc[GQ][8];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int t = res; t < n_valid; t += 4) {
-    const uint4 w = *reinterpret_cast<const uint4*>(vb + t * kDim + cg * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const float pt = p_s[h][t];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[h][2 * j] = __builtin_fmaf(pt, __uint_as_float(ws[j] << 16), acc[h][2 * j]);
-        acc[h][2 * j + 1] = __builtin_fmaf(pt, __uint_as_float(ws[j] & 0xFFFF0000u), acc[h][2 * j + 1]);
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    const float inv = 1.f / lsum[h];
-    const size_t pidx = (head0 + h) * a.parts + part0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[h][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (res == 0) a.po[pidx * kDim + cg * 8 + e] = v * inv;
-    }
-    if (lane == 0) a.plse[pidx] = (mx[h] + log2f(lsum[h])) * kLn2;
-  }
+  __shared__ Bf16Smem<GQ> sm;
+  bf16_chunk<GQ>(a, GQ, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // LSE merge: workgroup = (KV head, request), 256 threads.  The history
 // splits are merged per head into the rotated value domain, rotated back by
-// R_V^T, and merged with the bf16 partials.
+// R_V^T, and merged with the bf16 partials.  Loads are issued early: each
+// thread's half-row of R_V before anything else, then the partials.
 template <int GQ>
 __global__ void __launch_bounds__(256)
 merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
@@ -420,11 +318,18 @@ merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float wts[GQ][kMaxParts];
   __shared__ float lse_s[GQ][2];      // history LSE, bf16 LSE
-  __shared__ float orot[GQ][kDim];
+  __shared__ float orot[GQ][kDim];    // merged history output, rotated domain
+  __shared__ float obf[GQ][kDim];     // merged bf16 output
   const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
-  for (int i = tid; i < GQ * parts; i += 256) wts[i / parts][i % parts] = plse[(head0 + i / parts) * parts + i % parts];
+  // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
+  const int i = tid >> 1, kh = tid & 1;
+  float4 rr[16];
+  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  for (int x = tid; x < GQ * parts; x += 256) wts[x / parts][x % parts] = plse[(head0 + x / parts) * parts + x % parts];
   __syncthreads();
-  // per head: normalised weights of the history splits and of the bf16 partials
+  // per head and side: normalised weights of the partials
   for (int h = wave; h < GQ; h += 4) {
 #pragma unroll
     for (int side = 0; side < 2; ++side) {
@@ -443,50 +348,52 @@ merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
     }
   }
   __syncthreads();
-  for (int i = tid; i < GQ * kDim; i += 256) {
-    const int h = i / kDim, k = i % kDim;
+  // weighted sums of the partials, 16 loads in flight per thread and chunk
+  for (int x = tid; x < GQ * kDim; x += 256) {
+    const int h = x / kDim, k = x % kDim;
     const float* base = po + ((head0 + h) * parts) * kDim + k;
-    float o = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < splits; ++s) o = __builtin_fmaf(wts[h][s], base[static_cast<size_t>(s) * kDim], o);
-    orot[h][k] = o;
-  }
-  __syncthreads();
-  // history output back to the model domain: x_i = sum_k y_k R_V[i][k];
-  // thread (i, half) covers heads of one parity
-  const int i = tid & (kDim - 1), half = tid >> 7;
-  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim);
-  float oh[(GQ + 1) / 2];
+    float oh = 0.f, ob = 0.f;
+    for (int s0 = 0; s0 < parts; s0 += 16) {
+      float v[16];
 #pragma unroll
-  for (int j = 0; j < (GQ + 1) / 2; ++j) oh[j] = 0.f;
-#pragma unroll 2
-  for (int c4 = 0; c4 < kDim / 4; ++c4) {
-    const float4 rr = rrow[c4];
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < parts ? base[static_cast<size_t>(s0 + u) * kDim] : 0.f;
 #pragma unroll
-    for (int j = 0; j < (GQ + 1) / 2; ++j) {
-      const int h = 2 * j + half;
-      if (h < GQ) {
-        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 0], rr.x, oh[j]);
-        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 1], rr.y, oh[j]);
-        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 2], rr.z, oh[j]);
-        oh[j] = __builtin_fmaf(orot[h][4 * c4 + 3], rr.w, oh[j]);
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u;
+        if (s < splits) oh = __builtin_fmaf(wts[h][s], v[u], oh);
+        else if (s < parts) ob = __builtin_fmaf(wts[h][s], v[u], ob);
       }
     }
+    orot[h][k] = oh;
+    obf[h][k] = ob;
   }
+  __syncthreads();
+  // history output back to the model domain: x_i = sum_k y_k R_V[i][k]
+  float oh[GQ];
 #pragma unroll
-  for (int j = 0; j < (GQ + 1) / 2; ++j) {
-    const int h = 2 * j + half;
-    if (h >= GQ) continue;
-    const float* bb = po + ((head0 + h) * parts) * kDim + i;
-    float ob = 0.f;
-    for (int s = splits; s < parts; ++s) ob = __builtin_fmaf(wts[h][s], bb[static_cast<size_t>(s) * kDim], ob);
-    const float lh = lse_s[h][0], lb = lse_s[h][1];
-    const float mx = fmaxf(lh, lb);
-    const float wh = lh == -INFINITY ? 0.f : expf(lh - mx);
-    const float wb = lb == -INFINITY ? 0.f : expf(lb - mx);
-    const float den = wh + wb;
-    out[(head0 + h) * kDim + i] = den > 0.f ? (wh * oh[j] + wb * ob) / den : 0.f;
-    if (lse_out != nullptr && i == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
+  for (int h = 0; h < GQ; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int k = 64 * kh + 4 * c;
+      acc = __builtin_fmaf(orot[h][k + 0], rr[c].x, acc);
+      acc = __builtin_fmaf(orot[h][k + 1], rr[c].y, acc);
+      acc = __builtin_fmaf(orot[h][k + 2], rr[c].z, acc);
+      acc = __builtin_fmaf(orot[h][k + 3], rr[c].w, acc);
+    }
+    oh[h] = acc + __shfl_xor(acc, 1, 64);
+  }
+  if (kh == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float lh = lse_s[h][0], lb = lse_s[h][1];
+      const float mx = fmaxf(lh, lb);
+      const float wh = lh == -INFINITY ? 0.f : expf(lh - mx);
+      const float wb = lb == -INFINITY ? 0.f : expf(lb - mx);
+      const float den = wh + wb;
+      out[(head0 + h) * kDim + i] = den > 0.f ? (wh * oh[h] + wb * obf[h][i]) / den : 0.f;
+      if (lse_out != nullptr && i == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
+    }
   }
 }
 
@@ -557,19 +464,7 @@ template <int GQ>
 struct Bf16Run {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const oscar_dims& d = *a.dims;
-    Bf16Params p;
-    p.q = a.q;
-    p.sink_k = a.cache->sink_k;
-    p.sink_v = a.cache->sink_v;
-    p.recent_k = a.cache->recent_k;
-    p.recent_v = a.cache->recent_v;
-    p.seq_lens = a.cache->seq_lens;
-    p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
-    p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
-    p.hkv = d.num_kv_heads;
-    p.hq = d.num_q_heads;
-    p.parts = a.lay.parts;
-    p.first_part = a.lay.splits;
+    const Bf16Params p = make_bf16_params(a);
     const dim3 grid(kBf16Parts, d.num_kv_heads, a.cache->batch);
     bf16_kernel<GQ><<<grid, 64, 0, s>>>(p);
     return hipGetLastError();

@@ -1,0 +1,162 @@
+// Decode attention over the bf16 sink and recent tokens (page
+// "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务", section
+// "OSCAR的另一个关键点是": a bf16 kernel handles sink and recent, with the
+// unrotated query).  Five 64-slot chunks per (request, KV head): the sink,
+// then the recent ring in quarters; one wave each, each writing its own
+// partial (output, natural-log LSE) into the decode workspace.
+//   q . k: lane = token, its 256-byte key row in sixteen 16-byte loads;
+//   p . v: lane = (8-channel group, token residue mod 4), 16-byte loads
+//          coalesced along each value row, reduced over the residues.
+#pragma once
+
+#include <math.h>
+
+#include "oscar_device.h"
+#include "oscar_internal.h"
+
+namespace oscar {
+
+struct Bf16Params {
+  const uint16_t* q;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  const uint16_t* recent_k;
+  const uint16_t* recent_v;
+  const int32_t* seq_lens;
+  float* po;
+  float* plse;
+  int32_t hkv;
+  int32_t hq;
+  int32_t parts;        // partials per head (history splits + bf16 chunks)
+  int32_t first_part;   // index of the first bf16 partial
+};
+
+template <int GQ>
+struct Bf16Smem {
+  float q[GQ][kDim];
+  float p[GQ][kPage];
+};
+
+inline Bf16Params make_bf16_params(const DecodeArgs& a) {
+  Bf16Params p;
+  p.q = a.q;
+  p.sink_k = a.cache->sink_k;
+  p.sink_v = a.cache->sink_v;
+  p.recent_k = a.cache->recent_k;
+  p.recent_v = a.cache->recent_v;
+  p.seq_lens = a.cache->seq_lens;
+  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
+  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+  p.hkv = a.dims->num_kv_heads;
+  p.hq = a.dims->num_q_heads;
+  p.parts = a.lay.parts;
+  p.first_part = a.lay.splits;
+  return p;
+}
+
+// One chunk for query heads 0 .. gq-1 (gq <= GQ) of KV head kvh, request b.
+// Called by a whole 64-lane wave.
+template <int GQ>
+__device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int chunk, int kvh, int b,
+                                           Bf16Smem<GQ>& sm) {
+  const int lane = threadIdx.x & 63;
+  const int L = a.seq_lens[b];
+  const int n_sink = min(L, kSink);
+  const int n_recent = min(max(L - kSink, 0), kRecent);
+  const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * gq;
+  const size_t part0 = static_cast<size_t>(a.first_part + chunk);
+  if (n_valid == 0) {   // uniform across the wave
+    for (int i = lane; i < gq * kDim; i += 64)
+      a.po[((head0 + i / kDim) * a.parts + part0) * kDim + i % kDim] = 0.f;
+    if (lane < gq) a.plse[(head0 + lane) * a.parts + part0] = -INFINITY;
+    return;
+  }
+  for (int i = lane; i < GQ * kDim; i += 64)
+    sm.q[i / kDim][i % kDim] = i / kDim < gq ? bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2 : 0.f;
+  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
+  const uint16_t* kb = chunk == 0 ? a.sink_k + kv0 * kSink * kDim
+                                  : a.recent_k + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  const uint16_t* vb = chunk == 0 ? a.sink_v + kv0 * kSink * kDim
+                                  : a.recent_v + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  const bool valid = lane < n_valid;
+  // key row of this lane's token (a valid row is read either way)
+  uint4 krow[kDim / 8];
+  const uint4* row = reinterpret_cast<const uint4*>(kb + (valid ? lane : 0) * kDim);
+#pragma unroll
+  for (int v8 = 0; v8 < kDim / 8; ++v8) krow[v8] = row[v8];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float sc[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
+#pragma unroll
+  for (int v8 = 0; v8 < kDim / 8; ++v8) {
+    const uint32_t ws[4] = {krow[v8].x, krow[v8].y, krow[v8].z, krow[v8].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(ws[j] << 16);
+      const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
+      const int ch = v8 * 8 + 2 * j;
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        sc[h] = __builtin_fmaf(sm.q[h][ch], lo, sc[h]);
+        sc[h] = __builtin_fmaf(sm.q[h][ch + 1], hi, sc[h]);
+      }
+    }
+  }
+  float mx[GQ], lsum[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const float s = valid ? sc[h] : -INFINITY;
+    mx[h] = wave_max(s);
+    const float pr = valid ? exp2f(s - mx[h]) : 0.f;
+    lsum[h] = wave_sum(pr);
+    sm.p[h][lane] = pr;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int cg = lane & 15, res = lane >> 4;
+  uint4 vrow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = res + 4 * i;
+    vrow[i] = *reinterpret_cast<const uint4*>(vb + (t < n_valid ? t : 0) * kDim + cg * 8);
+  }
+  float acc[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = res + 4 * i;
+    const uint32_t ws[4] = {vrow[i].x, vrow[i].y, vrow[i].z, vrow[i].w};
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float pt = t < n_valid ? sm.p[h][t] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[h][2 * j] = __builtin_fmaf(pt, __uint_as_float(ws[j] << 16), acc[h][2 * j]);
+        acc[h][2 * j + 1] = __builtin_fmaf(pt, __uint_as_float(ws[j] & 0xFFFF0000u), acc[h][2 * j + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const float inv = 1.f / lsum[h];
+    const size_t pidx = (head0 + h) * a.parts + part0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (res == 0 && h < gq) a.po[pidx * kDim + cg * 8 + e] = v * inv;
+    }
+    if (lane == 0 && h < gq) a.plse[pidx] = (mx[h] + log2f(lsum[h])) * kLn2;
+  }
+}
+
+}  // namespace oscar

@@ -28,7 +28,8 @@
 // uniform across the wave and rare once the first page has set m.
 //
 // One wave per workgroup; the workgroup owns (history split, KV head,
-// request).  Per 64-token page a lane loads 4 x 16 B of codes and the
+// request), and five more workgroups per (KV head, request) run the bf16
+// sink/recent chunks (decode_bf16.h) alongside the history splits.  Per 64-token page a lane loads 4 x 16 B of codes and the
 // scale/zero entries of its tokens (the page layout puts each lane's MFMA
 // operands in one 16-byte load); the loads of pages p+1 and p+2 are in
 // flight while page p is processed (three register buffers, no copies).  Query heads are
@@ -37,6 +38,7 @@
 
 #include <hip/hip_ext.h>
 
+#include "decode_bf16.h"
 #include "oscar_device.h"
 #include "oscar_internal.h"
 
@@ -49,6 +51,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // four-head, G = 128 variant (2 or 3); the larger variants use 2.
 #ifndef OSCAR_HIST_BUFFERS
 #define OSCAR_HIST_BUFFERS 3
+#endif
+#ifndef OSCAR_HIST_MIN_WAVES
+#define OSCAR_HIST_MIN_WAVES 2
 #endif
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
@@ -111,6 +116,8 @@ struct MfmaParams {
   int32_t splits;
   int32_t parts;
   int32_t pages_per_split;
+  int32_t batch;
+  Bf16Params bf;          // the bf16 sink/recent chunks, run as extra workgroups
 };
 
 template <int G>
@@ -311,13 +318,28 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NHB, int G, int BUF>
-__global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
+template <int NHB, int G, int BUF, int MINW>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MINW)))
+hist_mfma_kernel(MfmaParams a) {
   constexpr int NG = kDim / G;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // 1-D grid: every history split first (workgroups are dispatched in id
+  // order, so these are the resident ones), then the bf16 chunks, which
+  // fill the slots freed as history splits finish.
+  const int id = blockIdx.x;
+  const int n_hist_wg = a.splits * a.hkv * a.batch;
   const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
-  // P' operand rows: [head block x group][row = 4 h + digit][16 dwords]
-  __shared__ int32_t pop[NHB * NG][16][16];
+  union Smem {
+    int32_t pop[NHB * NG][16][16];   // P' operand rows: [head block x group][4 h + digit][16 dwords]
+    Bf16Smem<4 * NHB> bf;
+  };
+  __shared__ Smem smem;
+  if (id >= n_hist_wg) {   // a bf16 sink/recent chunk
+    const int r = id - n_hist_wg;
+    bf16_chunk<4 * NHB>(a.bf, a.gq, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv), smem.bf);
+    return;
+  }
+  const int split = id % a.splits, kvh = (id / a.splits) % a.hkv, b = id / (a.splits * a.hkv);
+  int32_t(*pop)[16][16] = smem.pop;
 
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kBf16Tokens);
@@ -421,7 +443,9 @@ __global__ void __launch_bounds__(64) hist_mfma_kernel(MfmaParams a) {
 
 template <int NHB, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int BUF = (NHB == 1 && G == 128) ? OSCAR_HIST_BUFFERS : 2;
+  constexpr bool main_variant = NHB == 1 && G == 128;
+  constexpr int BUF = main_variant ? OSCAR_HIST_BUFFERS : 2;
+  constexpr int MINW = main_variant ? OSCAR_HIST_MIN_WAVES : 1;
   const oscar_dims& d = *a.dims;
   MfmaParams p;
   p.pages = a.cache->pages;
@@ -438,11 +462,13 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.splits = a.lay.splits;
   p.parts = a.lay.parts;
   p.pages_per_split = a.lay.pages_per_split;
-  const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
+  p.batch = a.cache->batch;
+  p.bf = make_bf16_params(a);
+  const dim3 grid((a.lay.splits + kBf16Parts) * d.num_kv_heads * a.cache->batch);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
-    hipExtLaunchKernelGGL(hist_mfma_kernel<NHB, G, BUF>, grid, dim3(64), 0, s, a.ev_start, a.ev_stop, 0, p);
+    hipExtLaunchKernelGGL(hist_mfma_kernel<NHB, G, BUF, MINW>, grid, dim3(64), 0, s, a.ev_start, a.ev_stop, 0, p);
   else
-    hist_mfma_kernel<NHB, G, BUF><<<grid, 64, 0, s>>>(p);
+    hist_mfma_kernel<NHB, G, BUF, MINW><<<grid, 64, 0, s>>>(p);
   return hipGetLastError();
 }
 

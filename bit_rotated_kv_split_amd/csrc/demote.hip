@@ -48,12 +48,22 @@ __device__ void quantize_tokens(QuantSmem<G, NT>& sm, int nt, const float* __res
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
-  for (int i = 0; i < kDim; i += 4) {
+  if constexpr (NT == 1) {
+    // one token: every load of the rotation column in flight at once
+    float rv[kDim];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const double rik = static_cast<double>(r[(i + u) * kDim + k]);
+    for (int i = 0; i < kDim; ++i) rv[i] = r[i * kDim + k];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
+    for (int i = 0; i < kDim; ++i)
+      acc[0][i & 3] = fma(static_cast<double>(sm.x[0][i]), static_cast<double>(rv[i]), acc[0][i & 3]);
+  } else {
+    for (int i = 0; i < kDim; i += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double rik = static_cast<double>(r[(i + u) * kDim + k]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
+      }
     }
   }
   const float c = clipv[k];

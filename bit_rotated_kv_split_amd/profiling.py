@@ -1,0 +1,130 @@
+"""Summaries of rocprofv3 output for the decode path (profiling aid).
+
+    python -m bit_rotated_kv_split_amd.profiling stats <run_kernel_stats.csv> [--match a,b,...]
+    python -m bit_rotated_kv_split_amd.profiling traffic <fetch_counter_collection.csv>
+        <write_counter_collection.csv> --kernel hist_mfma --workload b32-100k-g128
+        --name mfma [--out profiles/traffic.json]
+    python -m bit_rotated_kv_split_amd.profiling counters <counter_collection.csv> --kernel hist_mfma
+
+`traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch)
+of the history kernel into bytes per launch.  Each counter is scaled by
+what it reads for the 2 GiB device copy that `bench.py --copy-probe` runs in
+the same process (copy bytes / counter bytes), so a counter that covers
+only part of the memory channels is corrected.  The record carries a hash of
+the decode kernel sources; `bench.py` reports it only while that hash
+matches the sources it runs.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import sys
+
+COPY_BYTES = 2 << 30
+
+
+def _kernel_rows(path: str):
+    return list(csv.DictReader(open(path)))
+
+
+def stats(path: str, match: list[str] | None = None) -> str:
+    rows = _kernel_rows(path)
+    out = ["| kernel | calls | average µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if match and not any(m in name for m in match):
+            continue
+        out.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def _counter_values(path: str, counter: str):
+    """{kernel name: [value per dispatch]} and the copy-probe reading."""
+    per = collections.defaultdict(list)
+    copy = []
+    for r in _kernel_rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        name = r["Kernel_Name"]
+        if "copyBuffer" in name:
+            copy.append((int(r["Grid_Size"]), v))
+        else:
+            per[name].append(v)
+    big = max(copy) if copy else None
+    return per, (big[1] if big else None)
+
+
+def counters(path: str, kernel: str) -> dict:
+    res = collections.defaultdict(list)
+    for r in _kernel_rows(path):
+        if kernel in r["Kernel_Name"]:
+            res[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in res.items()}
+
+
+def source_sha(root: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(root, "bit_rotated_kv_split_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.startswith("decode"):
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str) -> dict:
+    res = {}
+    for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        per, copy_kib = _counter_values(path, counter)
+        vals = [v for name, vs in per.items() if kernel in name for v in vs]
+        if not vals or not copy_kib:
+            raise SystemExit(f"no {counter} readings for {kernel} or for the copy probe in {path}")
+        factor = COPY_BYTES / (copy_kib * 1024)
+        res[tag] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
+                    "copy_probe_kib": copy_kib, "scale": factor,
+                    "bytes": sum(vals) / len(vals) * 1024 * factor}
+    res["bytes_per_launch"] = int(res["fetch"]["bytes"] + res["write"]["bytes"])
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--match", default="")
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--name", required=True)
+    b.add_argument("--out", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernel", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(stats(args.csv, [m for m in args.match.split(",") if m]))
+    elif args.cmd == "counters":
+        for k, v in sorted(counters(args.csv, args.kernel).items()):
+            print(f"{k}: {v:.6g}")
+    else:
+        rec = traffic(args.fetch_csv, args.write_csv, args.kernel)
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        rec["source_sha"] = source_sha(root)
+        print(json.dumps(rec, indent=1))
+        if args.out:
+            data = json.load(open(args.out)) if os.path.exists(args.out) else {}
+            data[f"{args.workload}/{args.name}"] = rec
+            json.dump(data, open(args.out, "w"), indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
