@@ -37,4 +37,5 @@ from ._lib import (  # noqa: F401
     oscar_merge_lse,
     oscar_set_history_events,
     oscar_set_history_kernel,
+    oscar_set_history_target,
 )

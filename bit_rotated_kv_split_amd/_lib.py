@@ -76,6 +76,7 @@ _SIGS = [
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
+    ("oscar_set_history_target", ctypes.c_int, [ctypes.c_int32]),
     ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims)]),
     ("oscar_set_history_events", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_last_error", ctypes.c_char_p, []),
@@ -216,6 +217,13 @@ def oscar_set_history_kernel(kind: int) -> int:
     prev = lib().oscar_set_history_kernel(kind)
     if prev < 0:
         raise OscarError(OSCAR_EINVAL, f"invalid history kernel {kind}")
+    return prev
+
+
+def oscar_set_history_target(workgroups: int) -> int:
+    prev = lib().oscar_set_history_target(workgroups)
+    if prev < 0:
+        raise OscarError(OSCAR_EINVAL, f"invalid history target {workgroups}")
     return prev
 
 

@@ -17,6 +17,7 @@ thread_local std::string g_error;
 thread_local void* g_ev_before = nullptr;
 thread_local void* g_ev_after = nullptr;
 std::atomic<int> g_hist_kernel{0};
+std::atomic<int> g_hist_target{0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -81,31 +82,21 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len) {
+  (void)max_seq_len;
   WsLayout w;
-  const int pages = pages_for(max_seq_len);
-  const int pairs = batch * d.num_kv_heads;
-  // About as many workgroups as the history kernel keeps resident (256
-  // compute units x 4 SIMDs x 2 waves), without making a split shorter than
-  // 8 pages.
-#ifndef OSCAR_TARGET_WORKGROUPS
-#define OSCAR_TARGET_WORKGROUPS 2048
-#endif
-  // the eight-head history kernel keeps one wave per SIMD resident
-  const int kTargetWorkgroups =
-      d.num_q_heads / d.num_kv_heads > 4 ? OSCAR_TARGET_WORKGROUPS / 2 : OSCAR_TARGET_WORKGROUPS;
-  int splits = 1;
-  if (pages > 0 && pairs > 0) {
-    splits = (kTargetWorkgroups + pairs - 1) / pairs;
-    int max_splits = (pages + 7) / 8;
-    if (max_splits > kMaxSplits) max_splits = kMaxSplits;
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
-    const int pps = (pages + splits - 1) / splits;
-    splits = (pages + pps - 1) / pps;
-    w.pages_per_split = pps;
-  }
-  w.splits = splits;
-  w.parts = splits + kBf16Parts;
+  // About as many history workgroups as the history kernel keeps resident
+  // (256 compute units x 4 SIMDs x 2 waves; one wave per SIMD for the
+  // eight-head kernel), unless set with oscar_set_history_target.
+  int target_wg = g_hist_target.load();
+  if (target_wg == 0) target_wg = d.num_q_heads / d.num_kv_heads > 4 ? kDefaultTargetWg / 2 : kDefaultTargetWg;
+  int t = (target_wg + d.num_kv_heads - 1) / d.num_kv_heads;
+  if (t > kMaxSplits) t = kMaxSplits;
+  if (t < 1) t = 1;
+  w.target = t;
+  w.slots = t + batch;
+  // storage is sized for the largest target, so the layout (and the
+  // merge's view of it) does not depend on the current setting
+  const size_t cap = static_cast<size_t>(kMaxSplits) + batch;
   const size_t heads = static_cast<size_t>(batch) * d.num_q_heads;
   size_t off = 0;
   w.off_qrot = off;
@@ -114,10 +105,18 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
   off = align256(off + heads * 4 * sizeof(float));
   w.off_qpack = off;
   off = align256(off + static_cast<size_t>(batch) * d.num_kv_heads * kQPackBytes);
-  w.off_po = off;
-  off = align256(off + heads * w.parts * kDim * sizeof(float));
-  w.off_plse = off;
-  off = align256(off + heads * w.parts * sizeof(float));
+  w.off_sched = off;
+  off = align256(off + (1 + 3 * cap) * sizeof(int32_t));
+  w.off_req = off;
+  off = align256(off + 2 * static_cast<size_t>(batch) * sizeof(int32_t));
+  w.off_ho = off;
+  off = align256(off + cap * d.num_q_heads * kDim * sizeof(float));
+  w.off_hlse = off;
+  off = align256(off + cap * d.num_q_heads * sizeof(float));
+  w.off_bo = off;
+  off = align256(off + heads * kBf16Parts * kDim * sizeof(float));
+  w.off_blse = off;
+  off = align256(off + heads * kBf16Parts * sizeof(float));
   w.total = off;
   return w;
 }
@@ -168,6 +167,11 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
 int oscar_set_history_kernel(int kind) {
   if (kind < 0 || kind > 2) return -1;
   return g_hist_kernel.exchange(kind);
+}
+
+int oscar_set_history_target(int32_t workgroups) {
+  if (workgroups < 0) return -1;
+  return g_hist_target.exchange(workgroups);
 }
 
 int oscar_history_kernel_for(const oscar_dims* dims) {
@@ -223,7 +227,7 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
 
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
   if (check_dims(dims) || batch < 0 || max_seq_len < 0) return -1;
-  return workspace_layout(*dims, batch, max_seq_len).splits;
+  return workspace_layout(*dims, batch, max_seq_len).slots;
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {

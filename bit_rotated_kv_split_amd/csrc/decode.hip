@@ -30,11 +30,77 @@ namespace {
 // held as four signed base-256 digits.
 constexpr float kQFixMax = 67108864.0f;
 
+// History-split schedule of one decode call, computed by the 256 threads
+// of one workgroup from the device-resident lengths.  Pages per split
+// q = max(kMinSplitPages, ceil(total / max(1, target - B/2))); request b gets
+// S_b = ceil(pages_b / q) equal splits, numbered by a block-wide prefix scan.
+// Writes sched = {n_splits, then (request, page0, page1) per split} and
+// req[b] = {first split, S_b}.  n_splits <= target + B.
+__device__ void schedule_splits(const int32_t* __restrict__ seq_lens, int batch, int target,
+                                int32_t* __restrict__ sched, int32_t* __restrict__ req) {
+  const int tid = threadIdx.x;
+  __shared__ int red[256];
+  __shared__ int scan[256];
+  __shared__ int s_off;
+  int local = 0;
+  for (int b = tid; b < batch; b += 256) {
+    const int n_hist = max(0, seq_lens[b] - kBf16Tokens);
+    local += (n_hist + kPage - 1) / kPage;
+  }
+  red[tid] = local;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const int total = red[0];
+  const int denom = max(1, target - batch / 2);
+  const int q = max(kMinSplitPages, (total + denom - 1) / denom);
+  if (tid == 0) s_off = 0;
+  __syncthreads();
+  for (int base = 0; base < batch; base += 256) {
+    const int b = base + tid;
+    int pages = 0, nsp = 0;
+    if (b < batch) {
+      const int n_hist = max(0, seq_lens[b] - kBf16Tokens);
+      pages = (n_hist + kPage - 1) / kPage;
+      nsp = (pages + q - 1) / q;
+    }
+    scan[tid] = nsp;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = s_off + scan[tid] - nsp;
+    if (b < batch) {
+      req[2 * b] = first;
+      req[2 * b + 1] = nsp;
+      const int per = nsp > 0 ? (pages + nsp - 1) / nsp : 0;
+      for (int i = 0; i < nsp; ++i) {
+        int32_t* e = sched + 1 + 3 * (first + i);
+        e[0] = b;
+        e[1] = i * per;
+        e[2] = min((i + 1) * per, pages);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) s_off += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) sched[0] = s_off;
+}
+
 template <int GQ>
 __global__ void __launch_bounds__(256)
 qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int hq, int hkv, int G,
-            float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack) {
+            float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack,
+            const int32_t* __restrict__ seq_lens, int batch, int target, int32_t* __restrict__ sched,
+            int32_t* __restrict__ req) {
   const int kvh = blockIdx.x, b = blockIdx.y;
+  if (kvh == 0 && b == 0) schedule_splits(seq_lens, batch, target, sched, req);
   const int tid = threadIdx.x, k = tid & (kDim - 1), half = tid >> 7;
   const int wave = tid >> 6, lane = tid & 63;
   __shared__ float qs[GQ][kDim];
@@ -133,18 +199,18 @@ struct HistParams {
   int32_t max_pages;
   int32_t hkv;
   int32_t hq;
-  int32_t splits;
-  int32_t parts;
-  int32_t pages_per_split;
+  const int32_t* sched;
 };
 
-// Vector-ALU history kernel.  Workgroup = (split, KV head, request), four
+// Vector-ALU history kernel.  Workgroup = (scheduled split, KV head), four
 // waves; wave w takes pages p0+w, p0+w+4, ... of the split with its own
 // online-softmax state, and the four states are merged at the end.
 template <int GQ, int G>
 __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
   constexpr int NG = kDim / G;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  if (split >= a.sched[0]) return;   // unused slot (uniform)
+  const int b = a.sched[1 + 3 * split];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float q_s[GQ][kDim];
   __shared__ float qsum_s[GQ][4];
@@ -154,9 +220,8 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
 
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kBf16Tokens);
-  const int n_pages = (n_hist + kPage - 1) / kPage;
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, n_pages);
+  const int p0 = a.sched[2 + 3 * split];
+  const int p1 = a.sched[3 + 3 * split];
   const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * GQ;
   for (int i = tid; i < GQ * kDim; i += 256) q_s[i / kDim][i % kDim] = a.qrot[head0 * kDim + i];
   if (tid < GQ * 4) qsum_s[tid >> 2][tid & 3] = a.qsum[head0 * 4 + tid];
@@ -291,7 +356,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
         at += st_acc[w][h][c] * f;
       }
     }
-    const size_t pidx = (head0 + h) * a.parts + split;
+    const size_t pidx = static_cast<size_t>(split) * a.hq + kvh * GQ + h;
     a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
     if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
   }
@@ -305,65 +370,87 @@ __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
   bf16_chunk<GQ>(a, GQ, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
-// LSE merge: workgroup = (KV head, request), 256 threads.  The history
-// splits are merged per head into the rotated value domain, rotated back by
-// R_V^T, and merged with the bf16 partials.  Loads are issued early: each
-// thread's half-row of R_V before anything else, then the partials.
+// LSE merge: workgroup = (KV head, request), 256 threads.  The request's
+// history splits (from the schedule) are merged per head in the rotated
+// value domain, rotated back by R_V^T, and merged with the five bf16
+// partials.  Loads are issued early: each thread's half-row of R_V before
+// anything else, then the partials.
+struct MergeParams {
+  const float* ho;        // [slots][Hq][128]
+  const float* hlse;      // [slots][Hq]
+  const float* bo;        // [B][Hq][5][128]
+  const float* blse;      // [B][Hq][5]
+  const int32_t* req;     // [B][2] {first split, count}
+  const float* r_v;
+  float* out;
+  float* lse_out;
+  int32_t hq;
+};
+
 template <int GQ>
-__global__ void __launch_bounds__(256)
-merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
-             const float* __restrict__ r_v, int hq, int splits, int parts, float* __restrict__ out,
-             float* __restrict__ lse_out) {
+__global__ void __launch_bounds__(256) merge_kernel(MergeParams a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __shared__ float wts[GQ][kMaxParts];
-  __shared__ float lse_s[GQ][2];      // history LSE, bf16 LSE
-  __shared__ float orot[GQ][kDim];    // merged history output, rotated domain
-  __shared__ float obf[GQ][kDim];     // merged bf16 output
-  const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
+  constexpr int kMaxHist = kMaxSplits + 1;
+  __shared__ float wh[GQ][kMaxHist];   // history split weights
+  __shared__ float wb[GQ][kBf16Parts]; // bf16 partial weights
+  __shared__ float lse_s[GQ][2];       // history LSE, bf16 LSE
+  __shared__ float orot[GQ][kDim];     // merged history output, rotated domain
+  __shared__ float obf[GQ][kDim];      // merged bf16 output
+  const int first = a.req[2 * b], count = a.req[2 * b + 1];
+  const int h0 = kvh * GQ;             // first head of this KV head's group
+  const size_t bhead0 = static_cast<size_t>(b) * a.hq + h0;
   // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
   const int i = tid >> 1, kh = tid & 1;
   float4 rr[16];
-  const float4* rrow = reinterpret_cast<const float4*>(r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
 #pragma unroll
   for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
-  for (int x = tid; x < GQ * parts; x += 256) wts[x / parts][x % parts] = plse[(head0 + x / parts) * parts + x % parts];
+  for (int x = tid; x < GQ * count; x += 256) {
+    const int h = x / count, sp = x % count;
+    wh[h][sp] = a.hlse[static_cast<size_t>(first + sp) * a.hq + h0 + h];
+  }
+  for (int x = tid; x < GQ * kBf16Parts; x += 256)
+    wb[x / kBf16Parts][x % kBf16Parts] = a.blse[(bhead0 + x / kBf16Parts) * kBf16Parts + x % kBf16Parts];
   __syncthreads();
   // per head and side: normalised weights of the partials
   for (int h = wave; h < GQ; h += 4) {
 #pragma unroll
     for (int side = 0; side < 2; ++side) {
-      const int s0 = side ? splits : 0, s1 = side ? parts : splits;
+      float* w = side ? wb[h] : wh[h];
+      const int n = side ? kBf16Parts : count;
       float mx = -INFINITY;
-      for (int s = s0 + lane; s < s1; s += 64) mx = fmaxf(mx, wts[h][s]);
+      for (int sp = lane; sp < n; sp += 64) mx = fmaxf(mx, w[sp]);
       mx = wave_max(mx);
       float den = 0.f;
-      for (int s = s0 + lane; s < s1; s += 64) den += mx == -INFINITY ? 0.f : expf(wts[h][s] - mx);
+      for (int sp = lane; sp < n; sp += 64) den += mx == -INFINITY ? 0.f : expf(w[sp] - mx);
       den = wave_sum(den);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int s = s0 + lane; s < s1; s += 64) wts[h][s] = den > 0.f ? expf(wts[h][s] - mx) / den : 0.f;
+      for (int sp = lane; sp < n; sp += 64) w[sp] = den > 0.f ? expf(w[sp] - mx) / den : 0.f;
       if (lane == 0) lse_s[h][side] = den > 0.f ? mx + logf(den) : -INFINITY;
     }
   }
   __syncthreads();
-  // weighted sums of the partials, 16 loads in flight per thread and chunk
+  // weighted sums of the partials, up to 16 loads in flight per thread
   for (int x = tid; x < GQ * kDim; x += 256) {
     const int h = x / kDim, k = x % kDim;
-    const float* base = po + ((head0 + h) * parts) * kDim + k;
-    float oh = 0.f, ob = 0.f;
-    for (int s0 = 0; s0 < parts; s0 += 16) {
+    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
+    const size_t hstride = static_cast<size_t>(a.hq) * kDim;
+    float oh = 0.f;
+    for (int s0 = 0; s0 < count; s0 += 16) {
       float v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s0 + u < parts ? base[static_cast<size_t>(s0 + u) * kDim] : 0.f;
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < count ? hb[static_cast<size_t>(s0 + u) * hstride] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int s = s0 + u;
-        if (s < splits) oh = __builtin_fmaf(wts[h][s], v[u], oh);
-        else if (s < parts) ob = __builtin_fmaf(wts[h][s], v[u], ob);
-      }
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < count) oh = __builtin_fmaf(wh[h][s0 + u], v[u], oh);
     }
+    const float* bb = a.bo + ((bhead0 + h) * kBf16Parts) * kDim + k;
+    float ob = 0.f;
+#pragma unroll
+    for (int c = 0; c < kBf16Parts; ++c) ob = __builtin_fmaf(wb[h][c], bb[c * kDim], ob);
     orot[h][k] = oh;
     obf[h][k] = ob;
   }
@@ -388,11 +475,11 @@ merge_kernel(const float* __restrict__ po, const float* __restrict__ plse,
     for (int h = 0; h < GQ; ++h) {
       const float lh = lse_s[h][0], lb = lse_s[h][1];
       const float mx = fmaxf(lh, lb);
-      const float wh = lh == -INFINITY ? 0.f : expf(lh - mx);
-      const float wb = lb == -INFINITY ? 0.f : expf(lb - mx);
-      const float den = wh + wb;
-      out[(head0 + h) * kDim + i] = den > 0.f ? (wh * oh[h] + wb * obf[h][i]) / den : 0.f;
-      if (lse_out != nullptr && i == 0) lse_out[head0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
+      const float whh = lh == -INFINITY ? 0.f : expf(lh - mx);
+      const float wbb = lb == -INFINITY ? 0.f : expf(lb - mx);
+      const float den = whh + wbb;
+      a.out[(bhead0 + h) * kDim + i] = den > 0.f ? (whh * oh[h] + wbb * obf[h][i]) / den : 0.f;
+      if (a.lse_out != nullptr && i == 0) a.lse_out[bhead0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;
     }
   }
 }
@@ -419,7 +506,8 @@ struct QrotRun {
     qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
-        a.ws + a.lay.off_qpack);
+        a.ws + a.lay.off_qpack, a.cache->seq_lens, a.cache->batch, a.lay.target,
+        reinterpret_cast<int32_t*>(a.ws + a.lay.off_sched), reinterpret_cast<int32_t*>(a.ws + a.lay.off_req));
     return hipGetLastError();
   }
 };
@@ -434,15 +522,13 @@ struct HistValuRun {
     p.seq_lens = a.cache->seq_lens;
     p.qrot = reinterpret_cast<const float*>(a.ws + a.lay.off_qrot);
     p.qsum = reinterpret_cast<const float*>(a.ws + a.lay.off_qsum);
-    p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
-    p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+    p.po = reinterpret_cast<float*>(a.ws + a.lay.off_ho);
+    p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_hlse);
     p.max_pages = a.cache->max_pages_per_req;
     p.hkv = d.num_kv_heads;
     p.hq = d.num_q_heads;
-    p.splits = a.lay.splits;
-    p.parts = a.lay.parts;
-    p.pages_per_split = a.lay.pages_per_split;
-    const dim3 grid(a.lay.splits, d.num_kv_heads, a.cache->batch);
+    p.sched = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_sched);
+    const dim3 grid(a.lay.slots, d.num_kv_heads);
     const bool timed = a.ev_start != nullptr && a.ev_stop != nullptr;
     switch (d.group_size) {
       case 32: launch(hist_valu_kernel<GQ, 32>, grid, timed, a, p, s); break;
@@ -477,9 +563,17 @@ struct MergeRun {
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
                         hipStream_t s) {
     const dim3 grid(d.num_kv_heads, batch);
-    merge_kernel<GQ><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(ws + lay.off_po),
-                                          reinterpret_cast<const float*>(ws + lay.off_plse),
-                                          rot.r_v, d.num_q_heads, lay.splits, lay.parts, out, lse_out);
+    MergeParams p;
+    p.ho = reinterpret_cast<const float*>(ws + lay.off_ho);
+    p.hlse = reinterpret_cast<const float*>(ws + lay.off_hlse);
+    p.bo = reinterpret_cast<const float*>(ws + lay.off_bo);
+    p.blse = reinterpret_cast<const float*>(ws + lay.off_blse);
+    p.req = reinterpret_cast<const int32_t*>(ws + lay.off_req);
+    p.r_v = rot.r_v;
+    p.out = out;
+    p.lse_out = lse_out;
+    p.hq = d.num_q_heads;
+    merge_kernel<GQ><<<grid, 256, 0, s>>>(p);
     return hipGetLastError();
   }
 };

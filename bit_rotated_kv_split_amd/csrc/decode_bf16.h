@@ -23,12 +23,10 @@ struct Bf16Params {
   const uint16_t* recent_k;
   const uint16_t* recent_v;
   const int32_t* seq_lens;
-  float* po;
-  float* plse;
+  float* po;            // [B][Hq][5][128]
+  float* plse;          // [B][Hq][5]
   int32_t hkv;
   int32_t hq;
-  int32_t parts;        // partials per head (history splits + bf16 chunks)
-  int32_t first_part;   // index of the first bf16 partial
 };
 
 template <int GQ>
@@ -45,12 +43,10 @@ inline Bf16Params make_bf16_params(const DecodeArgs& a) {
   p.recent_k = a.cache->recent_k;
   p.recent_v = a.cache->recent_v;
   p.seq_lens = a.cache->seq_lens;
-  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
-  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_bo);
+  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_blse);
   p.hkv = a.dims->num_kv_heads;
   p.hq = a.dims->num_q_heads;
-  p.parts = a.lay.parts;
-  p.first_part = a.lay.splits;
   return p;
 }
 
@@ -65,11 +61,10 @@ __device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int chun
   const int n_recent = min(max(L - kSink, 0), kRecent);
   const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
   const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * gq;
-  const size_t part0 = static_cast<size_t>(a.first_part + chunk);
   if (n_valid == 0) {   // uniform across the wave
     for (int i = lane; i < gq * kDim; i += 64)
-      a.po[((head0 + i / kDim) * a.parts + part0) * kDim + i % kDim] = 0.f;
-    if (lane < gq) a.plse[(head0 + lane) * a.parts + part0] = -INFINITY;
+      a.po[((head0 + i / kDim) * kBf16Parts + chunk) * kDim + i % kDim] = 0.f;
+    if (lane < gq) a.plse[(head0 + lane) * kBf16Parts + chunk] = -INFINITY;
     return;
   }
   for (int i = lane; i < GQ * kDim; i += 64)
@@ -147,7 +142,7 @@ __device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int chun
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     const float inv = 1.f / lsum[h];
-    const size_t pidx = (head0 + h) * a.parts + part0;
+    const size_t pidx = (head0 + h) * kBf16Parts + chunk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = acc[h][e];

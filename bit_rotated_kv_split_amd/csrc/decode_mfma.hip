@@ -27,6 +27,13 @@
 // more than kSlack or a value would overflow the digits; that branch is
 // uniform across the wave and rare once the first page has set m.
 //
+// The digits of P' are rounded with error diffusion: each lane carries the
+// part of its last weight that rounding dropped into its next one.  Plain
+// rounding would lose the many weights far below the unit (the unit follows
+// the largest weight) while the zero-point sum and l keep them, which biases
+// the output along the dominant value direction; with the carry the
+// rounded weights of a lane add up to the exact ones within half a unit.
+//
 // One wave per workgroup; the workgroup owns (history split, KV head,
 // request), and five more workgroups per (KV head, request) run the bf16
 // sink/recent chunks (decode_bf16.h) alongside the history splits.  Per 64-token page a lane loads 4 x 16 B of codes and the
@@ -58,7 +65,14 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
-constexpr float kDigitMax = 268435455.0f;      // 4 unsigned base-128 digits: x < 2^28
+// P' digits: x < 2^31 - 2^24, written as four signed base-256 digits (the
+// bytes of x + 0x80808080, each with its top bit flipped)
+constexpr float kDigitLimit = 2130706432.0f;
+constexpr float kDigitUnitMax = 2147483648.0f; // the unit puts a page's largest weight at 2^28
+constexpr uint32_t kDigitBias = 0x80808080u;
+// Pages a head's int32 accumulators may take between folds: a page adds at
+// most 64 * 128 * 48 to a digit row.
+constexpr int kFoldPages = 4096;
 
 // Codes at positions 4b+j of a 16-code word -> byte b of result j, times
 // 4^j for j < 3.
@@ -77,10 +91,24 @@ __device__ __forceinline__ float q_digits(const v4i& d) {
   return static_cast<float>(lo) + 65536.f * static_cast<float>(d.z) + 16777216.f * static_cast<float>(d.w);
 }
 
-// value of the unsigned base-128 digit rows of P' . code (accumulated)
+// value of the signed base-256 digit rows of P' . code (accumulated)
 __device__ __forceinline__ float p_digits(const v4i& d) {
-  return static_cast<float>(d.x) + 128.f * static_cast<float>(d.y) + 16384.f * static_cast<float>(d.z) +
-         2097152.f * static_cast<float>(d.w);
+  return static_cast<float>(d.x) + 256.f * static_cast<float>(d.y) + 65536.f * static_cast<float>(d.z) +
+         16777216.f * static_cast<float>(d.w);
+}
+
+// Byte transpose: row d of the result holds byte d of b0..b3 (byte m = b_m).
+__device__ __forceinline__ void transpose4x4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3,
+                                             uint32_t (&row)[4]) {
+  // v_perm_b32 selects bytes of {src0 (bytes 4..7), src1 (bytes 0..3)}
+  const uint32_t lo01 = __builtin_amdgcn_perm(b1, b0, 0x05010400u);   // b0.0 b1.0 b0.1 b1.1
+  const uint32_t hi01 = __builtin_amdgcn_perm(b1, b0, 0x07030602u);   // b0.2 b1.2 b0.3 b1.3
+  const uint32_t lo23 = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
+  row[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  row[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  row[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  row[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
 // Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
@@ -92,6 +120,21 @@ __device__ __forceinline__ float row_reduce(float v, Op op) {
   x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
   x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
   return __int_as_float(x);
+}
+
+// float64 sum over the 16 lanes of a DPP row.
+template <int CTRL>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  const int plo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const int phi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  return v + __hiloint2double(phi, plo);
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v = dpp_add_f64<0xB1>(v);
+  v = dpp_add_f64<0x4E>(v);
+  v = dpp_add_f64<0x141>(v);
+  return dpp_add_f64<0x140>(v);
 }
 
 struct MaxOp {
@@ -107,16 +150,14 @@ struct MfmaParams {
   const int32_t* seq_lens;
   const uint8_t* qpack;
   const float* qsum;
-  float* po;
-  float* plse;
+  const int32_t* sched;   // split table: [0] = count, then {request, first page, end page}
+  float* po;              // [slots][Hq][128]
+  float* plse;            // [slots][Hq]
   int32_t max_pages;
   int32_t hkv;
   int32_t hq;
   int32_t gq;
-  int32_t splits;
-  int32_t parts;
-  int32_t pages_per_split;
-  int32_t batch;
+  int32_t slots;          // history workgroups per KV head in the grid
   Bf16Params bf;          // the bf16 sink/recent chunks, run as extra workgroups
 };
 
@@ -160,14 +201,28 @@ struct WaveState {
   v4i dacc[NHB][8];        // int32 digit accumulators of P' . code, channel block cb
   float accf[NHB][8];      // folded float accumulators
   float ls[NHB];           // per-lane partial sum of p
-  float zs[NHB][NG];       // per-lane partial sum of p * value zero
+  float carry[NHB][NG];    // rounding carry of this lane's P' digits, in [0, 1) units
+  int since_fold;          // pages since every head's accumulators were folded
+};
+
+// LDS of one history wave.  zacc holds each lane's partial sum of
+// p * value zero in float64: the zero-point term is common to every channel
+// of a group and large next to the output (it cancels against the code
+// term), so the rounding of a long float32 chain would come back
+// concentrated on a few channels after the rotation by R_V^T.  It lives in
+// LDS (one read-modify-write per page) to keep it out of the register budget.
+template <int NHB, int NG>
+struct HistSmem {
+  int32_t pop[NHB * NG][16][16];   // P' operand rows: [head block x group][4 h + digit][16 dwords]
+  double zacc[NHB * NG][64];
 };
 
 // Fold the int32 accumulators of flagged heads into float, rescale to the
 // new reference max and take a new P' unit from the current page.
 template <int NHB, int G>
 __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[NHB][4],
-                                    const PageRegs<G>& cur, const bool (&need)[NHB]) {
+                                    const PageRegs<G>& cur, const bool (&need)[NHB],
+                                    HistSmem<NHB, kDim / G>& sm, int lane) {
   constexpr int NG = kDim / G;
   // P' of this lane's tokens (residue j = n % 4 in the K-slot order) meets
   // codes masked in place, i.e. times 4^j for j < 3: carry 4^-j here
@@ -189,7 +244,7 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
     st.ls[hb] *= alpha;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      st.zs[hb][gi] *= alpha;
+      sm.zacc[hb * NG + gi][lane] *= static_cast<double>(alpha);
       float wmax = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -197,8 +252,9 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
         wmax = fmaxf(wmax, p * __uint_as_float(cur.vsz[m * NG + gi] << 16));
       }
       wmax = row_reduce(wmax, MaxOp());
-      const float u = fmaxf(wmax, 1e-30f) * (kHeadroom / kDigitMax);
+      const float u = fmaxf(wmax, 1e-30f) * (kHeadroom / kDigitUnitMax);
       st.unit[hb][gi] = need[hb] ? u : st.unit[hb][gi];
+      st.carry[hb][gi] = need[hb] ? 0.5f : st.carry[hb][gi];
       st.inv[hb][gi] = need[hb] ? slot / u : st.inv[hb][gi];
     }
     st.m_ref[hb] = m_new;
@@ -207,7 +263,7 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
 
 template <int NHB, int G>
 __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
-                                             int n_hist, int lane, int32_t (*pop)[16][16]) {
+                                             int n_hist, int lane, HistSmem<NHB, kDim / G>& sm) {
   constexpr int NG = kDim / G;
   const int n = lane & 15, lg = lane >> 4;
   // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n
@@ -216,7 +272,6 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
   for (int m = 0; m < 4; ++m) {
     const v4i b0 = unpack16(static_cast<uint32_t>(cur.kw[0][m]));
     const v4i b1 = unpack16(static_cast<uint32_t>(cur.kw[1][m]));
-    const bool valid = tok_base + 16 * (n >> 2) + 4 * m + (n & 3) < n_hist;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const v4i zero = {0, 0, 0, 0};
@@ -236,31 +291,44 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
             __builtin_fmaf(__uint_as_float(s1 << 16) * st.qs[hb], q_digits(d1),
                            __uint_as_float(s1 & 0xFFFF0000u) * st.qz[hb][1]);
       }
-      sc[hb][m] = valid ? s : -INFINITY;
+      sc[hb][m] = s;
+    }
+  }
+  if (tok_base + kPage > n_hist) {   // the request's last page (uniform)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bool valid = tok_base + 16 * (n >> 2) + 4 * m + (n & 3) < n_hist;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) sc[hb][m] = valid ? sc[hb][m] : -INFINITY;
     }
   }
   // ---- p against the reference max, P' in units of the head's fixed point
   float pr[NHB][4], xv[NHB][NG][4];
-  bool flag = false;
+  float dmax = -INFINITY, xmax = 0.f;   // largest score above m, largest P' (this lane)
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+  for (int hb = 0; hb < NHB; ++hb) {
+    dmax = fmaxf(dmax, fmaxf(fmaxf(sc[hb][0], sc[hb][1]), fmaxf(sc[hb][2], sc[hb][3])) - st.m_ref[hb]);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
-      flag |= sc[hb][m] > st.m_ref[hb] + kSlack;
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
-        flag |= xv[hb][gi][m] > kDigitMax;
+        xmax = fmaxf(xmax, xv[hb][gi][m]);
       }
     }
-  // ---- re-base the heads that need a new reference max or unit (rare)
+  }
+  const bool flag = (dmax > kSlack) | (xmax >= kDigitLimit);
+  // ---- re-base the heads that need a new reference max or unit (rare),
+  // and every head once its int32 accumulators have taken kFoldPages pages
   const uint64_t mask = __ballot(flag);
-  if (mask != 0) {
+  const bool force = ++st.since_fold >= kFoldPages;
+  if (mask != 0 || force) {
     bool need[NHB];
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) need[hb] = ((mask >> (16 * lg)) & 0xFFFFull) != 0;
-    rebase<NHB, G>(st, sc, cur, need);
+    for (int hb = 0; hb < NHB; ++hb) need[hb] = force || ((mask >> (16 * lg)) & 0xFFFFull) != 0;
+    if (force) st.since_fold = 0;
+    rebase<NHB, G>(st, sc, cur, need, sm, lane);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -278,22 +346,24 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
     for (int m = 0; m < 4; ++m) st.ls[hb] += pr[hb][m];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      uint32_t dig0 = 0, dig1 = 0, dig2 = 0, dig3 = 0;
+      uint32_t b[4];
+      float zpage = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t sz = cur.vsz[m * NG + gi];
-        st.zs[hb][gi] = __builtin_fmaf(pr[hb][m], __uint_as_float(sz & 0xFFFF0000u), st.zs[hb][gi]);
-        const uint32_t x = static_cast<uint32_t>(xv[hb][gi][m] + 0.5f);
-        dig0 |= (x & 127u) << (8 * m);
-        dig1 |= ((x >> 7) & 127u) << (8 * m);
-        dig2 |= ((x >> 14) & 127u) << (8 * m);
-        dig3 |= (x >> 21) << (8 * m);
+        zpage = __builtin_fmaf(pr[hb][m], __uint_as_float(sz & 0xFFFF0000u), zpage);
+        // floor with the carried fraction: the lane's rounded weights add up
+        // to its exact ones within one unit
+        const float t = xv[hb][gi][m] + st.carry[hb][gi];
+        b[m] = static_cast<uint32_t>(t) + kDigitBias;
+        st.carry[hb][gi] = __builtin_amdgcn_fractf(t);
       }
+      uint32_t dig[4];
+      transpose4x4(b[0], b[1], b[2], b[3], dig);
+      sm.zacc[hb * NG + gi][lane] += static_cast<double>(zpage);
       // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
-      pop[hb * NG + gi][4 * lg + 0][n] = static_cast<int32_t>(dig0);
-      pop[hb * NG + gi][4 * lg + 1][n] = static_cast<int32_t>(dig1);
-      pop[hb * NG + gi][4 * lg + 2][n] = static_cast<int32_t>(dig2);
-      pop[hb * NG + gi][4 * lg + 3][n] = static_cast<int32_t>(dig3);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) sm.pop[hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(dig[d] ^ kDigitBias);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -304,7 +374,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&pop[hb * NG + gi][n][lg * 4]);
+    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&sm.pop[hb * NG + gi][n][lg * 4]);
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
     const int gi = (16 * cb) / G;
@@ -322,14 +392,15 @@ template <int NHB, int G, int BUF, int MINW>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MINW)))
 hist_mfma_kernel(MfmaParams a) {
   constexpr int NG = kDim / G;
-  // 1-D grid: every history split first (workgroups are dispatched in id
-  // order, so these are the resident ones), then the bf16 chunks, which
-  // fill the slots freed as history splits finish.
+  // 1-D grid: every history split slot first (workgroups are dispatched in
+  // id order, so these are the resident ones), then the bf16 chunks, which
+  // fill the slots freed as history splits finish.  Slots beyond the
+  // scheduled split count exit at once.
   const int id = blockIdx.x;
-  const int n_hist_wg = a.splits * a.hkv * a.batch;
+  const int n_hist_wg = a.slots * a.hkv;
   const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
   union Smem {
-    int32_t pop[NHB * NG][16][16];   // P' operand rows: [head block x group][4 h + digit][16 dwords]
+    HistSmem<NHB, NG> hist;
     Bf16Smem<4 * NHB> bf;
   };
   __shared__ Smem smem;
@@ -338,14 +409,15 @@ hist_mfma_kernel(MfmaParams a) {
     bf16_chunk<4 * NHB>(a.bf, a.gq, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv), smem.bf);
     return;
   }
-  const int split = id % a.splits, kvh = (id / a.splits) % a.hkv, b = id / (a.splits * a.hkv);
-  int32_t(*pop)[16][16] = smem.pop;
+  const int split = id / a.hkv, kvh = id % a.hkv;
+  if (split >= a.sched[0]) return;
+  const int b = a.sched[1 + 3 * split];
+  const int p0 = a.sched[2 + 3 * split];
+  const int p1 = a.sched[3 + 3 * split];
+  HistSmem<NHB, NG>& sm = smem.hist;
 
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kBf16Tokens);
-  const int n_pages = (n_hist + kPage - 1) / kPage;
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, n_pages);
 
   WaveState<NHB, G> st;
   const uint8_t* qp = a.qpack + (static_cast<size_t>(b) * a.hkv + kvh) * kQPackBytes;
@@ -362,12 +434,14 @@ hist_mfma_kernel(MfmaParams a) {
     st.qs[hb] = qscale[h];
     st.m_ref[hb] = -INFINITY;
     st.ls[hb] = 0.f;
+    st.since_fold = 0;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       st.qz[hb][gi] = head_ok[hb] ? a.qsum[(head0 + h) * 4 + gi] : 0.f;
       st.unit[hb][gi] = 0.f;
       st.inv[hb][gi] = 0.f;
-      st.zs[hb][gi] = 0.f;
+      sm.zacc[hb * NG + gi][lane] = 0.0;
+      st.carry[hb][gi] = 0.5f;
     }
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
@@ -398,13 +472,13 @@ hist_mfma_kernel(MfmaParams a) {
   if (p0 + 1 < p1) load_page<G>(rb, page_ptr(p0 + 1), lane);
   for (int p = p0; p < p1; p += 3) {
     if (p + 2 < p1) load_page<G>(rc, page_ptr(p + 2), lane);
-    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, pop);
+    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, sm);
     if (p + 1 >= p1) break;
     if (p + 3 < p1) load_page<G>(ra, page_ptr(p + 3), lane);
-    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, pop);
+    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, sm);
     if (p + 2 >= p1) break;
     if (p + 4 < p1) load_page<G>(rb, page_ptr(p + 4), lane);
-    process_page<NHB, G>(st, rc, (p + 2) * kPage, n_hist, lane, pop);
+    process_page<NHB, G>(st, rc, (p + 2) * kPage, n_hist, lane, sm);
   }
   } else {
   // two register buffers: page p+1 is in flight while p is processed
@@ -412,10 +486,10 @@ hist_mfma_kernel(MfmaParams a) {
   if (p0 < p1) load_page<G>(ra, page_ptr(p0), lane);
   for (int p = p0; p < p1; p += 2) {
     if (p + 1 < p1) load_page<G>(rb, page_ptr(p + 1), lane);
-    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, pop);
+    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, sm);
     if (p + 1 >= p1) break;
     if (p + 2 < p1) load_page<G>(ra, page_ptr(p + 2), lane);
-    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, pop);
+    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, sm);
   }
   }
 
@@ -423,19 +497,21 @@ hist_mfma_kernel(MfmaParams a) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float l = row_reduce(st.ls[hb], AddOp());
-    float zsum[NG];
+    double zsum[NG];
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) zsum[gi] = row_reduce(st.zs[hb][gi], AddOp());
+    for (int gi = 0; gi < NG; ++gi) {
+      zsum[gi] = row_sum_f64(sm.zacc[hb * NG + gi][lane]);
+    }
     if (!head_ok[hb]) continue;
     const int h = 4 * hb + lg;
-    const size_t pidx = (head0 + h) * a.parts + split;
+    const size_t pidx = static_cast<size_t>(split) * a.hq + static_cast<size_t>(kvh) * a.gq + h;
     const bool any = l > 0.f;
     const float inv_l = any ? 1.f / l : 0.f;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const int gi = (16 * cb) / G;
-      const float o = st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb]) + zsum[gi];
-      a.po[pidx * kDim + 16 * cb + n] = o * inv_l;
+      const double o = static_cast<double>(st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb])) + zsum[gi];
+      a.po[pidx * kDim + 16 * cb + n] = static_cast<float>(o) * inv_l;
     }
     if (n == 0) a.plse[pidx] = any ? (st.m_ref[hb] + log2f(l)) * kLn2 : -INFINITY;
   }
@@ -453,18 +529,16 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.seq_lens = a.cache->seq_lens;
   p.qpack = a.ws + a.lay.off_qpack;
   p.qsum = reinterpret_cast<const float*>(a.ws + a.lay.off_qsum);
-  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_po);
-  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_plse);
+  p.sched = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_sched);
+  p.po = reinterpret_cast<float*>(a.ws + a.lay.off_ho);
+  p.plse = reinterpret_cast<float*>(a.ws + a.lay.off_hlse);
   p.max_pages = a.cache->max_pages_per_req;
   p.hkv = d.num_kv_heads;
   p.hq = d.num_q_heads;
   p.gq = d.num_q_heads / d.num_kv_heads;
-  p.splits = a.lay.splits;
-  p.parts = a.lay.parts;
-  p.pages_per_split = a.lay.pages_per_split;
-  p.batch = a.cache->batch;
+  p.slots = a.lay.slots;
   p.bf = make_bf16_params(a);
-  const dim3 grid((a.lay.splits + kBf16Parts) * d.num_kv_heads * a.cache->batch);
+  const dim3 grid((a.lay.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
     hipExtLaunchKernelGGL(hist_mfma_kernel<NHB, G, BUF, MINW>, grid, dim3(64), 0, s, a.ev_start, a.ev_stop, 0, p);
   else

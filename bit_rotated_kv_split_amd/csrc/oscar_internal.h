@@ -10,22 +10,38 @@
 
 namespace oscar {
 
-// Partials per (request, query head): S history splits, then the bf16
-// sink/recent chunks (the sink and four quarters of the ring).
+// bf16 sink/recent partials per (request, query head): the sink and four
+// quarters of the recent ring.
 constexpr int kBf16Parts = 5;
+// Upper bound on the history splits of one request.
 constexpr int kMaxSplits = 251;
-constexpr int kMaxParts = kMaxSplits + kBf16Parts;
+// Smallest history split, in pages.
+constexpr int kMinSplitPages = 8;
+// History workgroups the split schedule aims for by default (halved for
+// query groups wider than four heads).
+constexpr int kDefaultTargetWg = 2048;
 
 // Workspace layout of one decode call (offsets in bytes, 256-aligned).
+//
+// History splits are scheduled on the device (the query-rotation kernel
+// reads the lengths): the batch's history pages are cut into splits of at
+// most q pages, each request getting ceil(pages / q) equal ones, numbered
+// 0 .. n_splits-1 across the batch.  `slots` bounds n_splits; the history
+// kernels launch slots x Hkv workgroups and the unused ones exit at once.
+// The split tables and partials are sized for kMaxSplits + B splits
+// whatever the target, so the offsets depend only on (dims, B).
 struct WsLayout {
-  int32_t splits = 1;           // history splits S
-  int32_t parts = 1 + kBf16Parts;
-  int32_t pages_per_split = 0;  // pages one split covers
+  int32_t target = 1;           // splits per KV head the schedule aims for
+  int32_t slots = 1;            // upper bound on splits per KV head
   size_t off_qrot = 0;          // float [B][Hq][128]: R_K-rotated query * log2(e)/sqrt(128)
   size_t off_qsum = 0;          // float [B][Hq][4]: per-group sums of that query
   size_t off_qpack = 0;         // matrix-core operands, kQPackBytes per (b, kv head)
-  size_t off_po = 0;            // float [B][Hq][parts][128] partial outputs
-  size_t off_plse = 0;          // float [B][Hq][parts] partial log-sum-exp (natural log)
+  size_t off_sched = 0;         // int32 [1 + 3 * slots]: n_splits, then {request, page0, page1}
+  size_t off_req = 0;           // int32 [B][2]: {first split, split count}
+  size_t off_ho = 0;            // float [slots][Hq][128]: history partial outputs (rotated)
+  size_t off_hlse = 0;          // float [slots][Hq]: history partial log-sum-exp (natural log)
+  size_t off_bo = 0;            // float [B][Hq][5][128]: bf16 partial outputs
+  size_t off_blse = 0;          // float [B][Hq][5]
   size_t total = 0;
 };
 

@@ -136,7 +136,15 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
                           int32_t n_tokens, const uint16_t* k_tokens,
                           const uint16_t* v_tokens, void* stream);
 
-/* Number of history splits the decode uses for (batch, max_seq_len). */
+/* Upper bound on the history splits per KV head that oscar_decode_attn
+ * schedules for a batch of this size.  The splits themselves are chosen on
+ * the device from the lengths: the batch's history pages are cut into
+ * splits of at most q pages, q = max(8, ceil(total pages / max(1, T - B/2)))
+ * with T = min(251, ceil(W / Hkv)) and W the oscar_set_history_target
+ * value (default 2048; 1024 when Hq/Hkv > 4), each request getting
+ * ceil(its pages / q) splits of equal size (the last one shorter).  The
+ * bound returned is T + B; -1 for invalid arguments.  max_seq_len is not
+ * used. */
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len);
 
 /* Workspace bytes oscar_decode_attn / oscar_merge_lse need (device memory,
@@ -149,9 +157,10 @@ size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32
  * q: bf16 [B][Hq][128] (unrotated).  Query head h reads KV head h/(Hq/Hkv).
  * The query is rotated by R_K once per (request, head) (third page, method
  * paragraphs: the online overhead lives inside the decode kernels); the
- * history is split into oscar_history_splits() ranges and each produces a
- * partial output (in the rotated value domain) and its log-sum-exp; the
- * sink and recent tokens produce one more partial with the unrotated query.
+ * history pages of the batch are split into page ranges on the device (see
+ * oscar_history_splits) and each produces a partial output (in the rotated
+ * value domain) and its log-sum-exp; the sink and recent tokens produce
+ * five more partials with the unrotated query.
  * Scores use scale 1/sqrt(128).  Results go to `workspace` for
  * oscar_merge_lse.  max_seq_len >= every L_b. */
 int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot,
@@ -204,6 +213,13 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
  * available), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
  * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
 int oscar_set_history_kernel(int kind);
+
+/* How many history workgroups the split schedule of oscar_decode_attn aims
+ * for: the batch's history pages are cut into about workgroups / Hkv
+ * splits (at least 8 pages each, at most 251 per request).  0 = default
+ * (2048; 1024 when Hq/Hkv > 4).  Process-wide; the workspace layout does
+ * not depend on it.  Returns the previous value, or -1 for a negative one. */
+int oscar_set_history_target(int32_t workgroups);
 
 /* History kernel the current selection launches for dims: 1 = vector-ALU,
  * 2 = matrix-core; -1 for invalid dims or an unsupported forced choice. */

@@ -38,9 +38,25 @@ def test_block_bytes():
 def test_workspace_and_splits():
     d = ok.make_dims(32, 8, 128)
     s = ok.oscar_history_splits(d, 32, 100_000)
-    assert 1 <= s <= 1558
-    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= 32 * 32 * (s + 1) * 129 * 4
-    assert ok.oscar_history_splits(d, 1, 300) == 1          # no history
+    # default target min(251, 2048 / 8) splits per KV head, plus the batch
+    assert s == 251 + 32
+    assert ok.oscar_history_splits(d, 32, 1000) == s        # lengths decide on the device
+    # partials for 251 + B history splits and five bf16 chunks per head
+    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= (283 * 32 + 32 * 32 * 5) * 129 * 4
+    gqa8 = ok.make_dims(64, 8, 128)
+    assert ok.oscar_history_splits(gqa8, 4, 1000) == 128 + 4  # 1024 workgroups for 8-wide groups
+    prev = ok.oscar_set_history_target(64)
+    try:
+        assert ok.oscar_history_splits(d, 32, 100_000) == 8 + 32
+        # the layout does not follow the target
+        assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) == \
+            ok.oscar_decode_workspace_bytes(d, 32, 10)
+        ok.oscar_set_history_target(1)
+        assert ok.oscar_history_splits(d, 2, 100_000) == 1 + 2
+    finally:
+        ok.oscar_set_history_target(prev)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_set_history_target(-1)
     bad = ok.make_dims(32, 8, 128, head_dim=64)
     assert ok.oscar_decode_workspace_bytes(bad, 1, 1000) == 0
     assert ok.oscar_history_splits(bad, 1, 1000) == -1
