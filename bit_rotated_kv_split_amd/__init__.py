@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     oscar_calibrate,
     oscar_calibrate_max_tokens,
     oscar_calibrate_workspace_bytes,
+    oscar_decode,
     oscar_decode_attn,
     oscar_decode_workspace_bytes,
     oscar_history_kernel_for,
@@ -35,6 +36,7 @@ from ._lib import (  # noqa: F401
     oscar_kv_fill_history,
     oscar_last_error,
     oscar_merge_lse,
+    oscar_read_history_schedule,
     oscar_set_history_events,
     oscar_set_history_kernel,
     oscar_set_history_target,

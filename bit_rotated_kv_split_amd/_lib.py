@@ -65,6 +65,9 @@ _SIGS = [
     ("oscar_decode_attn", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    ("oscar_decode", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -75,6 +78,9 @@ _SIGS = [
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("oscar_read_history_schedule", ctypes.c_int, [_P(OscarDims), ctypes.c_int32, ctypes.c_void_p,
+                                                   ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_int32, ctypes.c_void_p]),
     ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
     ("oscar_set_history_target", ctypes.c_int, [ctypes.c_int32]),
     ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims)]),
@@ -182,6 +188,13 @@ def oscar_decode_attn(dims, rot, cache, q, max_seq_len: int, workspace, workspac
                                    _stream(stream)))
 
 
+def oscar_decode(dims, rot, cache, q, max_seq_len: int, workspace, workspace_bytes: int, out,
+                 lse_out=None, stream=None) -> None:
+    _check(lib().oscar_decode(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(q),
+                              max_seq_len, _ptr(workspace), workspace_bytes, _ptr(out),
+                              _ptr(lse_out), _stream(stream)))
+
+
 def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspace_bytes: int,
                     out, lse_out=None, stream=None) -> None:
     _check(lib().oscar_merge_lse(ctypes.byref(dims), ctypes.byref(rot), batch, max_seq_len,
@@ -211,6 +224,21 @@ def oscar_calibrate(dims, n_tokens: int, q, k, v, clip_percentile: float, r_k, r
                                  clip_percentile, _ptr(r_k), _ptr(r_v), _ptr(clip_k), _ptr(clip_v),
                                  host(r_k_host), host(r_v_host), _ptr(workspace), workspace_bytes,
                                  _stream(stream)))
+
+
+def oscar_read_history_schedule(dims, batch: int, workspace, workspace_bytes: int, stream=None):
+    """(splits int32 [n][3] {request, first page, end page}, requests int32
+    [batch][2] {first split, count}) of the last decode on this workspace."""
+    import numpy as np
+    cap = lib().oscar_history_splits(ctypes.byref(dims), batch, 1)
+    splits = np.zeros((max(cap, 1), 3), dtype=np.int32)
+    reqs = np.zeros((batch, 2), dtype=np.int32)
+    n = lib().oscar_read_history_schedule(ctypes.byref(dims), batch, _ptr(workspace), workspace_bytes,
+                                          splits.ctypes.data, reqs.ctypes.data, splits.shape[0],
+                                          _stream(stream))
+    if n < 0:
+        _check(-n)
+    return splits[:n].copy(), reqs
 
 
 def oscar_set_history_kernel(kind: int) -> int:

@@ -89,14 +89,12 @@ WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_le
   // eight-head kernel), unless set with oscar_set_history_target.
   int target_wg = g_hist_target.load();
   if (target_wg == 0) target_wg = d.num_q_heads / d.num_kv_heads > 4 ? kDefaultTargetWg / 2 : kDefaultTargetWg;
-  int t = (target_wg + d.num_kv_heads - 1) / d.num_kv_heads;
-  if (t > kMaxSplits) t = kMaxSplits;
-  if (t < 1) t = 1;
+  const int t = (target_wg + d.num_kv_heads - 1) / d.num_kv_heads;
   w.target = t;
   w.slots = t + batch;
   // storage is sized for the largest target, so the layout (and the
   // merge's view of it) does not depend on the current setting
-  const size_t cap = static_cast<size_t>(kMaxSplits) + batch;
+  const size_t cap = static_cast<size_t>((kMaxTargetWg + d.num_kv_heads - 1) / d.num_kv_heads) + batch;
   const size_t heads = static_cast<size_t>(batch) * d.num_q_heads;
   size_t off = 0;
   w.off_qrot = off;
@@ -170,7 +168,7 @@ int oscar_set_history_kernel(int kind) {
 }
 
 int oscar_set_history_target(int32_t workgroups) {
-  if (workgroups < 0) return -1;
+  if (workgroups < 0 || workgroups > kMaxTargetWg) return -1;
   return g_hist_target.exchange(workgroups);
 }
 
@@ -235,9 +233,13 @@ size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32
   return workspace_layout(*dims, batch, max_seq_len).total;
 }
 
-int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
-                      const uint16_t* q, int32_t max_seq_len, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared body of oscar_decode_attn (out == NULL: partials only) and
+// oscar_decode (merged output).
+int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                float* out, float* lse_out, void* stream) {
   g_error.clear();
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
@@ -270,7 +272,29 @@ int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const o
     e = launch_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "bf16 launch");
   }
+  if (out != nullptr) {
+    e = launch_merge(*dims, *rot, cache->batch, a.ws, lay, out, lse_out, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
   return OSCAR_OK;
+}
+
+}  // namespace
+
+int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                      const uint16_t* q, int32_t max_seq_len, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                 float* out, float* lse_out, void* stream) {
+  if (out == nullptr && cache != nullptr && cache->batch > 0) {
+    g_error.clear();
+    return fail(OSCAR_EINVAL, "out is NULL");
+  }
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, stream);
 }
 
 int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,
@@ -289,6 +313,35 @@ int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t b
                                     out, lse_out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return OSCAR_OK;
+}
+
+int oscar_read_history_schedule(const oscar_dims* dims, int32_t batch, const void* workspace,
+                                size_t workspace_bytes, int32_t* splits, int32_t* requests,
+                                int32_t capacity, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims))) return -rc;
+  if (batch < 1) return -fail(OSCAR_EINVAL, "batch %d < 1", batch);
+  if (workspace == nullptr || splits == nullptr || requests == nullptr)
+    return -fail(OSCAR_EINVAL, "workspace, splits or requests is NULL");
+  const WsLayout lay = workspace_layout(*dims, batch, 1);
+  if (workspace_bytes < lay.total)
+    return -fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  int32_t n = 0;
+  hipError_t e = hipMemcpyAsync(&n, ws + lay.off_sched, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return -hip_fail(e, "schedule read");
+  if (n < 0 || n > capacity) return -fail(OSCAR_EINVAL, "%d splits do not fit capacity %d", n, capacity);
+  if (n > 0)
+    e = hipMemcpyAsync(splits, ws + lay.off_sched + sizeof(int32_t), 3 * sizeof(int32_t) * n,
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(requests, ws + lay.off_req, 2 * sizeof(int32_t) * batch, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return -hip_fail(e, "schedule read");
+  return n;
 }
 
 }  // extern "C"

@@ -31,39 +31,79 @@ namespace {
 constexpr float kQFixMax = 67108864.0f;
 
 // History-split schedule of one decode call, computed by the 256 threads
-// of one workgroup from the device-resident lengths.  Pages per split
-// q = max(kMinSplitPages, ceil(total / max(1, target - B/2))); request b gets
-// S_b = ceil(pages_b / q) equal splits, numbered by a block-wide prefix scan.
-// Writes sched = {n_splits, then (request, page0, page1) per split} and
-// req[b] = {first split, S_b}.  n_splits <= target + B.
+// of one workgroup from the device-resident lengths.  The pages per split q
+// is the smallest q >= max(kMinSplitPages, ceil(longest / kMaxSplits)) for
+// which the batch needs at most `target` splits (request b taking
+// S_b = ceil(pages_b / q)), found by bisection; when even one split per
+// request exceeds the target, q is the longest request.  Each request's splits are equal (the last one shorter),
+// numbered by a block-wide prefix scan.  Writes sched = {n_splits, then
+// (request, page0, page1) per split} and req[b] = {first split, S_b}.
+// n_splits <= max(target, B).
+// Block-wide (256 threads) sum and max of an int: wave reduction, then the
+// four wave results through LDS (red holds at least 4 ints).
+__device__ __forceinline__ int block_sum(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ int block_max(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
 __device__ void schedule_splits(const int32_t* __restrict__ seq_lens, int batch, int target,
                                 int32_t* __restrict__ sched, int32_t* __restrict__ req) {
   const int tid = threadIdx.x;
-  __shared__ int red[256];
+  constexpr int kCached = 1024;   // history page counts kept in LDS (the rest re-read)
+  __shared__ int red[4];
   __shared__ int scan[256];
   __shared__ int s_off;
-  int local = 0;
-  for (int b = tid; b < batch; b += 256) {
+  __shared__ int pages_s[kCached];
+  auto pages_from_len = [&](int b) {
     const int n_hist = max(0, seq_lens[b] - kBf16Tokens);
-    local += (n_hist + kPage - 1) / kPage;
+    return (n_hist + kPage - 1) / kPage;
+  };
+  int local_max = 0, local_total = 0, local_busy = 0;
+  for (int b = tid; b < batch; b += 256) {
+    const int pg = pages_from_len(b);
+    if (b < kCached) pages_s[b] = pg;
+    local_max = max(local_max, pg);
+    local_total += pg;
+    local_busy += pg > 0;
   }
-  red[tid] = local;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+  auto pages_of = [&](int b) { return b < kCached ? pages_s[b] : pages_from_len(b); };
+  const int max_pages = block_max(local_max, red);
+  const int total = block_sum(local_total, red);
+  const int busy = block_sum(local_busy, red);   // requests with history
+  // bracket: count(q) >= total / q needs q >= total / target, and
+  // count(q) <= total / q + busy holds at q = total / (target - busy)
+  int lo = max(max(kMinSplitPages, (max_pages + kMaxSplits - 1) / kMaxSplits),   // <= kMaxSplits per request
+               (total + target - 1) / target);
+  int hi = target > busy ? (total + target - busy - 1) / (target - busy) : max_pages;
+  hi = max(lo, min(hi, max_pages));
+  while (lo < hi) {   // uniform across the block
+    const int mid = (lo + hi) / 2;
+    int local = 0;
+    for (int b = tid; b < batch; b += 256) local += (pages_of(b) + mid - 1) / mid;
+    if (block_sum(local, red) <= target) hi = mid;
+    else lo = mid + 1;
   }
-  const int total = red[0];
-  const int denom = max(1, target - batch / 2);
-  const int q = max(kMinSplitPages, (total + denom - 1) / denom);
+  const int q = lo;
   if (tid == 0) s_off = 0;
   __syncthreads();
   for (int base = 0; base < batch; base += 256) {
     const int b = base + tid;
     int pages = 0, nsp = 0;
     if (b < batch) {
-      const int n_hist = max(0, seq_lens[b] - kBf16Tokens);
-      pages = (n_hist + kPage - 1) / kPage;
+      pages = pages_of(b);
       nsp = (pages + q - 1) / q;
     }
     scan[tid] = nsp;
@@ -99,8 +139,13 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
             float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack,
             const int32_t* __restrict__ seq_lens, int batch, int target, int32_t* __restrict__ sched,
             int32_t* __restrict__ req) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  if (kvh == 0 && b == 0) schedule_splits(seq_lens, batch, target, sched, req);
+  // row 0 of the grid (dispatched first) holds the split scheduler; rows
+  // 1 .. B rotate the queries of request blockIdx.y - 1
+  const int kvh = blockIdx.x, b = static_cast<int>(blockIdx.y) - 1;
+  if (b < 0) {
+    if (kvh == 0) schedule_splits(seq_lens, batch, target, sched, req);
+    return;
+  }
   const int tid = threadIdx.x, k = tid & (kDim - 1), half = tid >> 7;
   const int wave = tid >> 6, lane = tid & 63;
   __shared__ float qs[GQ][kDim];
@@ -367,7 +412,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
 template <int GQ>
 __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
   __shared__ Bf16Smem<GQ> sm;
-  bf16_chunk<GQ>(a, GQ, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+  bf16_chunk<GQ>(a, GQ, 0, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // LSE merge: workgroup = (KV head, request), 256 threads.  The request's
@@ -502,7 +547,7 @@ template <int GQ>
 struct QrotRun {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const oscar_dims& d = *a.dims;
-    const dim3 grid(d.num_kv_heads, a.cache->batch);
+    const dim3 grid(d.num_kv_heads, a.cache->batch + 1);
     qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),

@@ -50,25 +50,27 @@ inline Bf16Params make_bf16_params(const DecodeArgs& a) {
   return p;
 }
 
-// One chunk for query heads 0 .. gq-1 (gq <= GQ) of KV head kvh, request b.
-// Called by a whole 64-lane wave.
+// One chunk for query heads h_lo .. h_lo + nh - 1 (nh = min(GQ, gq - h_lo))
+// of the gq-head group of KV head kvh, request b.  Called by a whole 64-lane
+// wave.
 template <int GQ>
-__device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int chunk, int kvh, int b,
+__device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int h_lo, int chunk, int kvh, int b,
                                            Bf16Smem<GQ>& sm) {
   const int lane = threadIdx.x & 63;
+  const int nh = min(GQ, gq - h_lo);
   const int L = a.seq_lens[b];
   const int n_sink = min(L, kSink);
   const int n_recent = min(max(L - kSink, 0), kRecent);
   const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
-  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * gq;
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * gq + h_lo;
   if (n_valid == 0) {   // uniform across the wave
-    for (int i = lane; i < gq * kDim; i += 64)
+    for (int i = lane; i < nh * kDim; i += 64)
       a.po[((head0 + i / kDim) * kBf16Parts + chunk) * kDim + i % kDim] = 0.f;
-    if (lane < gq) a.plse[(head0 + lane) * kBf16Parts + chunk] = -INFINITY;
+    if (lane < nh) a.plse[(head0 + lane) * kBf16Parts + chunk] = -INFINITY;
     return;
   }
   for (int i = lane; i < GQ * kDim; i += 64)
-    sm.q[i / kDim][i % kDim] = i / kDim < gq ? bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2 : 0.f;
+    sm.q[i / kDim][i % kDim] = i / kDim < nh ? bf16_to_f32(a.q[head0 * kDim + i]) * kScoreScaleLog2 : 0.f;
   const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
   const uint16_t* kb = chunk == 0 ? a.sink_k + kv0 * kSink * kDim
                                   : a.recent_k + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
@@ -148,9 +150,9 @@ __device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int chun
       float v = acc[h][e];
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      if (res == 0 && h < gq) a.po[pidx * kDim + cg * 8 + e] = v * inv;
+      if (res == 0 && h < nh) a.po[pidx * kDim + cg * 8 + e] = v * inv;
     }
-    if (lane == 0 && h < gq) a.plse[pidx] = (mx[h] + log2f(lsum[h])) * kLn2;
+    if (lane == 0 && h < nh) a.plse[pidx] = (mx[h] + log2f(lsum[h])) * kLn2;
   }
 }
 

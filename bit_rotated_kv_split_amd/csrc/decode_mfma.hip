@@ -54,8 +54,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Launch-shape knob (compile-time): register page buffers per wave for the
-// four-head, G = 128 variant (2 or 3); the larger variants use 2.
+// Launch-shape knobs (compile-time): register page buffers per wave (2 or 3)
+// and the waves per SIMD the register budget is sized for.
 #ifndef OSCAR_HIST_BUFFERS
 #define OSCAR_HIST_BUFFERS 3
 #endif
@@ -388,25 +388,30 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NHB, int G, int BUF, int MINW>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MINW)))
+template <int G, int WAVES, int BUF, int MINW>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(MINW)))
 hist_mfma_kernel(MfmaParams a) {
+  constexpr int NHB = 1;
   constexpr int NG = kDim / G;
   // 1-D grid: every history split slot first (workgroups are dispatched in
   // id order, so these are the resident ones), then the bf16 chunks, which
   // fill the slots freed as history splits finish.  Slots beyond the
-  // scheduled split count exit at once.
+  // scheduled split count exit at once.  A query group wider than four
+  // heads takes two waves, heads 4w .. 4w+3 each; both read the same pages,
+  // the second mostly from the compute unit's cache.
   const int id = blockIdx.x;
   const int n_hist_wg = a.slots * a.hkv;
-  const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
+  const int wave = WAVES == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+  const int lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
   union Smem {
-    HistSmem<NHB, NG> hist;
-    Bf16Smem<4 * NHB> bf;
+    HistSmem<NHB, NG> hist[WAVES];
+    Bf16Smem<4> bf[WAVES];
   };
   __shared__ Smem smem;
-  if (id >= n_hist_wg) {   // a bf16 sink/recent chunk
+  if (id >= n_hist_wg) {   // a bf16 sink/recent chunk, four heads per wave
     const int r = id - n_hist_wg;
-    bf16_chunk<4 * NHB>(a.bf, a.gq, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv), smem.bf);
+    bf16_chunk<4>(a.bf, a.gq, 4 * wave, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv),
+                  smem.bf[wave]);
     return;
   }
   const int split = id / a.hkv, kvh = id % a.hkv;
@@ -414,7 +419,7 @@ hist_mfma_kernel(MfmaParams a) {
   const int b = a.sched[1 + 3 * split];
   const int p0 = a.sched[2 + 3 * split];
   const int p1 = a.sched[3 + 3 * split];
-  HistSmem<NHB, NG>& sm = smem.hist;
+  HistSmem<NHB, NG>& sm = smem.hist[wave];
 
   const int L = a.seq_lens[b];
   const int n_hist = max(0, L - kBf16Tokens);
@@ -428,8 +433,8 @@ hist_mfma_kernel(MfmaParams a) {
   for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + ((hf * 4 + lg) * kQPackRows + hb * 16 + n) * 16);
-    const int h = 4 * hb + lg;
+      st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + ((hf * 4 + lg) * kQPackRows + (wave + hb) * 16 + n) * 16);
+    const int h = 4 * (wave + hb) + lg;
     head_ok[hb] = h < a.gq;
     st.qs[hb] = qscale[h];
     st.m_ref[hb] = -INFINITY;
@@ -465,32 +470,19 @@ hist_mfma_kernel(MfmaParams a) {
     const int phys = __builtin_amdgcn_readlane(pt_reg, p - pt_base);
     return base + static_cast<size_t>(phys) * blk_stride;
   };
-  if constexpr (BUF == 3) {
-  // three register buffers: pages p+1 and p+2 are in flight while p is processed
-  PageRegs<G> ra, rb, rc;
-  if (p0 < p1) load_page<G>(ra, page_ptr(p0), lane);
-  if (p0 + 1 < p1) load_page<G>(rb, page_ptr(p0 + 1), lane);
-  for (int p = p0; p < p1; p += 3) {
-    if (p + 2 < p1) load_page<G>(rc, page_ptr(p + 2), lane);
-    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, sm);
-    if (p + 1 >= p1) break;
-    if (p + 3 < p1) load_page<G>(ra, page_ptr(p + 3), lane);
-    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, sm);
-    if (p + 2 >= p1) break;
-    if (p + 4 < p1) load_page<G>(rb, page_ptr(p + 4), lane);
-    process_page<NHB, G>(st, rc, (p + 2) * kPage, n_hist, lane, sm);
-  }
-  } else {
-  // two register buffers: page p+1 is in flight while p is processed
-  PageRegs<G> ra, rb;
-  if (p0 < p1) load_page<G>(ra, page_ptr(p0), lane);
-  for (int p = p0; p < p1; p += 2) {
-    if (p + 1 < p1) load_page<G>(rb, page_ptr(p + 1), lane);
-    process_page<NHB, G>(st, ra, p * kPage, n_hist, lane, sm);
-    if (p + 1 >= p1) break;
-    if (p + 2 < p1) load_page<G>(ra, page_ptr(p + 2), lane);
-    process_page<NHB, G>(st, rb, (p + 1) * kPage, n_hist, lane, sm);
-  }
+  // BUF register page buffers: pages p+1 .. p+BUF-1 are in flight while p
+  // is processed.  The inner loop is unrolled, so buffer indices are static.
+  PageRegs<G> buf[BUF];
+#pragma unroll
+  for (int k = 0; k < BUF - 1; ++k)
+    if (p0 + k < p1) load_page<G>(buf[k], page_ptr(p0 + k), lane);
+  for (int p = p0; p < p1; p += BUF) {
+#pragma unroll
+    for (int k = 0; k < BUF; ++k) {
+      if (p + k + BUF - 1 < p1) load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(p + k + BUF - 1), lane);
+      process_page<NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm);
+      if (p + k + 1 >= p1) break;
+    }
   }
 
   // ---- partial output of this split (rotated value domain)
@@ -503,7 +495,7 @@ hist_mfma_kernel(MfmaParams a) {
       zsum[gi] = row_sum_f64(sm.zacc[hb * NG + gi][lane]);
     }
     if (!head_ok[hb]) continue;
-    const int h = 4 * hb + lg;
+    const int h = 4 * (wave + hb) + lg;
     const size_t pidx = static_cast<size_t>(split) * a.hq + static_cast<size_t>(kvh) * a.gq + h;
     const bool any = l > 0.f;
     const float inv_l = any ? 1.f / l : 0.f;
@@ -517,11 +509,10 @@ hist_mfma_kernel(MfmaParams a) {
   }
 }
 
-template <int NHB, int G>
+template <int G, int WAVES>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr bool main_variant = NHB == 1 && G == 128;
-  constexpr int BUF = main_variant ? OSCAR_HIST_BUFFERS : 2;
-  constexpr int MINW = main_variant ? OSCAR_HIST_MIN_WAVES : 1;
+  constexpr int BUF = OSCAR_HIST_BUFFERS;
+  constexpr int MINW = OSCAR_HIST_MIN_WAVES;
   const oscar_dims& d = *a.dims;
   MfmaParams p;
   p.pages = a.cache->pages;
@@ -539,10 +530,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.slots = a.lay.slots;
   p.bf = make_bf16_params(a);
   const dim3 grid((a.lay.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
+  const dim3 block(64 * WAVES);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
-    hipExtLaunchKernelGGL(hist_mfma_kernel<NHB, G, BUF, MINW>, grid, dim3(64), 0, s, a.ev_start, a.ev_stop, 0, p);
+    hipExtLaunchKernelGGL(hist_mfma_kernel<G, WAVES, BUF, MINW>, grid, block, 0, s, a.ev_start, a.ev_stop, 0, p);
   else
-    hist_mfma_kernel<NHB, G, BUF, MINW><<<grid, 64, 0, s>>>(p);
+    hist_mfma_kernel<G, WAVES, BUF, MINW><<<grid, block, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -556,8 +548,8 @@ bool hist_mfma_supported(const oscar_dims& d) {
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s) {
   const int g = a.dims->num_q_heads / a.dims->num_kv_heads;
   const bool two = g > 4;
-  if (a.dims->group_size == 64) return two ? launch_t<2, 64>(a, s) : launch_t<1, 64>(a, s);
-  return two ? launch_t<2, 128>(a, s) : launch_t<1, 128>(a, s);
+  if (a.dims->group_size == 64) return two ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
+  return two ? launch_t<128, 2>(a, s) : launch_t<128, 1>(a, s);
 }
 
 }  // namespace oscar

@@ -18,8 +18,11 @@ constexpr int kMaxSplits = 251;
 // Smallest history split, in pages.
 constexpr int kMinSplitPages = 8;
 // History workgroups the split schedule aims for by default (halved for
-// query groups wider than four heads).
+// query groups wider than four heads, whose workgroups take two waves):
+// about what the chip keeps resident, so the splits run in one round.
 constexpr int kDefaultTargetWg = 2048;
+// Largest settable target (bounds the workspace).
+constexpr int kMaxTargetWg = 8192;
 
 // Workspace layout of one decode call (offsets in bytes, 256-aligned).
 //
@@ -28,8 +31,8 @@ constexpr int kDefaultTargetWg = 2048;
 // most q pages, each request getting ceil(pages / q) equal ones, numbered
 // 0 .. n_splits-1 across the batch.  `slots` bounds n_splits; the history
 // kernels launch slots x Hkv workgroups and the unused ones exit at once.
-// The split tables and partials are sized for kMaxSplits + B splits
-// whatever the target, so the offsets depend only on (dims, B).
+// The split tables and partials are sized for ceil(kMaxTargetWg / Hkv) + B
+// splits whatever the target, so the offsets depend only on (dims, B).
 struct WsLayout {
   int32_t target = 1;           // splits per KV head the schedule aims for
   int32_t slots = 1;            // upper bound on splits per KV head

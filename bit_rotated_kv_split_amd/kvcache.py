@@ -81,10 +81,8 @@ class DecodeWorkspace:
 def decode_step(cache: PagedKVCache, rot: Rotation, ws: DecodeWorkspace, q, out, lse=None,
                 k_new=None, v_new=None, stream=None) -> None:
     """One decode step on the current stream: demote (and append k_new/v_new
-    if given), decode attention, LSE merge.  seq_lens must already count the
-    new token."""
+    if given), then decode attention with the merge (oscar_decode).
+    seq_lens must already count the new token."""
     c = cache.struct()
     _lib.oscar_kv_demote(cache.dims, rot.struct, c, k_new, v_new, stream)
-    _lib.oscar_decode_attn(cache.dims, rot.struct, c, q, ws.max_seq_len, ws.buf, ws.nbytes, stream)
-    _lib.oscar_merge_lse(cache.dims, rot.struct, cache.batch, ws.max_seq_len, ws.buf, ws.nbytes,
-                         out, lse, stream)
+    _lib.oscar_decode(cache.dims, rot.struct, c, q, ws.max_seq_len, ws.buf, ws.nbytes, out, lse, stream)

@@ -138,13 +138,14 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
 
 /* Upper bound on the history splits per KV head that oscar_decode_attn
  * schedules for a batch of this size.  The splits themselves are chosen on
- * the device from the lengths: the batch's history pages are cut into
- * splits of at most q pages, q = max(8, ceil(total pages / max(1, T - B/2)))
- * with T = min(251, ceil(W / Hkv)) and W the oscar_set_history_target
- * value (default 2048; 1024 when Hq/Hkv > 4), each request getting
- * ceil(its pages / q) splits of equal size (the last one shorter).  The
- * bound returned is T + B; -1 for invalid arguments.  max_seq_len is not
- * used. */
+ * the device from the lengths: with T = ceil(W / Hkv) and W the
+ * oscar_set_history_target value (default 2048; 1024 when Hq/Hkv > 4), the
+ * pages per split q is the smallest q >= max(8, ceil(longest / 251)) for
+ * which the batch needs at most T splits, request b taking
+ * ceil(pages_b / q) splits of equal size (the last one shorter); if one
+ * split per request already exceeds T, q is the longest request's page
+ * count.  The bound returned is T + B; -1 for invalid arguments.
+ * max_seq_len is not used. */
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len);
 
 /* Workspace bytes oscar_decode_attn / oscar_merge_lse need (device memory,
@@ -166,6 +167,13 @@ size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32
 int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot,
                       const oscar_cache* cache, const uint16_t* q, int32_t max_seq_len,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode attention with the merge in one call: oscar_decode_attn followed
+ * by oscar_merge_lse on the same stream (out float32 [B][Hq][128], lse_out
+ * float32 [B][Hq] or NULL); out may be NULL only for an empty batch. */
+int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                 float* out, float* lse_out, void* stream);
 
 /* Log-sum-exp merge: combine the history partials, rotate the history
  * output back by R_V^T, merge it with the sink/recent partial and write
@@ -215,10 +223,10 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
 int oscar_set_history_kernel(int kind);
 
 /* How many history workgroups the split schedule of oscar_decode_attn aims
- * for: the batch's history pages are cut into about workgroups / Hkv
- * splits (at least 8 pages each, at most 251 per request).  0 = default
- * (2048; 1024 when Hq/Hkv > 4).  Process-wide; the workspace layout does
- * not depend on it.  Returns the previous value, or -1 for a negative one. */
+ * for (see oscar_history_splits); 0 = default (2048; 1024 when Hq/Hkv > 4,
+ * whose workgroups hold two waves), at most 8192.  Process-wide; the
+ * workspace layout does not depend on it.  Returns the previous value, or
+ * -1 for a value out of range. */
 int oscar_set_history_target(int32_t workgroups);
 
 /* History kernel the current selection launches for dims: 1 = vector-ALU,
@@ -230,6 +238,17 @@ int oscar_history_kernel_for(const oscar_dims* dims);
  * stop events (hipExtLaunchKernelGGL), so their elapsed time is that
  * kernel's execution.  Thread-local; NULL clears it. */
 int oscar_set_history_events(void* before, void* after);
+
+/* Copy the history-split schedule that the last oscar_decode_attn on this
+ * workspace wrote (device) to the host: splits (host int32 [capacity][3])
+ * gets {request, first page, end page} per split, requests (host int32
+ * [batch][2]) gets {first split, split count} per request.  Synchronous on
+ * `stream`.  Returns the number of splits, or minus an OSCAR_E* code
+ * (-OSCAR_EINVAL when it exceeds capacity).  For inspection and tests; the decode
+ * path itself never reads the schedule back. */
+int oscar_read_history_schedule(const oscar_dims* dims, int32_t batch, const void* workspace,
+                                size_t workspace_bytes, int32_t* splits, int32_t* requests,
+                                int32_t capacity, void* stream);
 
 /* Thread-local text of the last error ("" if none). */
 const char* oscar_last_error(void);

@@ -22,15 +22,20 @@ pytestmark = pytest.mark.gpu
 KERNELS = {"valu": 1, "mfma": 2}
 
 
-def run_decode(cache, rot, q, max_len, kind):
+def run_decode(cache, rot, q, max_len, kind, two_phase=False):
+    """Decode attention through oscar_decode, or oscar_decode_attn +
+    oscar_merge_lse when two_phase."""
     prev = ok.oscar_set_history_kernel(kind)
     try:
         ws = DecodeWorkspace(cache.dims, cache.batch, max_len)
-        out = torch.empty((cache.batch, cache.num_q_heads, 128), dtype=torch.float32, device="cuda")
-        lse = torch.empty((cache.batch, cache.num_q_heads), dtype=torch.float32, device="cuda")
+        out = torch.full((cache.batch, cache.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((cache.batch, cache.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
         c = cache.struct()
-        ok.oscar_decode_attn(cache.dims, rot.struct, c, q, max_len, ws.buf, ws.nbytes)
-        ok.oscar_merge_lse(cache.dims, rot.struct, cache.batch, max_len, ws.buf, ws.nbytes, out, lse)
+        if two_phase:
+            ok.oscar_decode_attn(cache.dims, rot.struct, c, q, max_len, ws.buf, ws.nbytes)
+            ok.oscar_merge_lse(cache.dims, rot.struct, cache.batch, max_len, ws.buf, ws.nbytes, out, lse)
+        else:
+            ok.oscar_decode(cache.dims, rot.struct, c, q, max_len, ws.buf, ws.nbytes, out, lse)
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy()
     finally:
@@ -110,6 +115,82 @@ def test_split_targets_edges(kernel, target):
         ok.oscar_set_history_target(prev)
 
 
+def _reference_split_pages(pages, target, max_per_request=251, min_pages=8):
+    """The documented split rule: the smallest q >= max(8, ceil(longest /
+    251)) whose split count sum(ceil(pages_b / q)) is at most target, else
+    the longest request's page count."""
+    pages = np.asarray(pages, dtype=np.int64)
+    longest = int(pages.max()) if pages.size else 0
+    lo = max(min_pages, -(-longest // max_per_request))
+    count = lambda q: int(np.sum(-(-pages // q)))
+    for q in range(lo, max(lo, longest) + 1):
+        if count(q) <= target:
+            return q
+    return max(lo, longest)
+
+
+@pytest.mark.parametrize("target", [0, 1, 40, 700])
+def test_schedule_invariants(target):
+    """The device schedule read back: per-request splits tile [0, pages_b)
+    in equal pieces, at most 251 per request, and follow the documented
+    choice of the split size."""
+    lens = [int(x) for x in gen.ragged_lengths(93, 300, 1, 40000)]
+    w = small("sched", 94, 4, 2, 128, lens)
+    layout, model, cal, rot, cache = setup(w)
+    q = W.queries_tensor(model, 0, w.batch)
+    prev = ok.oscar_set_history_target(target)
+    try:
+        ws = DecodeWorkspace(cache.dims, cache.batch, max(lens))
+        ok.oscar_decode_attn(cache.dims, rot.struct, cache.struct(), q, max(lens), ws.buf, ws.nbytes)
+        splits, reqs = ok.oscar_read_history_schedule(cache.dims, cache.batch, ws.buf, ws.nbytes)
+        slots = ok.oscar_history_splits(cache.dims, cache.batch, max(lens))
+    finally:
+        ok.oscar_set_history_target(prev)
+    t = slots - w.batch
+    pages = [max(0, L - 320 + 63) // 64 for L in lens]
+    q_ref = _reference_split_pages(pages, t)
+    busy = sum(p > 0 for p in pages)
+    assert len(splits) <= max(t, busy)
+    assert reqs[:, 1].sum() == len(splits)
+    for b, pg in enumerate(pages):
+        first, cnt = int(reqs[b, 0]), int(reqs[b, 1])
+        assert cnt == -(-pg // q_ref), (b, pg, cnt, q_ref)
+        assert cnt <= 251
+        if cnt == 0:
+            continue
+        per = -(-pg // cnt)
+        rows = splits[first:first + cnt]
+        assert (rows[:, 0] == b).all()
+        assert rows[0, 1] == 0 and rows[-1, 2] == pg
+        assert (rows[1:, 1] == rows[:-1, 2]).all()
+        assert (rows[:, 2] - rows[:, 1] == np.minimum(per, pg - rows[:, 1])).all()
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_long_single_split_precision(kernel):
+    """One 20K-token request in a single history split (target 1), against
+    the oracle at 1.5e-4: a long split must not drift.  (Rounding each small
+    fixed-point weight on its own to the unit of the largest one dropped the
+    many small weights from the value sum while l and the zero-point sum kept
+    them, a 5e-4 error on this case.)"""
+    w = small("long", 60, 8, 2, 128, [20000])
+    layout, model, cal, rot, cache = setup(w)
+    q_bits = model.queries(0, 1)
+    q = W.queries_tensor(model, 0, 1)
+    prev = ok.oscar_set_history_target(1)
+    try:
+        out, lse = run_decode(cache, rot, q, 20000, KERNELS[kernel])
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(str(e))
+        raise
+    finally:
+        ok.oscar_set_history_target(prev)
+    ref, ref_lse = oracle_request(model, layout, cal, q_bits[0], 0, 20000)
+    assert_close(out[0], ref, "long split", atol=1.5e-4, rel_l2=1e-5)
+    assert np.abs(lse[0] - ref_lse).max() < 1e-4
+
+
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_schedule_over_256_requests(kernel):
     """More requests than the scheduler's scan block (256 threads); a mix of
@@ -174,6 +255,25 @@ def test_deterministic_and_split_independent(kernel):
     # weights round differently per split, but must not drift with length
     assert_close(c, a, "split layouts", atol=1e-4, rel_l2=1e-5)
     assert_close(lc, la, "split layouts (lse)", atol=1e-4, rel_l2=1e-5)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("gqa,group", [(4, 64), (5, 128)])
+def test_decode_equals_two_phase(kernel, gqa, group):
+    """oscar_decode is oscar_decode_attn + oscar_merge_lse in one call: the
+    same launches, so the same bits."""
+    lens = [7000, 321, 2000, 65, 4500]
+    w = small(f"phases{gqa}", 75 + gqa, 2 * gqa, 2, group, lens)
+    layout, model, cal, rot, cache = setup(w)
+    q = W.queries_tensor(model, 0, w.batch)
+    try:
+        a, la = run_decode(cache, rot, q, max(lens), KERNELS[kernel])
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(str(e))
+        raise
+    b, lb = run_decode(cache, rot, q, max(lens), KERNELS[kernel], two_phase=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
 def test_valu_and_mfma_agree():

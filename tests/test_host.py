@@ -38,11 +38,11 @@ def test_block_bytes():
 def test_workspace_and_splits():
     d = ok.make_dims(32, 8, 128)
     s = ok.oscar_history_splits(d, 32, 100_000)
-    # default target min(251, 2048 / 8) splits per KV head, plus the batch
-    assert s == 251 + 32
+    # default target 2048 / 8 splits per KV head, plus the batch
+    assert s == 256 + 32
     assert ok.oscar_history_splits(d, 32, 1000) == s        # lengths decide on the device
-    # partials for 251 + B history splits and five bf16 chunks per head
-    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= (283 * 32 + 32 * 32 * 5) * 129 * 4
+    # partials for 8192 / 8 + B history splits and five bf16 chunks per head
+    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= (1056 * 32 + 32 * 32 * 5) * 129 * 4
     gqa8 = ok.make_dims(64, 8, 128)
     assert ok.oscar_history_splits(gqa8, 4, 1000) == 128 + 4  # 1024 workgroups for 8-wide groups
     prev = ok.oscar_set_history_target(64)
@@ -55,8 +55,9 @@ def test_workspace_and_splits():
         assert ok.oscar_history_splits(d, 2, 100_000) == 1 + 2
     finally:
         ok.oscar_set_history_target(prev)
-    with pytest.raises(ok.OscarError):
-        ok.oscar_set_history_target(-1)
+    for bad_target in (-1, 8193):
+        with pytest.raises(ok.OscarError):
+            ok.oscar_set_history_target(bad_target)
     bad = ok.make_dims(32, 8, 128, head_dim=64)
     assert ok.oscar_decode_workspace_bytes(bad, 1, 1000) == 0
     assert ok.oscar_history_splits(bad, 1, 1000) == -1
@@ -123,6 +124,10 @@ def test_null_and_inconsistent_arguments():
         ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 250, 10, 0x1000, 0x1000, 0)
     with pytest.raises(ok.OscarError):
         ok.oscar_merge_lse(d, _rot(), 1, 100, None, 1 << 30, 0x1000, None, 0)
+    # fused decode needs an output
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode(d, _rot(), _cache(), 0x1000, 100, 0x1000, 1 << 30, None, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "out" in ok.oscar_last_error()
 
 
 def test_empty_batch_and_zero_tokens_are_no_ops():
@@ -130,6 +135,7 @@ def test_empty_batch_and_zero_tokens_are_no_ops():
     ok.oscar_kv_demote(d, _rot(), _cache(batch=0), None, None, 0)
     ok.oscar_decode_attn(d, _rot(), _cache(batch=0), None, 100, None, 0, 0)
     ok.oscar_merge_lse(d, _rot(), 0, 100, None, 0, None, None, 0)
+    ok.oscar_decode(d, _rot(), _cache(batch=0), None, 100, None, 0, None, None, 0)
     ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 0, 0, None, None, 0)
 
 
