@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the OSCAR INT2 KV-cache path on one MI355X.
 
-A step is one pass of the whole hot path over the batch: append + demotion
-(oscar_kv_demote), then oscar_decode: query rotation and split schedule, one
-launch of INT2 history split-K + bf16 sink/recent whose last workgroup per
-(request, KV head) does the LSE merge + value un-rotation.  Inputs
+A step is one pass of the whole hot path over the batch (oscar_decode_step):
+append + demotion, query rotation and the split schedule in one launch; INT2
+history split-K + bf16 sink/recent in a second; LSE merge + value
+un-rotation in a third.  Inputs
 (cache, queries, new tokens, lengths) are resident in HBM before timing
 starts; every step appends one token per request, so lengths grow by one.
 
@@ -221,8 +221,8 @@ def main() -> int:
             ok.oscar_set_history_events(None, None)
         else:
             ok.oscar_set_history_events(ev_b[timed_idx].ptr, ev_a[timed_idx].ptr)
-        ok.oscar_kv_demote(dims, rot.struct, c, kn_all[s], vn_all[s], stream)
-        ok.oscar_decode(dims, rot.struct, c, q_all[s], max_len, ws.buf, ws.nbytes, out, None, stream)
+        ok.oscar_decode_step(dims, rot.struct, c, kn_all[s], vn_all[s], q_all[s], max_len, ws.buf,
+                             ws.nbytes, out, None, stream)
 
     for s in range(warmup):
         step(s, None)

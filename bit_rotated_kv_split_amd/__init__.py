@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     oscar_calibrate_workspace_bytes,
     oscar_decode,
     oscar_decode_attn,
+    oscar_decode_step,
     oscar_decode_workspace_bytes,
     oscar_history_kernel_for,
     oscar_history_splits,

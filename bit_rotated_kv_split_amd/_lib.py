@@ -68,6 +68,10 @@ _SIGS = [
     ("oscar_decode", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_decode_step", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]),
     ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -193,6 +197,13 @@ def oscar_decode(dims, rot, cache, q, max_seq_len: int, workspace, workspace_byt
     _check(lib().oscar_decode(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(q),
                               max_seq_len, _ptr(workspace), workspace_bytes, _ptr(out),
                               _ptr(lse_out), _stream(stream)))
+
+
+def oscar_decode_step(dims, rot, cache, k_new, v_new, q, max_seq_len: int, workspace,
+                      workspace_bytes: int, out, lse_out=None, stream=None) -> None:
+    _check(lib().oscar_decode_step(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
+                                   _ptr(k_new), _ptr(v_new), _ptr(q), max_seq_len, _ptr(workspace),
+                                   workspace_bytes, _ptr(out), _ptr(lse_out), _stream(stream)))
 
 
 def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspace_bytes: int,

@@ -239,10 +239,13 @@ namespace {
 // oscar_decode (merged output).
 int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
-                float* out, float* lse_out, void* stream) {
+                float* out, float* lse_out, bool demote, const uint16_t* k_new, const uint16_t* v_new,
+                void* stream) {
   g_error.clear();
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(OSCAR_EINVAL, "k_new and v_new must both be set or both be NULL");
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
   if (cache->batch == 0) return OSCAR_OK;
   if (q == nullptr || workspace == nullptr) return fail(OSCAR_EINVAL, "q or workspace is NULL");
@@ -255,6 +258,11 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
+  DemoteStep dm;
+  if (demote) {
+    dm = make_demote_step(*dims, *rot, *cache, k_new, v_new);
+    a.demote = &dm;
+  }
   hipError_t e = launch_qrot(a, s);
   if (e != hipSuccess) return hip_fail(e, "query rotation launch");
   const int kind = g_hist_kernel.load();
@@ -284,7 +292,8 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
 int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                       const uint16_t* q, int32_t max_seq_len, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, nullptr, stream);
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, nullptr, false,
+                     nullptr, nullptr, stream);
 }
 
 int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
@@ -294,7 +303,20 @@ int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_
     g_error.clear();
     return fail(OSCAR_EINVAL, "out is NULL");
   }
-  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, stream);
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, false,
+                     nullptr, nullptr, stream);
+}
+
+int oscar_decode_step(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                      const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse_out, void* stream) {
+  if (out == nullptr && cache != nullptr && cache->batch > 0) {
+    g_error.clear();
+    return fail(OSCAR_EINVAL, "out is NULL");
+  }
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, true,
+                     k_new, v_new, stream);
 }
 
 int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,

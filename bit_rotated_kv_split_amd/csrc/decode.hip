@@ -20,8 +20,7 @@
 #include <math.h>
 
 #include "decode_bf16.h"
-#include "oscar_device.h"
-#include "oscar_internal.h"
+#include "demote_device.h"
 
 namespace oscar {
 namespace {
@@ -138,12 +137,21 @@ __global__ void __launch_bounds__(256)
 qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int hq, int hkv, int G,
             float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack,
             const int32_t* __restrict__ seq_lens, int batch, int target, int32_t* __restrict__ sched,
-            int32_t* __restrict__ req) {
-  // row 0 of the grid (dispatched first) holds the split scheduler; rows
-  // 1 .. B rotate the queries of request blockIdx.y - 1
+            int32_t* __restrict__ req, DemoteStep dm) {
+  // Row 0 of the grid (dispatched first) holds the split scheduler; rows
+  // 1 .. B rotate the queries of request blockIdx.y - 1; rows B+1 .. 2B, when
+  // launched, demote the step's oldest recent token of request
+  // blockIdx.y - B - 1 (threads 0..127 the key, 128..255 the value), which
+  // touches nothing the other rows read.
   const int kvh = blockIdx.x, b = static_cast<int>(blockIdx.y) - 1;
   if (b < 0) {
     if (kvh == 0) schedule_splits(seq_lens, batch, target, sched, req);
+    return;
+  }
+  if (b >= batch) {
+    __shared__ QuantSmem<1> dsm[2];
+    const int half = threadIdx.x >> 7;
+    demote_unit_g(G, dm, kvh, b - batch, half != 0, threadIdx.x & 127, dsm[half]);
     return;
   }
   const int tid = threadIdx.x, k = tid & (kDim - 1), half = tid >> 7;
@@ -415,11 +423,17 @@ __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
   bf16_chunk<GQ>(a, GQ, 0, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
-// LSE merge: workgroup = (KV head, request), 256 threads.  The request's
-// history splits (from the schedule) are merged per head in the rotated
-// value domain, rotated back by R_V^T, and merged with the five bf16
-// partials.  Loads are issued early: each thread's half-row of R_V before
-// anything else, then the partials.
+// LSE merge, two launch shapes.  merge_head_kernel: workgroup = (query
+// head, request), for batches too small to fill the chip by KV head;
+// merge_group_kernel: workgroup = (KV head, request), sharing R_V across the
+// group's heads.
+//
+// merge_head_kernel (256 threads): the request's
+// history splits (from the schedule) are merged in the rotated value domain,
+// rotated back by R_V^T, and merged with the five bf16 partials.  Thread t
+// weighs split t; the weighted sum over splits runs on both halves of the
+// workgroup (channel t % 128, every other split); the rotation gives each
+// thread half a row of R_V, loaded before anything else.
 struct MergeParams {
   const float* ho;        // [slots][Hq][128]
   const float* hlse;      // [slots][Hq]
@@ -430,10 +444,115 @@ struct MergeParams {
   float* out;
   float* lse_out;
   int32_t hq;
+  int32_t gq;
 };
 
+__device__ __forceinline__ float block_max_f(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum_f(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void __launch_bounds__(256) merge_head_kernel(MergeParams a) {
+  const int head = blockIdx.x, b = blockIdx.y, kvh = head / a.gq;
+  const int tid = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float w[kMaxSplits + 1];
+  __shared__ float ypart[2][kDim];
+  __shared__ float y[kDim];
+  const int first = a.req[2 * b], count = a.req[2 * b + 1];
+  const size_t bh = static_cast<size_t>(b) * a.hq + head;
+  // row i of R_V, columns 64 kh .. 64 kh + 63
+  const int i = tid >> 1, kh = tid & 1;
+  float4 rr[16];
+  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  // history split weights e^{lse - M} / sum (count <= kMaxSplits < 256)
+  const float l = tid < count ? a.hlse[static_cast<size_t>(first + tid) * a.hq + head] : -INFINITY;
+  const float mh = block_max_f(l, red);
+  const float e = mh == -INFINITY || tid >= count ? 0.f : expf(l - mh);
+  const float dh = block_sum_f(e, red);
+  if (tid < count) w[tid] = dh > 0.f ? e / dh : 0.f;
+  const float lse_h = dh > 0.f ? mh + logf(dh) : -INFINITY;
+  // bf16 partial weights (every thread computes the five)
+  float lb[kBf16Parts], mb = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kBf16Parts; ++c) {
+    lb[c] = a.blse[bh * kBf16Parts + c];
+    mb = fmaxf(mb, lb[c]);
+  }
+  float db = 0.f;
+#pragma unroll
+  for (int c = 0; c < kBf16Parts; ++c) db += lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb);
+  const float lse_b = mb + logf(db);   // the sink chunk always holds a token
+  __syncthreads();
+  // weighted sum over the splits: channel k, splits of parity par
+  {
+    const int k = tid & (kDim - 1), par = tid >> 7;
+    const float* hp = a.ho + (static_cast<size_t>(first) * a.hq + head) * kDim + k;
+    const size_t stride = static_cast<size_t>(a.hq) * kDim;
+    float acc = 0.f;
+    for (int s0 = par; s0 < count; s0 += 32) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int sp = s0 + 2 * u;
+        v[u] = sp < count ? hp[static_cast<size_t>(sp) * stride] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int sp = s0 + 2 * u;
+        if (sp < count) acc = __builtin_fmaf(w[sp], v[u], acc);
+      }
+    }
+    ypart[par][k] = acc;
+  }
+  __syncthreads();
+  if (tid < kDim) y[tid] = ypart[0][tid] + ypart[1][tid];
+  __syncthreads();
+  // back to the model domain: x_i = sum_k y_k R_V[i][k]
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int k = 64 * kh + 4 * c;
+    acc = __builtin_fmaf(y[k + 0], rr[c].x, acc);
+    acc = __builtin_fmaf(y[k + 1], rr[c].y, acc);
+    acc = __builtin_fmaf(y[k + 2], rr[c].z, acc);
+    acc = __builtin_fmaf(y[k + 3], rr[c].w, acc);
+  }
+  const float xh = acc + __shfl_xor(acc, 1, 64);
+  if (kh == 0) {
+    float ob = 0.f;
+#pragma unroll
+    for (int c = 0; c < kBf16Parts; ++c) {
+      const float wc = lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb) / db;
+      ob = __builtin_fmaf(wc, a.bo[(bh * kBf16Parts + c) * kDim + i], ob);
+    }
+    const float mx = fmaxf(lse_h, lse_b);
+    const float eh = lse_h == -INFINITY ? 0.f : expf(lse_h - mx), eb = expf(lse_b - mx);
+    const float den = eh + eb;
+    a.out[bh * kDim + i] = (eh * xh + eb * ob) / den;
+    if (a.lse_out != nullptr && i == 0) a.lse_out[bh] = mx + logf(den);
+  }
+}
+
+// merge_group_kernel (256 threads): the request's history splits are
+// merged per head in the rotated value domain, rotated back by R_V^T, and
+// merged with the five bf16 partials.  Loads are issued early: each
+// thread's half-row of R_V before anything else, then the partials.
 template <int GQ>
-__global__ void __launch_bounds__(256) merge_kernel(MergeParams a) {
+__global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int kMaxHist = kMaxSplits + 1;
@@ -547,12 +666,14 @@ template <int GQ>
 struct QrotRun {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const oscar_dims& d = *a.dims;
-    const dim3 grid(d.num_kv_heads, a.cache->batch + 1);
+    const int batch = a.cache->batch;
+    const dim3 grid(d.num_kv_heads, 1 + batch + (a.demote != nullptr ? batch : 0));
     qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
-        a.ws + a.lay.off_qpack, a.cache->seq_lens, a.cache->batch, a.lay.target,
-        reinterpret_cast<int32_t*>(a.ws + a.lay.off_sched), reinterpret_cast<int32_t*>(a.ws + a.lay.off_req));
+        a.ws + a.lay.off_qpack, a.cache->seq_lens, batch, a.lay.target,
+        reinterpret_cast<int32_t*>(a.ws + a.lay.off_sched), reinterpret_cast<int32_t*>(a.ws + a.lay.off_req),
+        a.demote != nullptr ? *a.demote : DemoteStep{});
     return hipGetLastError();
   }
 };
@@ -603,25 +724,16 @@ struct Bf16Run {
 };
 
 template <int GQ>
-struct MergeRun {
-  static hipError_t run(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
-                        const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
-                        hipStream_t s) {
-    const dim3 grid(d.num_kv_heads, batch);
-    MergeParams p;
-    p.ho = reinterpret_cast<const float*>(ws + lay.off_ho);
-    p.hlse = reinterpret_cast<const float*>(ws + lay.off_hlse);
-    p.bo = reinterpret_cast<const float*>(ws + lay.off_bo);
-    p.blse = reinterpret_cast<const float*>(ws + lay.off_blse);
-    p.req = reinterpret_cast<const int32_t*>(ws + lay.off_req);
-    p.r_v = rot.r_v;
-    p.out = out;
-    p.lse_out = lse_out;
-    p.hq = d.num_q_heads;
-    merge_kernel<GQ><<<grid, 256, 0, s>>>(p);
+struct MergeGroupRun {
+  static hipError_t run(const MergeParams& p, int hkv, int32_t batch, hipStream_t s) {
+    merge_group_kernel<GQ><<<dim3(hkv, batch), 256, 0, s>>>(p);
     return hipGetLastError();
   }
 };
+
+// Below this many (request, KV head) workgroups the merge runs one
+// workgroup per query head.
+constexpr int kMergeGroupMinWgs = 128;
 
 }  // namespace
 
@@ -640,8 +752,22 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
                         hipStream_t s) {
-  return dispatch_gq<MergeRun>(d.num_q_heads / d.num_kv_heads, d, rot, batch, ws, lay, out,
-                               lse_out, s);
+  MergeParams p;
+  p.ho = reinterpret_cast<const float*>(ws + lay.off_ho);
+  p.hlse = reinterpret_cast<const float*>(ws + lay.off_hlse);
+  p.bo = reinterpret_cast<const float*>(ws + lay.off_bo);
+  p.blse = reinterpret_cast<const float*>(ws + lay.off_blse);
+  p.req = reinterpret_cast<const int32_t*>(ws + lay.off_req);
+  p.r_v = rot.r_v;
+  p.out = out;
+  p.lse_out = lse_out;
+  p.hq = d.num_q_heads;
+  p.gq = d.num_q_heads / d.num_kv_heads;
+  if (static_cast<int64_t>(batch) * d.num_kv_heads < kMergeGroupMinWgs) {
+    merge_head_kernel<<<dim3(d.num_q_heads, batch), 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  return dispatch_gq<MergeGroupRun>(p.gq, p, d.num_kv_heads, batch, s);
 }
 
 }  // namespace oscar

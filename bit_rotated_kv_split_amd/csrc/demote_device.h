@@ -1,0 +1,195 @@
+// Demotion device code shared by the demotion and decode-prologue kernels:
+// rotate, clip, quantize and pack tokens into history page blocks (page
+// "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务", section
+// "OSCAR的另一个关键点是"; the quantizer of the first page, section
+// "为什么 INT2 KV 缓存量化很难？").
+#pragma once
+
+#include "oscar_device.h"
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+constexpr int kMaxChunk = 16;
+
+// Shared memory of one 128-thread demotion unit (sized for the smallest
+// group, G = 32, so one type serves every G).
+template <int NT>
+struct QuantSmem {
+  static constexpr int kMaxNG = kDim / 32;
+  float x[NT][kDim];
+  float y[NT][kDim];
+  float scale[NT][kMaxNG];
+  float zero[NT][kMaxNG];
+  float xw[2][NT][2];          // per-wave (min, max) when a group spans both waves
+  uint8_t code[NT][kDim];
+};
+
+// Rotate, clip and quantize nt (<= NT) tokens held in sm.x.  Called by the
+// 128 threads of one unit (k = 0..127, two whole waves); every thread of the
+// workgroup passes the same barriers.  Leaves codes, scale and zero in sm.
+template <int G, int NT>
+__device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restrict__ r,
+                                const float* __restrict__ clipv, int k) {
+  constexpr int WG = G < 64 ? G : 64;   // group lanes inside one wave
+  const int lane = k & 63, wave = k >> 6;
+  auto& xw = sm.xw;
+  double acc[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
+  if constexpr (NT == 1) {
+    // one token: every load of the rotation column in flight at once
+    float rv[kDim];
+#pragma unroll
+    for (int i = 0; i < kDim; ++i) rv[i] = r[i * kDim + k];
+#pragma unroll
+    for (int i = 0; i < kDim; ++i)
+      acc[0][i & 3] = fma(static_cast<double>(sm.x[0][i]), static_cast<double>(rv[i]), acc[0][i & 3]);
+  } else {
+    for (int i = 0; i < kDim; i += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double rik = static_cast<double>(r[(i + u) * kDim + k]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
+      }
+    }
+  }
+  const float c = clipv[k];
+  float y[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const double sum = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
+    y[t] = fminf(fmaxf(static_cast<float>(sum), -c), c);
+    sm.y[t][k] = y[t];
+  }
+  // group min / max across the G lanes of a group
+  float mn[NT], mx[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    mn[t] = y[t];
+    mx[t] = y[t];
+#pragma unroll
+    for (int off = 1; off < WG; off <<= 1) {
+      mn[t] = fminf(mn[t], __shfl_xor(mn[t], off, 64));
+      mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], off, 64));
+    }
+  }
+  if constexpr (G == 128) {
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        xw[wave][t][0] = mn[t];
+        xw[wave][t][1] = mx[t];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      mn[t] = fminf(xw[0][t][0], xw[1][t][0]);
+      mx[t] = fmaxf(xw[0][t][1], xw[1][t][1]);
+    }
+  }
+  const int gi = k / G;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float range = mx[t] - mn[t];
+    const float s = bf16_round(range / 3.0f);
+    const float z = bf16_round(mn[t]);
+    if (k % G == 0 && t < nt) {
+      sm.scale[t][gi] = s;
+      sm.zero[t][gi] = z;
+    }
+    int code = 0;
+    if (s != 0.f) {
+      const float diff = y[t] - z;
+      const float q = rintf(diff / s);
+      code = static_cast<int>(fminf(fmaxf(q, 0.f), 3.f));
+    }
+    if (t < nt) sm.code[t][k] = static_cast<uint8_t>(code);
+  }
+  __syncthreads();
+}
+
+// Store nt quantized tokens occupying slots slot0 .. slot0+nt-1 of one page
+// block (all inside one 16-slot value word).  is_v selects the value half.
+template <int G, int NT>
+__device__ void store_tokens(const QuantSmem<NT>& sm, int nt, uint8_t* __restrict__ blk,
+                             int slot0, bool is_v, int k) {
+  constexpr int NG = kDim / G;
+  uint32_t* words = reinterpret_cast<uint32_t*>(blk);
+  if (!is_v) {
+    for (int job = k; job < nt * 8; job += kDim) {
+      const int t = job >> 3, d = job & 7;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w |= static_cast<uint32_t>(sm.code[t][16 * d + i]) << (2 * i);
+      words[d * 64 + qk_order(slot0 + t)] = w;
+    }
+  } else {
+    // channel k: one value word holds slots 16w..16w+15 of this channel
+    const int w = slot0 >> 4;
+    uint32_t bits = 0, mask = 0;
+    for (int t = 0; t < nt; ++t) {
+      const int sh = 2 * ((slot0 + t) & 15);
+      bits |= static_cast<uint32_t>(sm.code[t][k]) << sh;
+      mask |= 3u << sh;
+    }
+    uint32_t* wp = words + 512 + v_word_index(k, w);
+    const uint32_t old = (mask == 0xFFFFFFFFu) ? 0u : *wp;
+    *wp = (old & ~mask) | bits;
+  }
+  uint16_t* sz = reinterpret_cast<uint16_t*>(blk + kCodesBytes + (is_v ? kPage * NG * 4 : 0));
+  for (int job = k; job < nt * NG; job += kDim) {
+    const int t = job / NG, gi = job % NG;
+    uint16_t* e = sz + (qk_order(slot0 + t) * NG + gi) * 2;
+    e[0] = f32_to_bf16_rne(sm.scale[t][gi]);
+    e[1] = f32_to_bf16_rne(sm.zero[t][gi]);
+  }
+}
+
+// Demotion of one (request, KV head, K or V) for a decode step, by one
+// 128-thread unit (thread k): the token at position L-257 leaves the recent
+// ring for history index L-321, then the new token (if given) takes its
+// sink or recent slot.
+template <int G>
+__device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int k, QuantSmem<1>& sm) {
+  const DemoteArgs& a = is_v ? d.vv : d.kk;
+  const int hkv = a.hkv;
+  const int L = d.seq_lens[b];
+  uint16_t* recent = (is_v ? d.recent_v : d.recent_k) + (static_cast<size_t>(b) * hkv + kvh) * kRecent * kDim;
+  if (L > kBf16Tokens) {   // uniform across the workgroup
+    const int j = L - kBf16Tokens - 1;            // history index of position L-257
+    const int ring = (L - 1 - kSink) & (kRecent - 1);
+    sm.x[0][k] = bf16_to_f32(recent[ring * kDim + k]);
+    __syncthreads();
+    quantize_tokens<G, 1>(sm, 1, a.r + static_cast<size_t>(kvh) * kDim * kDim, a.clip + kvh * kDim, k);
+    const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + (j >> 6)];
+    uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
+    store_tokens<G, 1>(sm, 1, blk, j & 63, is_v, k);
+  }
+  const uint16_t* src = is_v ? d.v_new : d.k_new;
+  if (src != nullptr && L >= 1) {
+    const int p = L - 1;
+    const uint16_t val = src[(static_cast<size_t>(b) * hkv + kvh) * kDim + k];
+    if (p < kSink) {
+      uint16_t* sink = (is_v ? d.sink_v : d.sink_k) + (static_cast<size_t>(b) * hkv + kvh) * kSink * kDim;
+      sink[p * kDim + k] = val;
+    } else {
+      recent[((p - kSink) & (kRecent - 1)) * kDim + k] = val;
+    }
+  }
+}
+
+// Runtime-G dispatch of demote_unit.
+__device__ __forceinline__ void demote_unit_g(int group, const DemoteStep& d, int kvh, int b, bool is_v, int k,
+                                              QuantSmem<1>& sm) {
+  if (group == 32) demote_unit<32>(d, kvh, b, is_v, k, sm);
+  else if (group == 64) demote_unit<64>(d, kvh, b, is_v, k, sm);
+  else demote_unit<128>(d, kvh, b, is_v, k, sm);
+}
+
+}  // namespace
+}  // namespace oscar

@@ -66,6 +66,20 @@ struct DemoteArgs {
   int32_t hkv;
 };
 
+// Everything one decode step's demotion reads and writes.
+struct DemoteStep {
+  DemoteArgs kk, vv;
+  const int32_t* seq_lens;
+  uint16_t* sink_k;
+  uint16_t* sink_v;
+  uint16_t* recent_k;
+  uint16_t* recent_v;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+};
+
+DemoteStep make_demote_step(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
+                            const uint16_t* k_new, const uint16_t* v_new);
 hipError_t launch_demote(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
 hipError_t launch_fill(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
@@ -81,6 +95,7 @@ struct DecodeArgs {
   WsLayout lay;
   hipEvent_t ev_start = nullptr;   // when both set, the history kernel is launched
   hipEvent_t ev_stop = nullptr;    // with these as its start/stop timestamps
+  const DemoteStep* demote = nullptr;   // when set, the prologue launch also demotes
 };
 
 hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);

@@ -80,9 +80,8 @@ class DecodeWorkspace:
 
 def decode_step(cache: PagedKVCache, rot: Rotation, ws: DecodeWorkspace, q, out, lse=None,
                 k_new=None, v_new=None, stream=None) -> None:
-    """One decode step on the current stream: demote (and append k_new/v_new
-    if given), then decode attention with the merge (oscar_decode).
-    seq_lens must already count the new token."""
-    c = cache.struct()
-    _lib.oscar_kv_demote(cache.dims, rot.struct, c, k_new, v_new, stream)
-    _lib.oscar_decode(cache.dims, rot.struct, c, q, ws.max_seq_len, ws.buf, ws.nbytes, out, lse, stream)
+    """One decode step on the current stream (oscar_decode_step): demote (and
+    append k_new/v_new if given), decode attention, merge.  seq_lens must
+    already count the new token."""
+    _lib.oscar_decode_step(cache.dims, rot.struct, cache.struct(), k_new, v_new, q, ws.max_seq_len,
+                           ws.buf, ws.nbytes, out, lse, stream)

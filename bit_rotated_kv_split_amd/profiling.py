@@ -11,8 +11,8 @@ of the history kernel into bytes per launch.  Each counter is scaled by
 what it reads for the 2 GiB device copy that `bench.py --copy-probe` runs in
 the same process (copy bytes / counter bytes), so a counter that covers
 only part of the memory channels is corrected.  The record carries a hash of
-the decode kernel sources; `bench.py` reports it only while that hash
-matches the sources it runs.
+the decode kernel sources (csrc/decode*, csrc/*.h); `bench.py` reports it
+only while that hash matches the sources it runs.
 """
 from __future__ import annotations
 
@@ -72,7 +72,7 @@ def source_sha(root: str) -> str:
     h = hashlib.sha256()
     d = os.path.join(root, "bit_rotated_kv_split_amd", "csrc")
     for name in sorted(os.listdir(d)):
-        if name.startswith("decode"):
+        if name.startswith("decode") or name.endswith(".h"):
             h.update(open(os.path.join(d, name), "rb").read())
     return h.hexdigest()[:16]
 

@@ -175,6 +175,16 @@ int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_
                  const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                  float* out, float* lse_out, void* stream);
 
+/* One whole decode step: oscar_kv_demote(k_new, v_new) then
+ * oscar_decode, in three launches instead of four (the demotion runs in the
+ * query-rotation launch; it writes only the history slot of position L-257
+ * and the new token's slot, which that launch does not read).  Same
+ * arguments, requirements and results as those two calls in order. */
+int oscar_decode_step(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                      const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse_out, void* stream);
+
 /* Log-sum-exp merge: combine the history partials, rotate the history
  * output back by R_V^T, merge it with the sink/recent partial and write
  * out: float32 [B][Hq][128].  lse_out (may be NULL): float32 [B][Hq], the

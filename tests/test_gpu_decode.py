@@ -276,6 +276,39 @@ def test_decode_equals_two_phase(kernel, gqa, group):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("group", [32, 128])
+def test_decode_step_equals_separate_calls(group):
+    """oscar_decode_step (demotion inside the rotation launch) against
+    oscar_kv_demote + oscar_decode on a copy of the same cache: same output
+    bits, same cache bytes afterwards."""
+    lens = [2000, 330, 321, 64, 5000]
+    w = small(f"stepfuse{group}", 88, 8, 2, group, lens)
+    layout, model, cal, rot, cache = setup(w)
+    lens1 = layout.lens + 1
+    cache.seq_lens.copy_(torch.from_numpy(lens1.astype(np.int32)))
+    kn = W.new_tokens_tensor(model, layout, lens1, "k")
+    vn = W.new_tokens_tensor(model, layout, lens1, "v")
+    q = W.queries_tensor(model, 1, w.batch)
+    snap = [t.clone() for t in (cache.pages, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v)]
+    ws = DecodeWorkspace(cache.dims, w.batch, int(lens1.max()))
+    out_a = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    out_b = torch.empty_like(out_a)
+    lse_a = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    ok.oscar_decode_step(cache.dims, rot.struct, cache.struct(), kn, vn, q, ws.max_seq_len, ws.buf,
+                         ws.nbytes, out_a, lse_a)
+    torch.cuda.synchronize()
+    after_a = [t.clone() for t in (cache.pages, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v)]
+    for t, s0 in zip((cache.pages, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v), snap):
+        t.copy_(s0)
+    ok.oscar_kv_demote(cache.dims, rot.struct, cache.struct(), kn, vn)
+    ok.oscar_decode(cache.dims, rot.struct, cache.struct(), q, ws.max_seq_len, ws.buf, ws.nbytes, out_b, lse_b)
+    torch.cuda.synchronize()
+    for t, ta in zip((cache.pages, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v), after_a):
+        assert torch.equal(t, ta)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
 def test_valu_and_mfma_agree():
     w = small("agree", 70, 8, 2, 128, [7000, 321, 2000])
     layout, model, cal, rot, cache = setup(w)

@@ -128,6 +128,9 @@ def test_null_and_inconsistent_arguments():
     with pytest.raises(ok.OscarError) as e:
         ok.oscar_decode(d, _rot(), _cache(), 0x1000, 100, 0x1000, 1 << 30, None, None, 0)
     assert e.value.code == ok.OSCAR_EINVAL and "out" in ok.oscar_last_error()
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode_step(d, _rot(), _cache(), 0x1000, None, 0x1000, 100, 0x1000, 1 << 30, 0x1000, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "k_new" in ok.oscar_last_error()
 
 
 def test_empty_batch_and_zero_tokens_are_no_ops():
@@ -136,6 +139,7 @@ def test_empty_batch_and_zero_tokens_are_no_ops():
     ok.oscar_decode_attn(d, _rot(), _cache(batch=0), None, 100, None, 0, 0)
     ok.oscar_merge_lse(d, _rot(), 0, 100, None, 0, None, None, 0)
     ok.oscar_decode(d, _rot(), _cache(batch=0), None, 100, None, 0, None, None, 0)
+    ok.oscar_decode_step(d, _rot(), _cache(batch=0), None, None, None, 100, None, 0, None, None, 0)
     ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 0, 0, None, None, 0)
 
 
