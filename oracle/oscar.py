@@ -450,6 +450,15 @@ def merge_lse(outs, lses):
     return (w[:, :, None] * outs).sum(axis=0) / tot[:, None], mx + np.log(tot)
 
 
+def bf16_cache_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray):
+    """Decode attention over an all-bf16 KV cache: the baseline the pages
+    measure INT2 against ([A] §结果 and [B] §OSCAR的另一个关键点是 compare
+    with a BF16 KV cache).  q_bits [g][128], k_bits and v_bits [L][128]
+    bf16 bit patterns, no rotation, no quantization; one softmax with scale
+    1/sqrt(128) in float64.  Returns (out [g][128], natural-log lse [g])."""
+    return partial_attend(bf16_value(q_bits), bf16_value(k_bits), bf16_value(v_bits))
+
+
 def bits_per_element(L: int, group: int) -> float:
     """Average stored bits per KV element of a request holding L tokens:
     16 for the 320 bf16 tokens, 2 + 2*16/G for history (bf16 scale and zero

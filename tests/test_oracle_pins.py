@@ -423,6 +423,42 @@ def test_request_attention_brute_force(L):
         assert np.abs(lse[j * g:(j + 1) * g] - bl).max() < 1e-11
 
 
+@pytest.mark.parametrize("L", [1, 7, 16])
+def test_bf16_cache_attention_brute_force(L):
+    """The all-bf16 baseline attention against explicit loops (fsum, math.exp)."""
+    r = rng(300 + L)
+    q = gen.bf16_bits(r.standard_normal((3, 128)).astype(np.float32))
+    k = gen.bf16_bits((r.standard_normal((L, 128)) * 2).astype(np.float32))
+    v = gen.bf16_bits(r.standard_normal((L, 128)).astype(np.float32))
+    out, lse = O.bf16_cache_attention(q, k, v)
+    qv, kv, vv = O.bf16_value(q), O.bf16_value(k), O.bf16_value(v)
+    for h in range(3):
+        sc = [math.fsum(qv[h, c] * kv[t, c] for c in range(128)) / math.sqrt(128) for t in range(L)]
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        tot = math.fsum(w)
+        ref = np.array([math.fsum(w[t] * vv[t, c] for t in range(L)) / tot for c in range(128)])
+        assert np.abs(out[h] - ref).max() < 1e-12
+        assert abs(lse[h] - (m + math.log(tot))) < 1e-12
+
+
+def test_bf16_cache_attention_is_request_attention_without_history():
+    """Up to 320 tokens the INT2 cache holds everything in bf16, so the two
+    oracle routes must agree exactly there."""
+    r = rng(301)
+    L, hkv, g = 300, 2, 3
+    k = gen.bf16_bits(r.standard_normal((L, hkv, 128)).astype(np.float32))
+    v = gen.bf16_bits(r.standard_normal((L, hkv, 128)).astype(np.float32))
+    q = gen.bf16_bits(r.standard_normal((hkv * g, 128)).astype(np.float32))
+    eye = np.broadcast_to(np.eye(128, dtype=np.float32), (hkv, 128, 128)).copy()
+    clip = np.full((hkv, 128), 10.0, dtype=np.float32)
+    out, lse = O.request_attention(q, k, v, eye, eye, clip, clip, 128)
+    for j in range(hkv):
+        o2, l2 = O.bf16_cache_attention(q[j * g:(j + 1) * g], k[:, j], v[:, j])
+        assert np.abs(out[j * g:(j + 1) * g] - o2).max() < 1e-13
+        assert np.abs(lse[j * g:(j + 1) * g] - l2).max() < 1e-13
+
+
 def test_split_merge_equals_single_softmax():
     r = rng(16)
     q = r.standard_normal((3, 128))
