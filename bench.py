@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PAGE = 64
 METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 100K ctx, batch 32"
 
 
@@ -134,6 +135,17 @@ def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 
                       f"(numpy); {done_bytes / 1e9:.3f} GB of the step's algorithmic bytes"}
 
 
+def default_layers(workload: str) -> int:
+    """Independent layer caches a run cycles through: the single-request
+    workload's cache (57 MB) would otherwise sit in the 256 MB last-level
+    cache, so ten are cycled (one per step) to keep its reads in HBM."""
+    return 10 if workload == "b1-100k" else 1
+
+
+def pct(xs, q):
+    return round(float(np.percentile(np.asarray(xs), q)), 2)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,10 +153,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b32-100k-g128", choices=sorted(workloads()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent layer caches cycled one per step (0: 10 for b1-100k, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads in the oracle sample")
+    ap.add_argument("--bf16-baseline", choices=["auto", "on", "off"], default="auto",
+                    help="also time the all-bf16 cache decode step (auto: on for the 32 x 100K workloads)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run one 2 GiB device copy (bandwidth reference, PMC scale)")
+                    help="accepted for older command lines; the 2 GiB copy probe always runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path runs within one MI355X and "
@@ -162,7 +178,9 @@ def main() -> int:
     w = workloads()[args.workload]()
     steps, warmup = args.steps, args.warmup
     total = steps + warmup
-    layout = W.Layout(w, None, extra_tokens=total)
+    n_layers = args.layers or default_layers(args.workload)
+    appends = -(-total // n_layers)          # tokens each layer cache receives
+    layout = W.Layout(w, None, extra_tokens=appends)
     model = W.SyntheticModel(w)
     B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
     dims = ok.make_dims(hq, hkv, w.group_size)
@@ -185,96 +203,111 @@ def main() -> int:
     rot = Rotation(r_k, r_v, c_k, c_v)
 
     t0 = time.perf_counter()
-    cache = W.build_cache(w, layout, model, rot)
+    caches = [W.build_cache(w, layout, model, rot) for _ in range(n_layers)]
     fill_s = time.perf_counter() - t0
 
-    # per-step inputs, resident before timing
-    lens_all = layout.lens[None, :] + np.arange(1, total + 1)[:, None]
-    seq_dev = torch.from_numpy(lens_all.astype(np.int32)).cuda()
+    # per-step inputs, resident before timing.  Step s runs layer s % n_layers
+    # after that layer's (s // n_layers + 1)-th append.
+    lens_t = layout.lens[None, :] + np.arange(1, appends + 1)[:, None]      # [appends][B]
+    lens_step = np.stack([lens_t[s // n_layers] for s in range(total)])
+    seq_dev = torch.from_numpy(lens_t.astype(np.int32)).cuda()
     q_all = torch.stack([W.queries_tensor(model, s, B) for s in range(1, total + 1)])
-    kn = np.zeros((total, B, hkv, 128), np.uint16)
+    kn = np.zeros((appends, B, hkv, 128), np.uint16)
     vn = np.zeros_like(kn)
     for b in range(B):
         p0 = int(layout.lens[b])
         for j in range(hkv):
-            for src, a, n in layout.src_ranges(b, p0, total):
+            for src, a, n in layout.src_ranges(b, p0, appends):
                 kn[a - p0:a - p0 + n, b, j] = gen.kv_tokens_bf16(w.seed, "k", src, j, a, n, model.k_scale[j])
                 vn[a - p0:a - p0 + n, b, j] = gen.kv_tokens_bf16(w.seed, "v", src, j, a, n, model.v_scale[j])
     kn_all = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).cuda()
     vn_all = torch.from_numpy(vn.view(np.int16)).view(torch.bfloat16).cuda()
-    max_len = int(lens_all.max())
+    max_len = int(lens_t.max())
     ws = DecodeWorkspace(dims, B, max_len)
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
-    base = cache.struct()
-    structs = [ok.make_cache(cache.pages, cache.n_pages, cache.sink_k, cache.sink_v, cache.recent_k,
-                             cache.recent_v, cache.page_table, cache.max_pages_per_req,
-                             seq_dev[s].data_ptr(), B) for s in range(total)]
-    del base
+    structs = [[ok.make_cache(c.pages, c.n_pages, c.sink_k, c.sink_v, c.recent_k, c.recent_v, c.page_table,
+                              c.max_pages_per_req, seq_dev[t].data_ptr(), B) for t in range(appends)]
+               for c in caches]
     kind = {"auto": 0, "valu": 1, "mfma": 2}[args.kernel]
     ok.oscar_set_history_kernel(kind)
-    ev_b = [HipEvent() for _ in range(steps)]
-    ev_a = [HipEvent() for _ in range(steps)]
 
-    def step(s: int, timed_idx: int | None):
-        c = structs[s]
-        if timed_idx is None:
+    def timed_run(one_step):
+        """Warm up, then time `steps` steps: per-step and history-launch events."""
+        ev_b = [HipEvent() for _ in range(steps)]
+        ev_a = [HipEvent() for _ in range(steps)]
+        marks = [HipEvent() for _ in range(steps + 1)]
+        for s in range(warmup):
             ok.oscar_set_history_events(None, None)
-        else:
-            ok.oscar_set_history_events(ev_b[timed_idx].ptr, ev_a[timed_idx].ptr)
-        ok.oscar_decode_step(dims, rot.struct, c, kn_all[s], vn_all[s], q_all[s], max_len, ws.buf,
-                             ws.nbytes, out, None, stream)
+            one_step(s)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            marks[i].record(stream)
+            ok.oscar_set_history_events(ev_b[i].ptr, ev_a[i].ptr)
+            one_step(warmup + i)
+        marks[steps].record(stream)
+        marks[steps].synchronize()
+        torch.cuda.synchronize()
+        ok.oscar_set_history_events(None, None)
+        step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]
+        hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(steps)]
+        return step_us, hist_us
 
-    for s in range(warmup):
-        step(s, None)
-    torch.cuda.synchronize()
+    def int2_step(s: int):
+        t = s // n_layers
+        ok.oscar_decode_step(dims, rot.struct, structs[s % n_layers][t], kn_all[t], vn_all[t], q_all[s], max_len,
+                             ws.buf, ws.nbytes, out, None, stream)
+
     print(f"[bench] {w.name}: B={B} Hq={hq} Hkv={hkv} G={w.group_size} L0={int(layout.lens.min())}.."
-          f"{int(layout.lens.max())} splits={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
+          f"{int(layout.lens.max())} layers={n_layers} slots={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
           file=sys.stderr, flush=True)
-    start, end = HipEvent(), HipEvent()
-    start.record(stream)
-    for i in range(steps):
-        step(warmup + i, i)
-    end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    ok.oscar_set_history_events(None, None)
-    step_ms = start.elapsed_ms(end) / steps
-    k3_ms = [ev_b[i].elapsed_ms(ev_a[i]) for i in range(steps)]
+    step_us, k3_us = timed_run(int2_step)
+    step_ms = sum(step_us) / steps / 1e3
 
     kname = "mfma" if ok.oscar_history_kernel_for(dims) == 2 else "valu"
     # the timed launch: history splits, plus the bf16 sink/recent chunks when
     # the matrix-core kernel runs them in the same launch
     launch_tot = 0
     step_tot = 0
+    unique_tot = 0
     for i in range(steps):
-        lens_i = lens_all[warmup + i]
+        lens_i = lens_step[warmup + i]
         hb, sb = step_bytes(lens_i, hkv, hq, w.group_size)
         launch_tot += hb + (bf16_bytes(lens_i, hkv) if kname == "mfma" else 0)
         step_tot += sb
-    k3_gbs = launch_tot / (sum(k3_ms) * 1e-3) / 1e9
-    value = step_tot / (step_ms * 1e-3 * steps) / 1e9
+        shared_tok = PAGE * (sum(layout.shared_pages) - layout.chain_len) if layout.chain_len else 0
+        unique_tot += sb - shared_tok * hkv * hist_unit_bytes(w.group_size)
+    k3_gbs = launch_tot / (sum(k3_us) * 1e-6) / 1e9
+    value = step_tot / (sum(step_us) * 1e-6) / 1e9
     traffic = load_traffic(args.workload, kname)
 
-    copy_gbs = None
-    if args.copy_probe:
-        nb = 2 << 30
-        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        c0, c1 = HipEvent(), HipEvent()
-        c0.record(stream)
-        dst.copy_(src)
-        c1.record(stream)
-        c1.synchronize()
-        copy_gbs = round(2 * nb / (c0.elapsed_ms(c1) * 1e-3) / 1e9, 1)
-        del src, dst
+    # bandwidth reference: one 2 GiB device copy
+    nb = 2 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = HipEvent(), HipEvent()
+    c0.record(stream)
+    dst.copy_(src)
+    c1.record(stream)
+    c1.synchronize()
+    copy_gbs = round(2 * nb / (c0.elapsed_ms(c1) * 1e-3) / 1e9, 1)
+    del src, dst
+
+    base = None
+    if args.bf16_baseline == "on" or (args.bf16_baseline == "auto" and args.workload.startswith("b32-100k")):
+        base = bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len,
+                             timed_run, n_layers, stream, dims, hkv, hq)
+        if base is not None:
+            base["int2_step_speedup"] = round(base["us_per_step"] / (step_ms * 1e3), 3)
+            base["int2_history_speedup"] = round(base["history_us"] / (sum(k3_us) / steps), 3)
+            base["byte_ratio"] = round(base["bytes_per_step"] / (step_tot / steps), 3)
 
     cpu = None
     if not args.no_cpu_baseline:
         hosted = {"r_k32": r_k.cpu().numpy(), "r_v32": r_v.cpu().numpy(),
                   "clip_k": c_k.cpu().numpy(), "clip_v": c_v.cpu().numpy()}
-        cpu = cpu_baseline(model, layout, hosted, lens_all[-1], min(args.cpu_heads, hkv))
+        cpu = cpu_baseline(model, layout, hosted, lens_step[-1], min(args.cpu_heads, hkv))
 
     res = {
         "metric": METRIC,
@@ -285,6 +318,8 @@ def main() -> int:
         "warmup": warmup,
         "ms_per_step": round(step_ms, 4),
         "us_per_step": round(step_ms * 1e3, 2),
+        "step_us_p50": pct(step_us, 50),
+        "step_us_p99": pct(step_us, 99),
         "pct_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -293,21 +328,60 @@ def main() -> int:
         "data": "synthetic (seeded generator; library-calibrated rotations)",
         "config": {"workload": w.name, "batch": B, "context": int(layout.lens.max()),
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
-                   "group_size": w.group_size, "page_size": 64, "history_splits": ws.splits,
-                   "history_kernel": kname, "parallelism": "single GPU"},
+                   "group_size": w.group_size, "page_size": 64, "history_split_slots": ws.splits,
+                   "layer_caches": n_layers, "history_kernel": kname, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(k3_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(k3_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": f"history ({kname})" + (" + bf16 sink/recent" if kname == "mfma" else ""),
-                     "avg_us": round(1e3 * sum(k3_ms) / steps, 2),
+                     "avg_us": round(sum(k3_us) / steps, 2),
                      "bytes_per_launch": int(launch_tot / steps),
+                     "frac_of_copy": round(k3_gbs / copy_gbs, 4),
                      "unit_bytes": {"history_token_head": hist_unit_bytes(w.group_size),
                                     "bf16_token_head": 512}},
-        "cpu_baseline": cpu,
         "copy_gbs": copy_gbs,
+        "cpu_baseline": cpu,
+        "bf16_baseline": base,
         "calibration_s": round(calib_s, 2),
     }
+    if layout.chain_len:
+        res["unique_value"] = round(unique_tot / (sum(step_us) * 1e-6) / 1e9, 2)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len, timed_run,
+                  n_layers, stream, dims, hkv, hq):
+    """The same steps on an all-bf16 cache (oscar_bf16_append + oscar_bf16_decode)."""
+    if n_layers != 1:
+        return None
+    t0 = time.perf_counter()
+    bcache = W.build_bf16_cache(w, layout, extra_tokens=appends)
+    fill_s = time.perf_counter() - t0
+    seq_dev = torch.from_numpy(lens_t.astype(np.int32)).cuda()
+    structs = [ok.make_bf16_cache(bcache.pages, bcache.n_pages, bcache.page_table, bcache.max_pages_per_req,
+                                  seq_dev[t].data_ptr(), w.batch) for t in range(appends)]
+    nb = ok.oscar_bf16_decode_workspace_bytes(dims, w.batch)
+    wsb = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, hq, 128), dtype=torch.float32, device="cuda")
+
+    def one(s: int):
+        ok.oscar_bf16_append(dims, structs[s], kn_all[s], vn_all[s], stream)
+        ok.oscar_bf16_decode(dims, structs[s], q_all[s], max_len, wsb, nb, out, None, stream)
+
+    step_us, hist_us = timed_run(one)
+    steps = len(step_us)
+    warm = len(lens_t) - steps
+    hist_b = [int(lens_t[warm + i].sum()) * hkv * 512 for i in range(steps)]
+    step_b = [hb + w.batch * hq * 128 * (2 + 4) + w.batch * hkv * 512 for hb in hist_b]
+    del bcache, wsb
+    torch.cuda.empty_cache()
+    h_gbs = sum(hist_b) / (sum(hist_us) * 1e-6) / 1e9
+    return {"us_per_step": round(sum(step_us) / steps, 2), "step_us_p50": pct(step_us, 50),
+            "value": round(sum(step_b) / (sum(step_us) * 1e-6) / 1e9, 2), "unit": "GB/s",
+            "history_us": round(sum(hist_us) / steps, 2), "history_gbs": round(h_gbs, 1),
+            "history_frac": round(h_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": int(sum(step_b) / steps),
+            "fill_s": round(fill_s, 1),
+            "what": "oscar_bf16_append + oscar_bf16_decode over the same tokens, all in bf16 pages"}
 
 
 if __name__ == "__main__":

@@ -51,6 +51,12 @@ class OscarCache(ctypes.Structure):
                 ("seq_lens", ctypes.c_void_p), ("batch", ctypes.c_int32)]
 
 
+class OscarBf16Cache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("page_table", ctypes.c_void_p), ("max_pages_per_req", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("batch", ctypes.c_int32)]
+
+
 # (name, restype, argtypes) of every exported function
 _P = ctypes.POINTER
 _SIGS = [
@@ -86,6 +92,15 @@ _SIGS = [
                                                    ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int32, ctypes.c_void_p]),
     ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
+    ("oscar_bf16_block_bytes", ctypes.c_size_t, []),
+    ("oscar_bf16_fill", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_bf16_append", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_bf16_decode_workspace_bytes", ctypes.c_size_t, [_P(OscarDims), ctypes.c_int32]),
+    ("oscar_bf16_decode", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]),
     ("oscar_set_history_target", ctypes.c_int, [ctypes.c_int32]),
     ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims)]),
     ("oscar_set_history_events", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
@@ -156,6 +171,13 @@ def make_cache(pages, n_pages: int, sink_k, sink_v, recent_k, recent_v, page_tab
     c = OscarCache(_ptr(pages), n_pages, _ptr(sink_k), _ptr(sink_v), _ptr(recent_k),
                    _ptr(recent_v), _ptr(page_table), max_pages_per_req, _ptr(seq_lens), batch)
     c._keep = (pages, sink_k, sink_v, recent_k, recent_v, page_table, seq_lens)
+    return c
+
+
+def make_bf16_cache(pages, n_pages: int, page_table, max_pages_per_req: int, seq_lens,
+                    batch: int) -> OscarBf16Cache:
+    c = OscarBf16Cache(_ptr(pages), n_pages, _ptr(page_table), max_pages_per_req, _ptr(seq_lens), batch)
+    c._keep = (pages, page_table, seq_lens)
     return c
 
 
@@ -250,6 +272,32 @@ def oscar_read_history_schedule(dims, batch: int, workspace, workspace_bytes: in
     if n < 0:
         _check(-n)
     return splits[:n].copy(), reqs
+
+
+def oscar_bf16_block_bytes() -> int:
+    return lib().oscar_bf16_block_bytes()
+
+
+def oscar_bf16_fill(dims, cache, request: int, pos_begin: int, n_tokens: int, k_tokens, v_tokens,
+                    stream=None) -> None:
+    _check(lib().oscar_bf16_fill(ctypes.byref(dims), ctypes.byref(cache), request, pos_begin, n_tokens,
+                                 _ptr(k_tokens), _ptr(v_tokens), _stream(stream)))
+
+
+def oscar_bf16_append(dims, cache, k_new, v_new, stream=None) -> None:
+    _check(lib().oscar_bf16_append(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+                                   _stream(stream)))
+
+
+def oscar_bf16_decode_workspace_bytes(dims, batch: int) -> int:
+    return lib().oscar_bf16_decode_workspace_bytes(ctypes.byref(dims), batch)
+
+
+def oscar_bf16_decode(dims, cache, q, max_seq_len: int, workspace, workspace_bytes: int, out,
+                      lse_out=None, stream=None) -> None:
+    _check(lib().oscar_bf16_decode(ctypes.byref(dims), ctypes.byref(cache), _ptr(q), max_seq_len,
+                                   _ptr(workspace), workspace_bytes, _ptr(out), _ptr(lse_out),
+                                   _stream(stream)))
 
 
 def oscar_set_history_kernel(kind: int) -> int:

@@ -72,6 +72,18 @@ int check_cache(const oscar_cache* c, bool need_pages) {
   return OSCAR_OK;
 }
 
+int check_bf16_cache(const oscar_bf16_cache* c) {
+  if (c == nullptr) return fail(OSCAR_EINVAL, "cache is NULL");
+  if (c->batch < 0) return fail(OSCAR_EINVAL, "batch %d < 0", c->batch);
+  if (c->batch == 0) return OSCAR_OK;
+  if (!c->pages || !c->page_table || !c->seq_lens)
+    return fail(OSCAR_EINVAL, "bf16 cache has a NULL pages/page_table/seq_lens pointer");
+  if (c->max_pages_per_req <= 0 || c->n_pages <= 0)
+    return fail(OSCAR_EINVAL, "max_pages_per_req %d / n_pages %lld must be positive", c->max_pages_per_req,
+                static_cast<long long>(c->n_pages));
+  return OSCAR_OK;
+}
+
 int pages_for(int32_t max_seq_len) {
   const int n_hist = max_seq_len > kBf16Tokens ? max_seq_len - kBf16Tokens : 0;
   return (n_hist + kPage - 1) / kPage;
@@ -364,6 +376,73 @@ int oscar_read_history_schedule(const oscar_dims* dims, int32_t batch, const voi
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return -hip_fail(e, "schedule read");
   return n;
+}
+
+size_t oscar_bf16_block_bytes(void) { return 2u * kPage * kDim * sizeof(uint16_t); }
+
+int oscar_bf16_fill(const oscar_dims* dims, const oscar_bf16_cache* cache, int32_t request,
+                    int32_t pos_begin, int32_t n_tokens, const uint16_t* k_tokens,
+                    const uint16_t* v_tokens, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_bf16_cache(cache))) return rc;
+  if (request < 0 || request >= cache->batch)
+    return fail(OSCAR_EINVAL, "request %d outside batch %d", request, cache->batch);
+  if (pos_begin < 0 || n_tokens < 0) return fail(OSCAR_EINVAL, "pos_begin %d / n_tokens %d must be >= 0", pos_begin, n_tokens);
+  if (n_tokens == 0) return OSCAR_OK;
+  if (k_tokens == nullptr || v_tokens == nullptr) return fail(OSCAR_EINVAL, "token pointers are NULL");
+  const int64_t last_page = (static_cast<int64_t>(pos_begin) + n_tokens - 1) / kPage;
+  if (last_page >= cache->max_pages_per_req)
+    return fail(OSCAR_EINVAL, "position %lld beyond max_pages_per_req %d",
+                static_cast<long long>(pos_begin) + n_tokens - 1, cache->max_pages_per_req);
+  const hipError_t e = launch_base_fill(*dims, *cache, request, pos_begin, n_tokens, k_tokens, v_tokens,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bf16 fill launch");
+  return OSCAR_OK;
+}
+
+int oscar_bf16_append(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* k_new,
+                      const uint16_t* v_new, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_bf16_cache(cache))) return rc;
+  if (cache->batch == 0) return OSCAR_OK;
+  if (k_new == nullptr || v_new == nullptr) return fail(OSCAR_EINVAL, "k_new or v_new is NULL");
+  const hipError_t e = launch_base_append(*dims, *cache, k_new, v_new, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bf16 append launch");
+  return OSCAR_OK;
+}
+
+size_t oscar_bf16_decode_workspace_bytes(const oscar_dims* dims, int32_t batch) {
+  if (check_dims(dims) || batch < 0) return 0;
+  return base_layout(*dims, batch, g_hist_target.load()).total;
+}
+
+int oscar_bf16_decode(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
+                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse_out, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_bf16_cache(cache))) return rc;
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (cache->batch == 0) return OSCAR_OK;
+  if (q == nullptr || workspace == nullptr || out == nullptr) return fail(OSCAR_EINVAL, "q, workspace or out is NULL");
+  if ((max_seq_len + kPage - 1) / kPage > cache->max_pages_per_req)
+    return fail(OSCAR_EINVAL, "max_seq_len %d needs %d pages > max_pages_per_req %d", max_seq_len,
+                (max_seq_len + kPage - 1) / kPage, cache->max_pages_per_req);
+  const BaseLayout lay = base_layout(*dims, cache->batch, g_hist_target.load());
+  if (workspace_bytes < lay.total)
+    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (g_ev_before != nullptr && g_ev_after != nullptr) {
+    ev0 = static_cast<hipEvent_t>(g_ev_before);
+    ev1 = static_cast<hipEvent_t>(g_ev_after);
+  }
+  const hipError_t e = launch_base_decode(*dims, *cache, q, static_cast<uint8_t*>(workspace), lay, out, lse_out,
+                                          static_cast<hipStream_t>(stream), ev0, ev1);
+  if (e != hipSuccess) return hip_fail(e, "bf16 decode launch");
+  return OSCAR_OK;
 }
 
 }  // extern "C"

@@ -107,6 +107,25 @@ hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t 
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,
                         hipStream_t s);
 
+// ---- all-bf16 baseline (baseline_bf16.hip)
+struct BaseLayout {
+  int32_t target = 1;
+  int32_t slots = 1;
+  size_t off_sched = 0;   // int32 [1 + 3 cap]
+  size_t off_req = 0;     // int32 [B][2]
+  size_t off_ho = 0;      // float [cap][Hq][128]
+  size_t off_hlse = 0;    // float [cap][Hq]
+  size_t total = 0;
+};
+BaseLayout base_layout(const oscar_dims& d, int32_t batch, int target_wg);
+hipError_t launch_base_decode(const oscar_dims& d, const oscar_bf16_cache& c, const uint16_t* q, uint8_t* ws,
+                              const BaseLayout& lay, float* out, float* lse_out, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1);
+hipError_t launch_base_fill(const oscar_dims& d, const oscar_bf16_cache& c, int32_t request, int32_t pos_begin,
+                            int32_t n_tokens, const uint16_t* k_tokens, const uint16_t* v_tokens, hipStream_t s);
+hipError_t launch_base_append(const oscar_dims& d, const oscar_bf16_cache& c, const uint16_t* k_new,
+                              const uint16_t* v_new, hipStream_t s);
+
 size_t calibrate_workspace_bytes(const oscar_dims& d, int32_t n_tokens);
 int32_t calibrate_max_tokens();
 hipError_t run_calibration(const oscar_dims& d, int32_t n, const float* q, const float* k,

@@ -53,6 +53,34 @@ class PagedKVCache:
         return self._struct
 
 
+class Bf16PagedCache:
+    """The all-bf16 baseline cache (``oscar_bf16_cache`` in include/oscar.h):
+      pages      bf16  [n_pages][Hkv][2][64][128]  (keys, then values, of 64 positions)
+      page_table int32 [B][max_pages_per_req]      (position p -> page p // 64, row p % 64)
+      seq_lens   int32 [B]
+    """
+
+    def __init__(self, num_q_heads: int, num_kv_heads: int, batch: int, max_pages_per_req: int,
+                 n_pages: int, device: str = "cuda"):
+        self.dims = _lib.make_dims(num_q_heads, num_kv_heads, 128)
+        self.batch = batch
+        self.num_q_heads = num_q_heads
+        self.num_kv_heads = num_kv_heads
+        self.max_pages_per_req = max_pages_per_req
+        self.n_pages = n_pages
+        self.pages = torch.zeros((max(n_pages, 1), num_kv_heads, 2, _lib.PAGE, _lib.HEAD_DIM),
+                                 dtype=torch.bfloat16, device=device)
+        self.page_table = torch.zeros((batch, max(max_pages_per_req, 1)), dtype=torch.int32, device=device)
+        self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self._struct = None
+
+    def struct(self) -> _lib.OscarBf16Cache:
+        if self._struct is None:
+            self._struct = _lib.make_bf16_cache(self.pages, self.n_pages, self.page_table,
+                                                self.max_pages_per_req, self.seq_lens, self.batch)
+        return self._struct
+
+
 class Rotation:
     """Float32 device copies of R_K, R_V [Hkv][128][128] and clips [Hkv][128]."""
 

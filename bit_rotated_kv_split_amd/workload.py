@@ -167,3 +167,45 @@ def build_cache(w: configs.Workload, layout: Layout, model: SyntheticModel, rot:
         fill_hist(b, _lib.PAGE * layout.shared_pages[b], n_h)
     torch.cuda.current_stream().synchronize()
     return cache
+
+
+def build_bf16_cache(w: configs.Workload, layout: Layout, device: str = "cuda", chunk_tokens: int = 16384,
+                     extra_tokens: int = 0):
+    """The all-bf16 baseline cache holding the same tokens as build_cache
+    (every position of every request in bf16 pages, filled from the GPU
+    generator through oscar_bf16_fill).  Pages are a seeded permutation."""
+    from .kvcache import Bf16PagedCache
+    B, hkv = w.batch, w.num_kv_heads
+    lens = layout.lens
+    need = [-(-(int(L) + extra_tokens) // _lib.PAGE) for L in lens]
+    total = max(sum(need), 1)
+    ids = gen.permutation(w.seed + 7, total) if w.paged else np.arange(total, dtype=np.int32)
+    max_pages = max(max(need), 1)
+    pt = np.zeros((B, max_pages), dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        pt[b, :need[b]] = ids[nxt:nxt + need[b]]
+        nxt += need[b]
+    cache = Bf16PagedCache(w.num_q_heads, hkv, B, max_pages, total, device)
+    cache.page_table.copy_(torch.from_numpy(pt))
+    cache.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    model = SyntheticModel(w)
+    ks = torch.from_numpy(model.k_scale).to(device)
+    vs = torch.from_numpy(model.v_scale).to(device)
+    stream = torch.cuda.current_stream().cuda_stream
+    stage_k = torch.empty((chunk_tokens, hkv, 128), dtype=torch.bfloat16, device=device)
+    stage_v = torch.empty_like(stage_k)
+    cs = cache.struct()
+    for b in range(B):
+        L = int(lens[b])
+        p = 0
+        while p < L:
+            n = min(chunk_tokens, L - p)
+            for dst, which, scale in ((stage_k, "k", ks), (stage_v, "v", vs)):
+                for src, p0, m in layout.src_ranges(b, p, n):
+                    synth_gpu.fill_kv(dst.data_ptr() + 2 * (p0 - p) * hkv * 128, m, hkv, hkv * 128, 128,
+                                      w.seed, which, src, p0, scale, stream)
+            _lib.oscar_bf16_fill(cache.dims, cs, b, p, n, stage_k, stage_v, stream)
+            p += n
+    torch.cuda.current_stream().synchronize()
+    return cache

@@ -260,6 +260,48 @@ int oscar_read_history_schedule(const oscar_dims* dims, int32_t batch, const voi
                                 size_t workspace_bytes, int32_t* splits, int32_t* requests,
                                 int32_t capacity, void* stream);
 
+/* ---- All-bf16 KV-cache baseline -----------------------------------------
+ * The cache the pages compare OSCAR against (first page, section "结果";
+ * second page, section "OSCAR的另一个关键点是"): every token of a request in
+ * bf16, unrotated.  Page block of one (page, KV head): keys [64][128] then
+ * values [64][128], bf16 (oscar_bf16_block_bytes() = 32768); pages[n_pages]
+ * [Hkv][block].  page_table[B][max_pages_per_req] maps position p to page
+ * p/64, row p%64.  Same ownership and error conventions as the INT2 calls. */
+typedef struct oscar_bf16_cache {
+  uint16_t* pages;
+  int64_t n_pages;
+  const int32_t* page_table;
+  int32_t max_pages_per_req;
+  const int32_t* seq_lens;   /* device [B]: L including the current token */
+  int32_t batch;
+} oscar_bf16_cache;
+
+size_t oscar_bf16_block_bytes(void);
+
+/* Copy tokens [pos_begin, pos_begin + n_tokens) of one request (k_tokens,
+ * v_tokens: device bf16 [n_tokens][Hkv][128]) into its pages. */
+int oscar_bf16_fill(const oscar_dims* dims, const oscar_bf16_cache* cache, int32_t request,
+                    int32_t pos_begin, int32_t n_tokens, const uint16_t* k_tokens,
+                    const uint16_t* v_tokens, void* stream);
+
+/* One step's append: token L_b - 1 of every request from k_new, v_new
+ * (device bf16 [B][Hkv][128]); seq_lens already count it. */
+int oscar_bf16_append(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* k_new,
+                      const uint16_t* v_new, void* stream);
+
+/* Device workspace bytes of oscar_bf16_decode (256-byte aligned). */
+size_t oscar_bf16_decode_workspace_bytes(const oscar_dims* dims, int32_t batch);
+
+/* Decode attention over the bf16 cache: q bf16 [B][Hq][128] -> out float32
+ * [B][Hq][128], lse_out float32 [B][Hq] (natural log) or NULL.  One softmax
+ * over all L tokens with scale 1/sqrt(128).  Split-K over pages with the
+ * same schedule rule as oscar_decode_attn (no tokens skipped), then a merge;
+ * three launches.  The oscar_set_history_events hook times the split-K
+ * launch. */
+int oscar_bf16_decode(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
+                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse_out, void* stream);
+
 /* Thread-local text of the last error ("" if none). */
 const char* oscar_last_error(void);
 

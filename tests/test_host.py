@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "oscar.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -160,3 +160,27 @@ def test_last_error_is_thread_local():
     t.start()
     t.join()
     assert seen == [""] and "head_dim" in ok.oscar_last_error()
+
+
+def test_bf16_baseline_host_checks():
+    d = ok.make_dims(32, 8, 128)
+    assert ok.oscar_bf16_block_bytes() == 2 * 64 * 128 * 2
+    assert ok.oscar_bf16_decode_workspace_bytes(d, 32) >= (1024 + 32) * 32 * 129 * 4
+    fake = 0x1000
+    c = ok.make_bf16_cache(fake, 10, fake, 4, fake, 2)
+    with pytest.raises(ok.OscarError) as e:   # 300 positions need 5 pages > 4
+        ok.oscar_bf16_decode(d, c, fake, 300, fake, 1 << 30, fake, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "max_pages_per_req" in ok.oscar_last_error()
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_bf16_decode(d, c, fake, 100, fake, 16, fake, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "workspace" in ok.oscar_last_error()
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_bf16_fill(d, c, 2, 0, 10, fake, fake, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "request" in ok.oscar_last_error()
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_bf16_fill(d, c, 0, 250, 10, fake, fake, 0)
+    assert e.value.code == ok.OSCAR_EINVAL
+    with pytest.raises(ok.OscarError):
+        ok.oscar_bf16_append(d, c, None, fake, 0)
+    empty = ok.make_bf16_cache(fake, 10, fake, 4, fake, 0)
+    ok.oscar_bf16_decode(d, empty, None, 100, None, 0, None, None, 0)
