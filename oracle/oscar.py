@@ -270,12 +270,132 @@ def dequantize(codes: np.ndarray, s: np.ndarray, z: np.ndarray, group: int) -> n
     return out.astype(np.float32).reshape(n, HEAD_DIM)
 
 
-def demote(x_bits: np.ndarray, r32: np.ndarray, clip32: np.ndarray, group: int):
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebook variant.  [B] (the paragraph comparing OSCAR with
+# TurboQuant) says only that OSCAR's code repository pairs the
+# attention-aware rotation with a Lloyd-Max codebook.
+# READING: the codebook is the 4-level Lloyd-Max (minimum mean-squared
+# error) quantizer of the standard normal distribution, applied to each
+# group after normalising it by its mean and standard deviation, which take
+# the places of the uniform quantizer's zero point and scale: zero = mean,
+# scale = population standard deviation, both computed in float64, rounded
+# to float32 and then to bfloat16.  u = (y - zero) / scale in IEEE float32;
+# the code is the number of float32 decision thresholds strictly below u
+# (the nearest level, ties to the lower one); a group with scale 0 gets code
+# 0.  The stored codebook is the float32 levels; a value decodes to
+# zero + scale * level[code].  The decision thresholds are the float64
+# midpoints of adjacent float64 levels, rounded to float32.
+# ---------------------------------------------------------------------------
+
+def _normal_pdf(x: float) -> float:
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _normal_tail(x: float) -> float:
+    """P(X > x) for X ~ N(0, 1), x >= 0 (inf gives 0)."""
+    return 0.0 if x == math.inf else 0.5 * math.erfc(x / math.sqrt(2.0))
+
+
+def lloyd_max_gaussian(n_levels: int = LEVELS, max_iter: int = 100000):
+    """Lloyd-Max quantizer of N(0, 1) with an even number of levels.
+
+    Lloyd's alternation on the positive half (the density is symmetric, and
+    so is the optimum): the thresholds are the midpoints of adjacent levels,
+    and each level is the mean of N(0, 1) restricted to its cell, which on
+    (a, b) is (pdf(a) - pdf(b)) / P(a < X < b).  Starts from levels
+    1/2, 3/2, ... and stops once an iteration moves no level by more than
+    1e-15 (float64 resolution; about 60 iterations for four levels), then
+    takes one more.  Returns float64 (levels ascending [n], thresholds [n - 1]).
+    """
+    if n_levels % 2 or n_levels < 2:
+        raise ValueError("n_levels must be even and >= 2")
+    half = n_levels // 2
+    lev = [k + 0.5 for k in range(half)]
+    extra = 1
+    for _ in range(max_iter):
+        edges = [0.0] + [(lev[k] + lev[k + 1]) / 2 for k in range(half - 1)] + [math.inf]
+        new = []
+        for a, b in zip(edges[:-1], edges[1:]):
+            pdf_b = 0.0 if b == math.inf else _normal_pdf(b)
+            new.append((_normal_pdf(a) - pdf_b) / (_normal_tail(a) - _normal_tail(b)))
+        settled = max(abs(x - y) for x, y in zip(new, lev)) <= 1e-15
+        lev = new
+        if settled:
+            if extra == 0:
+                break
+            extra -= 1
+    levels = np.array([-x for x in reversed(lev)] + lev, dtype=np.float64)
+    thresholds = (levels[:-1] + levels[1:]) / 2
+    return levels, thresholds
+
+
+def lloyd_max_codebook():
+    """The stored codebook: float32 levels [4] and float32 thresholds [3]."""
+    lev, thr = lloyd_max_gaussian(LEVELS)
+    return lev.astype(np.float32), thr.astype(np.float32)
+
+
+def quantize_groups_lloyd(y: np.ndarray, group: int):
+    """Lloyd-Max codebook quantization per token and group (READING above).
+
+    Returns codes uint8 [n][128] and scale (standard deviation), zero (mean)
+    as float32 [n][128/group], both bfloat16 values.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    n = y.shape[0]
+    ng = HEAD_DIM // group
+    yg = y.reshape(n, ng, group)
+    y64 = yg.astype(np.float64)
+    mean = y64.sum(axis=2) / group
+    var = ((y64 - mean[:, :, None]) ** 2).sum(axis=2) / group
+    z = bf16_round(mean.astype(np.float32))
+    s = bf16_round(np.sqrt(var).astype(np.float32))
+    _, thr = lloyd_max_codebook()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = ((yg - z[:, :, None]).astype(np.float32) / s[:, :, None]).astype(np.float32)
+    codes = sum((u > t).astype(np.int64) for t in thr)
+    codes = np.where(s[:, :, None] == 0, 0, codes)
+    return codes.astype(np.uint8).reshape(n, HEAD_DIM), s, z
+
+
+def dequantize_lloyd(codes: np.ndarray, s: np.ndarray, z: np.ndarray, group: int) -> np.ndarray:
+    """y_hat = zero + scale * level[code] with the float32 levels, in float64."""
+    lev, _ = lloyd_max_codebook()
+    n = codes.shape[0]
+    ng = HEAD_DIM // group
+    lv = lev.astype(np.float64)[codes.reshape(n, ng, group)]
+    out = z[:, :, None].astype(np.float64) + s[:, :, None].astype(np.float64) * lv
+    return out.reshape(n, HEAD_DIM)
+
+
+CODEBOOKS = ("uniform", "lloyd-max")
+
+
+def quantize(y: np.ndarray, group: int, codebook: str = "uniform"):
+    """Dispatch on the codebook: "uniform" (min/max, the pages' INT2) or
+    "lloyd-max" (the variant above)."""
+    if codebook == "uniform":
+        return quantize_groups(y, group)
+    if codebook == "lloyd-max":
+        return quantize_groups_lloyd(y, group)
+    raise ValueError(codebook)
+
+
+def dequantize_any(codes, s, z, group: int, codebook: str = "uniform") -> np.ndarray:
+    """Dequantized history in the stored domain for either codebook."""
+    if codebook == "uniform":
+        return dequantize(codes, s, z, group)
+    if codebook == "lloyd-max":
+        return dequantize_lloyd(codes, s, z, group)
+    raise ValueError(codebook)
+
+
+def demote(x_bits: np.ndarray, r32: np.ndarray, clip32: np.ndarray, group: int, codebook: str = "uniform"):
     """Rotate, clip and quantize bf16 tokens [n][128] (bit patterns) of one
     KV head: the per-token work of the fused demotion kernel
     ([B] §OSCAR的另一个关键点是).  Returns (codes, scale, zero)."""
     x = bf16_value(x_bits)
-    return quantize_groups(clip(rotate(x, r32), clip32), group)
+    return quantize(clip(rotate(x, r32), clip32), group, codebook)
 
 
 # ---------------------------------------------------------------------------
@@ -380,15 +500,15 @@ def regions(L: int):
 
 
 def quantized_history(k_bits: np.ndarray, v_bits: np.ndarray, r_k32, r_v32, clip_k, clip_v,
-                      group: int):
+                      group: int, codebook: str = "uniform"):
     """Demote every history token of one (request, KV head).
 
     ``k_bits``/``v_bits`` are the bf16 tokens at history positions
     64 .. L-257 ([n_hist][128]).  Each token is demoted on its own, so the
     result does not depend on the order in which tokens left the window.
     """
-    hk = demote(k_bits, r_k32, clip_k, group)
-    hv = demote(v_bits, r_v32, clip_v, group)
+    hk = demote(k_bits, r_k32, clip_k, group, codebook)
+    hv = demote(v_bits, r_v32, clip_v, group, codebook)
     return hk, hv
 
 
@@ -479,12 +599,13 @@ def history_memory_ratio(group: int, with_metadata: bool = True) -> float:
 
 def request_attention(q_bits: np.ndarray, k_tokens: np.ndarray, v_tokens: np.ndarray,
                       r_k32: np.ndarray, r_v32: np.ndarray, clip_k: np.ndarray,
-                      clip_v: np.ndarray, group: int):
+                      clip_v: np.ndarray, group: int, codebook: str = "uniform"):
     """Attention output of one request after its latest append and demotion.
 
     ``q_bits`` [Hq][128]; ``k_tokens``/``v_tokens`` [L][Hkv][128] bf16 bits
     of every token so far (position order); rotations [Hkv][128][128] and
-    clips [Hkv][128] float32.  Returns out [Hq][128] float64 and lse [Hq].
+    clips [Hkv][128] float32; ``codebook`` "uniform" or "lloyd-max".
+    Returns out [Hq][128] float64 and lse [Hq].
     """
     L, hkv = k_tokens.shape[0], k_tokens.shape[1]
     hq = q_bits.shape[0]
@@ -496,9 +617,9 @@ def request_attention(q_bits: np.ndarray, k_tokens: np.ndarray, v_tokens: np.nda
     for j in range(hkv):
         hist = slice(SINK, SINK + n_hist)
         (ck, sk, zk), (cv, sv, zv) = quantized_history(
-            k_tokens[hist, j], v_tokens[hist, j], r_k32[j], r_v32[j], clip_k[j], clip_v[j], group)
-        kh = dequantize(ck, sk, zk, group)
-        vh = dequantize(cv, sv, zv, group)
+            k_tokens[hist, j], v_tokens[hist, j], r_k32[j], r_v32[j], clip_k[j], clip_v[j], group, codebook)
+        kh = dequantize_any(ck, sk, zk, group, codebook)
+        vh = dequantize_any(cv, sv, zv, group, codebook)
         o, l = attend(q_bits[j * g:(j + 1) * g], k_tokens[bf16_pos, j], v_tokens[bf16_pos, j],
                       kh, vh, r_k32[j], r_v32[j])
         out[j * g:(j + 1) * g] = o

@@ -370,7 +370,19 @@ def test_logit_error_identity():
 
 
 # -------------------------------------------------------------------- P10
-def _brute_request(q_bits, k_bits, v_bits, rk, rv, ck, cv, group):
+def _brute_dequant(codes, s, z, group, codebook):
+    """One token's dequantized values, element by element."""
+    lev = O.lloyd_max_codebook()[0]
+    out = np.zeros(128)
+    for c in range(128):
+        gi = c // group
+        k = int(codes[0, c])
+        out[c] = (float(z[0, gi]) + float(s[0, gi]) * float(lev[k])) if codebook == "lloyd-max" \
+            else float(np.float32(np.float32(k) * s[0, gi] + z[0, gi]))
+    return out
+
+
+def _brute_request(q_bits, k_bits, v_bits, rk, rv, ck, cv, group, codebook="uniform"):
     """Two-pass softmax with explicit loops over tokens; history keys and values
     are rotated back to the model domain (k_hat R^T, v_hat R^T) instead of
     rotating the query and the output."""
@@ -380,10 +392,10 @@ def _brute_request(q_bits, k_bits, v_bits, rk, rv, ck, cv, group):
     keys, vals = [], []
     for t in range(L):
         if t in hist:
-            codes, s, z = O.demote(k_bits[t:t + 1], rk, ck, group)
-            keys.append(O.dequantize(codes, s, z, group)[0].astype(np.float64) @ rk.astype(np.float64).T)
-            codes, s, z = O.demote(v_bits[t:t + 1], rv, cv, group)
-            vals.append(O.dequantize(codes, s, z, group)[0].astype(np.float64) @ rv.astype(np.float64).T)
+            codes, s, z = O.demote(k_bits[t:t + 1], rk, ck, group, codebook)
+            keys.append(_brute_dequant(codes, s, z, group, codebook) @ rk.astype(np.float64).T)
+            codes, s, z = O.demote(v_bits[t:t + 1], rv, cv, group, codebook)
+            vals.append(_brute_dequant(codes, s, z, group, codebook) @ rv.astype(np.float64).T)
         elif t < n_s or t >= L - n_r:
             keys.append(O.bf16_value(k_bits[t]))
             vals.append(O.bf16_value(v_bits[t]))
@@ -400,8 +412,9 @@ def _brute_request(q_bits, k_bits, v_bits, rk, rv, ck, cv, group):
     return out, lse
 
 
-@pytest.mark.parametrize("L", [1, 40, 64, 65, 200, 320, 321, 333, 400])
-def test_request_attention_brute_force(L):
+@pytest.mark.parametrize("L,codebook", [(L, "uniform") for L in (1, 40, 64, 65, 200, 320, 321, 333, 400)]
+                         + [(L, "lloyd-max") for L in (321, 400)])
+def test_request_attention_brute_force(L, codebook):
     r = rng(100 + L)
     hq, hkv, group = 4, 2, 64
     k = gen.bf16_bits(r.standard_normal((L, hkv, 128)).astype(np.float32))
@@ -415,10 +428,11 @@ def test_request_attention_brute_force(L):
     rv = np.stack(rots[hkv:])
     ck = np.full((hkv, 128), 2.5, dtype=np.float32)
     cv = np.full((hkv, 128), 2.0, dtype=np.float32)
-    out, lse = O.request_attention(q, k, v, rk, rv, ck, cv, group)
+    out, lse = O.request_attention(q, k, v, rk, rv, ck, cv, group, codebook)
     g = hq // hkv
     for j in range(hkv):
-        bo, bl = _brute_request(q[j * g:(j + 1) * g], k[:, j], v[:, j], rk[j], rv[j], ck[j], cv[j], group)
+        bo, bl = _brute_request(q[j * g:(j + 1) * g], k[:, j], v[:, j], rk[j], rv[j], ck[j], cv[j], group,
+                                codebook)
         assert np.abs(out[j * g:(j + 1) * g] - bo).max() < 1e-11
         assert np.abs(lse[j * g:(j + 1) * g] - bl).max() < 1e-11
 
@@ -514,3 +528,130 @@ def test_plausible_mistakes_fail_a_pin():
     _, u = O.eig_descending(c)
     wrong = O.hadamard() @ u.T @ O.bit_reversal_matrix()
     assert np.abs(np.diag(wrong.T @ c @ wrong) - np.trace(c) / 128).max() > 1e-3 * np.trace(c)
+
+
+# ------------------------------------------------------------ Lloyd-Max codebook
+# Pins of the codebook variant against the textbook solution and its
+# optimality conditions (J. Max, "Quantizing for minimum distortion", IRE
+# Transactions on Information Theory IT-6, 1960, Table I for the normal
+# distribution, N = 4: output levels 0.4528 and 1.510, decision level
+# 0.9816, mean squared error 0.1175).
+
+def test_lloyd_max_matches_the_published_four_level_normal_quantizer():
+    lev, thr = O.lloyd_max_gaussian(4)
+    assert np.array_equal(lev, -lev[::-1]) and thr[1] == 0.0
+    assert abs(lev[2] - 0.4528) < 5e-5 and abs(lev[3] - 1.510) < 5e-4
+    assert abs(thr[2] - 0.9816) < 5e-5
+
+
+def _normal_cell_moments(a, b):
+    from scipy import integrate
+    pdf = lambda x: math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    m0 = integrate.quad(pdf, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+    m1 = integrate.quad(lambda x: x * pdf(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+    return m0, m1
+
+
+def _normal_mse(levels, thresholds):
+    from scipy import integrate
+    pdf = lambda x: math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    edges = [-math.inf] + list(thresholds) + [math.inf]
+    return sum(integrate.quad(lambda x, y=y: (x - y) ** 2 * pdf(x), a, b, epsabs=1e-14, epsrel=1e-12)[0]
+               for a, b, y in zip(edges[:-1], edges[1:], levels))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_lloyd_max_satisfies_centroid_and_nearest_neighbour_conditions(n):
+    """Each level is the mean of N(0,1) on its cell (quadrature, not the
+    closed form the oracle uses) and each threshold is equidistant from its
+    two levels; the two-level case is the closed form +-sqrt(2/pi)."""
+    lev, thr = O.lloyd_max_gaussian(n)
+    edges = [-math.inf] + list(thr) + [math.inf]
+    for a, b, y in zip(edges[:-1], edges[1:], lev):
+        m0, m1 = _normal_cell_moments(a, b)
+        assert abs(m1 / m0 - y) < 1e-9
+    assert np.allclose(thr, (lev[:-1] + lev[1:]) / 2, rtol=0, atol=1e-15)
+    if n == 2:
+        assert abs(lev[1] - math.sqrt(2 / math.pi)) < 1e-14
+
+
+def test_lloyd_max_is_a_local_minimum_of_the_distortion():
+    lev, thr = O.lloyd_max_gaussian(4)
+    d0 = _normal_mse(lev, thr)
+    assert abs(d0 - 0.1175) < 5e-5
+    # the best uniform 4-level quantizer of N(0,1) (step ~0.996) is worse
+    from scipy import optimize
+    uni = optimize.minimize_scalar(lambda d: _normal_mse(np.array([-1.5, -0.5, 0.5, 1.5]) * d,
+                                                         np.array([-1.0, 0.0, 1.0]) * d),
+                                   bounds=(0.5, 1.5), method="bounded")
+    assert uni.fun > d0 + 1e-3
+    for dl in (-1e-3, 1e-3):
+        for i in range(4):
+            l2 = lev.copy()
+            l2[i] += dl
+            assert _normal_mse(l2, thr) > d0
+        for i in (0, 2):
+            t2 = thr.copy()
+            t2[i] += dl
+            assert _normal_mse(lev, t2) > d0
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_lloyd_quantizer_statistics_brute_force_and_bound(group):
+    r = rng(40 + group)
+    n = 300
+    y = (r.standard_normal((n, 128)) * np.exp(r.standard_normal(128)) + r.standard_normal(128)).astype(np.float32)
+    codes, s, z = O.quantize_groups_lloyd(y, group)
+    ng = 128 // group
+    assert codes.dtype == np.uint8 and codes.max() <= 3
+    assert np.array_equal(O.bf16_round(s), s) and np.array_equal(O.bf16_round(z), z)
+    yg = y.reshape(n, ng, group)
+    import statistics
+    lev32, thr32 = O.lloyd_max_codebook()
+    for t in range(0, n, 7):
+        for gi in range(ng):
+            vals = [float(x) for x in yg[t, gi]]
+            # statistics computes the mean and population deviation exactly (rationals)
+            assert z[t, gi] == O.bf16_round(np.float32(statistics.fmean(vals)))
+            assert s[t, gi] == O.bf16_round(np.float32(statistics.pstdev(vals)))
+            for c in range(group):
+                u = float(np.float32(np.float32(yg[t, gi, c] - z[t, gi]) / s[t, gi]))
+                dist = [abs(u - float(l)) for l in lev32]
+                best = int(np.argmin(dist))
+                if min(abs(u - float(th)) for th in thr32) > 1e-6:
+                    assert codes[t, gi * group + c] == best
+    yhat = O.dequantize_lloyd(codes, s, z, group).reshape(n, ng, group)
+    # error bound: the largest half cell inside the outer levels, or the
+    # distance past the outer level
+    u = (yg - z[..., None]) / s[..., None]
+    inner = np.abs(u) <= lev32[3]
+    half_gap = max((lev32[1] - lev32[0]) / 2, (lev32[2] - lev32[1]) / 2)
+    err = np.abs(yhat - yg) / s[..., None]
+    assert (err[inner] <= half_gap + 1e-5).all()
+    assert np.allclose(err[~inner], np.abs(u[~inner]) - lev32[3], atol=1e-5)
+
+
+def test_lloyd_quantizer_mirror_constant_group_and_gaussian_distortion():
+    r = rng(44)
+    y = (r.standard_normal((200, 128)) * 3 + 1).astype(np.float32)
+    c1, s1, z1 = O.quantize_groups_lloyd(y, 64)
+    c2, s2, z2 = O.quantize_groups_lloyd(-y, 64)
+    assert np.array_equal(s1, s2) and np.array_equal(z1, -z2)
+    assert np.array_equal(c2, 3 - c1)
+    # constant group: scale 0, code 0, exact reconstruction of the bf16 value
+    yc = np.full((2, 128), 0.3, dtype=np.float32)
+    c, s, z = O.quantize_groups_lloyd(yc, 32)
+    assert (c == 0).all() and (s == 0).all()
+    assert np.array_equal(O.dequantize_lloyd(c, s, z, 32), np.broadcast_to(O.bf16_round(yc), yc.shape))
+    # Gaussian groups: relative distortion near the codebook's 0.1175, well
+    # under the min/max uniform quantizer's on the same data
+    g = r.standard_normal((4000, 128)).astype(np.float32)
+    c, s, z = O.quantize_groups_lloyd(g, 128)
+    yh = O.dequantize_lloyd(c, s, z, 128)
+    var = g.astype(np.float64).var(axis=1)
+    d_lm = (((yh - g) ** 2).mean(axis=1) / var).mean()
+    cu, su, zu = O.quantize_groups(g, 128)
+    yu = O.dequantize(cu, su, zu, 128).astype(np.float64)
+    d_u = (((yu - g) ** 2).mean(axis=1) / var).mean()
+    assert abs(d_lm - 0.1175) < 0.006
+    assert d_u > 1.5 * d_lm
