@@ -35,10 +35,13 @@ METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 100K ctx, batch 32"
 
 
 def workloads():
+    import dataclasses
     from synth import configs, gen
     return {
         "b32-100k-g128": lambda: configs.qwen3_8b_b32(128),
         "b32-100k-g64": lambda: configs.qwen3_8b_b32(64),
+        "b32-100k-g128-lloyd": lambda: dataclasses.replace(configs.qwen3_8b_b32(128),
+                                                           name="qwen3-8b-b32-100k-lloyd-max", codebook=1),
         "b1-100k": lambda: configs.qwen3_8b_b1(),
         "b16-128k": lambda: configs.qwen3_4b_b16(),
         "b32-ragged-gqa8": lambda: configs.qwen3_32b_ragged(
@@ -117,7 +120,8 @@ def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 
         q = model.queries(0, w.batch)[b][: n_heads * g]
         t0 = time.perf_counter()
         O.request_attention(q, host["k"], host["v"], cal_host["r_k32"][:n_heads], cal_host["r_v32"][:n_heads],
-                            cal_host["clip_k"][:n_heads], cal_host["clip_v"][:n_heads], w.group_size)
+                            cal_host["clip_k"][:n_heads], cal_host["clip_v"][:n_heads], w.group_size,
+                            ("uniform", "lloyd-max")[w.codebook])
         spent += time.perf_counter() - t0
         done_bytes += step_bytes(np.array([L]), n_heads, n_heads * g, w.group_size)[1]
         reqs += 1
@@ -183,7 +187,7 @@ def main() -> int:
     layout = W.Layout(w, None, extra_tokens=appends)
     model = W.SyntheticModel(w)
     B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
-    dims = ok.make_dims(hq, hkv, w.group_size)
+    dims = ok.make_dims(hq, hkv, w.group_size, codebook=w.codebook)
     stream = torch.cuda.current_stream().cuda_stream
 
     # offline calibration, by the library
@@ -295,7 +299,8 @@ def main() -> int:
     del src, dst
 
     base = None
-    if args.bf16_baseline == "on" or (args.bf16_baseline == "auto" and args.workload.startswith("b32-100k")):
+    if args.bf16_baseline == "on" or (args.bf16_baseline == "auto" and args.workload in ("b32-100k-g128",
+                                                                                       "b32-100k-g64")):
         base = bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len,
                              timed_run, n_layers, stream, dims, hkv, hq)
         if base is not None:
@@ -328,7 +333,8 @@ def main() -> int:
         "data": "synthetic (seeded generator; library-calibrated rotations)",
         "config": {"workload": w.name, "batch": B, "context": int(layout.lens.max()),
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
-                   "group_size": w.group_size, "page_size": 64, "history_split_slots": ws.splits,
+                   "group_size": w.group_size, "codebook": ("uniform", "lloyd-max")[w.codebook],
+                   "page_size": 64, "history_split_slots": ws.splits,
                    "layer_caches": n_layers, "history_kernel": kname, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(k3_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(k3_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,

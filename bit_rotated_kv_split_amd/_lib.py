@@ -19,6 +19,9 @@ OSCAR_EINVAL = 1
 OSCAR_EUNSUPPORTED = 2
 OSCAR_EHIP = 3
 
+CODEBOOK_UNIFORM = 0
+CODEBOOK_LLOYD_MAX = 1
+
 HEAD_DIM = 128
 PAGE = 64
 SINK = 64
@@ -35,7 +38,7 @@ class OscarDims(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("sink_len", ctypes.c_int32),
-                ("recent_len", ctypes.c_int32)]
+                ("recent_len", ctypes.c_int32), ("codebook", ctypes.c_int32)]
 
 
 class OscarRotation(ctypes.Structure):
@@ -61,6 +64,7 @@ class OscarBf16Cache(ctypes.Structure):
 _P = ctypes.POINTER
 _SIGS = [
     ("oscar_block_bytes", ctypes.c_size_t, [ctypes.c_int32]),
+    ("oscar_codebook", ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_kv_demote", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_kv_fill_history", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
@@ -156,8 +160,21 @@ def _check(rc: int) -> None:
 # ------------------------------------------------------------------ structs
 
 def make_dims(num_q_heads: int, num_kv_heads: int, group_size: int, head_dim: int = HEAD_DIM,
-              page_size: int = PAGE, sink_len: int = SINK, recent_len: int = RECENT) -> OscarDims:
-    return OscarDims(num_q_heads, num_kv_heads, head_dim, group_size, page_size, sink_len, recent_len)
+              page_size: int = PAGE, sink_len: int = SINK, recent_len: int = RECENT,
+              codebook: int = CODEBOOK_UNIFORM) -> OscarDims:
+    return OscarDims(num_q_heads, num_kv_heads, head_dim, group_size, page_size, sink_len, recent_len,
+                     codebook)
+
+
+def oscar_codebook(codebook: int):
+    """(levels float32 [4], thresholds float32 [3]) of a codebook, from the library."""
+    import numpy as np
+    lev = np.zeros(4, dtype=np.float32)
+    thr = np.zeros(3, dtype=np.float32)
+    rc = lib().oscar_codebook(codebook, lev.ctypes.data, thr.ctypes.data)
+    if rc != OSCAR_OK:
+        raise OscarError(rc, f"codebook {codebook}")
+    return lev, thr
 
 
 def make_rotation(r_k, r_v, clip_k, clip_v) -> OscarRotation:

@@ -47,6 +47,8 @@ int check_dims(const oscar_dims* d) {
     return fail(OSCAR_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads, d->num_kv_heads);
   const int g = d->num_q_heads / d->num_kv_heads;
   if (g > 8) return fail(OSCAR_EUNSUPPORTED, "query heads per KV head %d unsupported (<= 8)", g);
+  if (codebook_of(d->codebook) == nullptr)
+    return fail(OSCAR_EUNSUPPORTED, "codebook %d unsupported (0 uniform, 1 Lloyd-Max)", d->codebook);
   return OSCAR_OK;
 }
 
@@ -269,6 +271,10 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
     return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int kind = g_hist_kernel.load();
+  const bool use_mfma = kind == 2 || (kind == 0 && hist_mfma_supported(*dims));
+  if (kind == 2 && !hist_mfma_supported(*dims))
+    return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
   DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
   DemoteStep dm;
   if (demote) {
@@ -277,10 +283,6 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   }
   hipError_t e = launch_qrot(a, s);
   if (e != hipSuccess) return hip_fail(e, "query rotation launch");
-  const int kind = g_hist_kernel.load();
-  const bool use_mfma = kind == 2 || (kind == 0 && hist_mfma_supported(*dims));
-  if (kind == 2 && !hist_mfma_supported(*dims))
-    return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
   if (g_ev_before != nullptr && g_ev_after != nullptr) {
     a.ev_start = static_cast<hipEvent_t>(g_ev_before);
     a.ev_stop = static_cast<hipEvent_t>(g_ev_after);

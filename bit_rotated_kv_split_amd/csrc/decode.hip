@@ -151,12 +151,26 @@ struct HistParams {
   int32_t hkv;
   int32_t hq;
   const int32_t* sched;
+  float lev_lo, lev_hi;   // Lloyd-Max codebook: levels -hi, -lo, lo, hi
 };
+
+// Level of a 2-bit code: the code itself (uniform codebook) or the
+// Lloyd-Max level.
+template <bool LM>
+__device__ __forceinline__ float code_level(uint32_t c, float lo, float hi) {
+  if constexpr (LM) {
+    const float mag = (c == 0u || c == 3u) ? hi : lo;
+    return c >= 2u ? mag : -mag;
+  } else {
+    return static_cast<float>(c);
+  }
+}
 
 // Vector-ALU history kernel.  Workgroup = (scheduled split, KV head), four
 // waves; wave w takes pages p0+w, p0+w+4, ... of the split with its own
-// online-softmax state, and the four states are merged at the end.
-template <int GQ, int G>
+// online-softmax state, and the four states are merged at the end.  LM
+// selects the Lloyd-Max codebook (dequantized value zero + scale * level).
+template <int GQ, int G, bool LM>
 __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
   constexpr int NG = kDim / G;
   const int split = blockIdx.x, kvh = blockIdx.y;
@@ -208,7 +222,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
       const uint32_t w = words[d * 64 + qo];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float code = static_cast<float>((w >> (2 * i)) & 3u);
+        const float code = code_level<LM>((w >> (2 * i)) & 3u, a.lev_lo, a.lev_hi);
         const int ch = 16 * d + i;
 #pragma unroll
         for (int h = 0; h < GQ; ++h) dot[h][ch / G] = __builtin_fmaf(q_s[h][ch], code, dot[h][ch / G]);
@@ -267,7 +281,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
         const uint32_t w = words[512 + v_word_index(c, wq)];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float code = static_cast<float>((w >> (2 * i)) & 3u);
+          const float code = code_level<LM>((w >> (2 * i)) & 3u, a.lev_lo, a.lev_hi);
 #pragma unroll
           for (int h = 0; h < GQ; ++h)
             accv[h] = __builtin_fmaf(w_s[wave][h][gi][16 * wq + i], code, accv[h]);
@@ -592,12 +606,23 @@ struct HistValuRun {
     p.hkv = d.num_kv_heads;
     p.hq = d.num_q_heads;
     p.sched = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_sched);
+    const Codebook* cb = codebook_of(d.codebook);
+    p.lev_lo = cb->lev[2];
+    p.lev_hi = cb->lev[3];
     const dim3 grid(a.lay.slots, d.num_kv_heads);
     const bool timed = a.ev_start != nullptr && a.ev_stop != nullptr;
-    switch (d.group_size) {
-      case 32: launch(hist_valu_kernel<GQ, 32>, grid, timed, a, p, s); break;
-      case 64: launch(hist_valu_kernel<GQ, 64>, grid, timed, a, p, s); break;
-      default: launch(hist_valu_kernel<GQ, 128>, grid, timed, a, p, s); break;
+    if (d.codebook == OSCAR_CODEBOOK_LLOYD_MAX) {
+      switch (d.group_size) {
+        case 32: launch(hist_valu_kernel<GQ, 32, true>, grid, timed, a, p, s); break;
+        case 64: launch(hist_valu_kernel<GQ, 64, true>, grid, timed, a, p, s); break;
+        default: launch(hist_valu_kernel<GQ, 128, true>, grid, timed, a, p, s); break;
+      }
+    } else {
+      switch (d.group_size) {
+        case 32: launch(hist_valu_kernel<GQ, 32, false>, grid, timed, a, p, s); break;
+        case 64: launch(hist_valu_kernel<GQ, 64, false>, grid, timed, a, p, s); break;
+        default: launch(hist_valu_kernel<GQ, 128, false>, grid, timed, a, p, s); break;
+      }
     }
     return hipGetLastError();
   }

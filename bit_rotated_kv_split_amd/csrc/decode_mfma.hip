@@ -542,7 +542,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 
 bool hist_mfma_supported(const oscar_dims& d) {
   const int g = d.num_q_heads / d.num_kv_heads;
-  return (d.group_size == 64 || d.group_size == 128) && g >= 1 && g <= 8;
+  return (d.group_size == 64 || d.group_size == 128) && d.codebook == OSCAR_CODEBOOK_UNIFORM && g >= 1 && g <= 8;
 }
 
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s) {

@@ -17,7 +17,8 @@
 // float64 rounding of the sum lands within ~2^-22 ulp of a float32 tie.
 // Quantization uses IEEE float32 subtraction and division (no fast-math)
 // and round-half-even, so the codes and the bf16 scale/zero are a
-// deterministic function of the rotated values.
+// deterministic function of the rotated values (for the Lloyd-Max codebook
+// up to the summation order of the float64 group mean and variance).
 #include "demote_device.h"
 
 namespace oscar {
@@ -52,7 +53,7 @@ fill_kernel(DemoteArgs kk, DemoteArgs vv, int32_t request, int32_t hist_begin, i
   for (int t = nt; t < kMaxChunk; ++t) sm.x[t][k] = 0.f;
   __syncthreads();
   quantize_tokens<G, kMaxChunk>(sm, nt, a.r + static_cast<size_t>(kvh) * kDim * kDim,
-                                a.clip + kvh * kDim, k);
+                                a.clip + kvh * kDim, k, a.codebook, a.thr);
   const int phys = a.page_table[static_cast<size_t>(request) * a.max_pages + (j0 >> 6)];
   uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
   store_tokens<G, kMaxChunk>(sm, nt, blk, j0 & 63, is_v, k);
@@ -66,6 +67,8 @@ DemoteArgs make_args(const oscar_dims& d, const oscar_cache& c, const float* r, 
   a.page_table = c.page_table;
   a.max_pages = c.max_pages_per_req;
   a.hkv = d.num_kv_heads;
+  a.codebook = d.codebook;
+  a.thr = codebook_of(d.codebook)->thr[2];
   return a;
 }
 

@@ -2,7 +2,8 @@
 // rotate, clip, quantize and pack tokens into history page blocks (page
 // "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务", section
 // "OSCAR的另一个关键点是"; the quantizer of the first page, section
-// "为什么 INT2 KV 缓存量化很难？").
+// "为什么 INT2 KV 缓存量化很难？"; the Lloyd-Max codebook that the second
+// page's comparison with TurboQuant mentions).
 #pragma once
 
 #include "oscar_device.h"
@@ -23,15 +24,44 @@ struct QuantSmem {
   float scale[NT][kMaxNG];
   float zero[NT][kMaxNG];
   float xw[2][NT][2];          // per-wave (min, max) when a group spans both waves
+  double xd[2][2][NT];         // per-wave float64 (sum, sum of squares), same case
   uint8_t code[NT][kDim];
 };
 
+// Sum over the G lanes of this thread's group, in float64: a butterfly
+// inside the wave, then (G = 128) the two waves' halves through LDS.  Every
+// thread of the 128-thread unit calls it.
+template <int G, int NT>
+__device__ __forceinline__ void group_sum_f64(double (&v)[NT], double (&xd)[2][NT], int lane, int wave) {
+  constexpr int WG = G < 64 ? G : 64;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int off = 1; off < WG; off <<= 1) v[t] += __shfl_xor(v[t], off, 64);
+  if constexpr (G == 128) {
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xd[wave][t] = v[t];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = xd[0][t] + xd[1][t];
+  }
+}
+
 // Rotate, clip and quantize nt (<= NT) tokens held in sm.x.  Called by the
 // 128 threads of one unit (k = 0..127, two whole waves); every thread of the
-// workgroup passes the same barriers.  Leaves codes, scale and zero in sm.
+// workgroup passes the same barriers (the codebook is uniform across it).
+// Leaves codes, scale and zero in sm.
+//   OSCAR_CODEBOOK_UNIFORM: zero = bf16(min), scale = bf16((max - min) / 3),
+//     code = clamp(rint((y - zero) / scale), 0, 3).
+//   OSCAR_CODEBOOK_LLOYD_MAX: zero = bf16(float(mean)), scale =
+//     bf16(float(population standard deviation)), mean and deviation in
+//     float64; code = number of thresholds (-thr, 0, thr) below
+//     (y - zero) / scale.
+// A group whose scale is 0 gets code 0.
 template <int G, int NT>
 __device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restrict__ r,
-                                const float* __restrict__ clipv, int k) {
+                                const float* __restrict__ clipv, int k, int codebook, float thr) {
   constexpr int WG = G < 64 ? G : 64;   // group lanes inside one wave
   const int lane = k & 63, wave = k >> 6;
   auto& xw = sm.xw;
@@ -66,6 +96,37 @@ __device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restri
     y[t] = fminf(fmaxf(static_cast<float>(sum), -c), c);
     sm.y[t][k] = y[t];
   }
+  const int gi = k / G;
+  if (codebook == OSCAR_CODEBOOK_LLOYD_MAX) {
+    double mean[NT], sq[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mean[t] = static_cast<double>(y[t]);
+    group_sum_f64<G, NT>(mean, sm.xd[0], lane, wave);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      mean[t] /= G;
+      const double d = static_cast<double>(y[t]) - mean[t];
+      sq[t] = d * d;
+    }
+    group_sum_f64<G, NT>(sq, sm.xd[1], lane, wave);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float s = bf16_round(static_cast<float>(sqrt(sq[t] / G)));
+      const float z = bf16_round(static_cast<float>(mean[t]));
+      if (k % G == 0 && t < nt) {
+        sm.scale[t][gi] = s;
+        sm.zero[t][gi] = z;
+      }
+      int code = 0;
+      if (s != 0.f) {
+        const float u = (y[t] - z) / s;
+        code = (u > -thr) + (u > 0.f) + (u > thr);
+      }
+      if (t < nt) sm.code[t][k] = static_cast<uint8_t>(code);
+    }
+    __syncthreads();
+    return;
+  }
   // group min / max across the G lanes of a group
   float mn[NT], mx[NT];
 #pragma unroll
@@ -92,7 +153,6 @@ __device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restri
       mx[t] = fmaxf(xw[0][t][1], xw[1][t][1]);
     }
   }
-  const int gi = k / G;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float range = mx[t] - mn[t];
@@ -165,7 +225,8 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
     const int ring = (L - 1 - kSink) & (kRecent - 1);
     sm.x[0][k] = bf16_to_f32(recent[ring * kDim + k]);
     __syncthreads();
-    quantize_tokens<G, 1>(sm, 1, a.r + static_cast<size_t>(kvh) * kDim * kDim, a.clip + kvh * kDim, k);
+    quantize_tokens<G, 1>(sm, 1, a.r + static_cast<size_t>(kvh) * kDim * kDim, a.clip + kvh * kDim, k,
+                          a.codebook, a.thr);
     const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + (j >> 6)];
     uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
     store_tokens<G, 1>(sm, 1, blk, j & 63, is_v, k);

@@ -57,6 +57,14 @@ constexpr size_t kQPackBytes = kQPackOperandBytes + 256;
 
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len);
 
+// Float32 levels (ascending) and decision thresholds of a codebook
+// (OSCAR_CODEBOOK_*); nullptr for an unknown one.
+struct Codebook {
+  float lev[4];
+  float thr[3];
+};
+const Codebook* codebook_of(int32_t codebook);
+
 struct DemoteArgs {
   const float* r;        // [Hkv][128][128], K or V per blockIdx.z
   const float* clip;
@@ -64,6 +72,8 @@ struct DemoteArgs {
   const int32_t* page_table;
   int32_t max_pages;
   int32_t hkv;
+  int32_t codebook;      // OSCAR_CODEBOOK_*
+  float thr;             // Lloyd-Max: the positive decision threshold
 };
 
 // Everything one decode step's demotion reads and writes.

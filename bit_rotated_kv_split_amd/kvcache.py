@@ -22,8 +22,10 @@ class PagedKVCache:
     """
 
     def __init__(self, num_q_heads: int, num_kv_heads: int, group_size: int, batch: int,
-                 max_pages_per_req: int, n_pages: int, device: str = "cuda"):
-        self.dims = _lib.make_dims(num_q_heads, num_kv_heads, group_size)
+                 max_pages_per_req: int, n_pages: int, device: str = "cuda",
+                 codebook: int = _lib.CODEBOOK_UNIFORM):
+        self.dims = _lib.make_dims(num_q_heads, num_kv_heads, group_size, codebook=codebook)
+        self.codebook = codebook
         self.batch = batch
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads

@@ -114,7 +114,7 @@ def build_cache(w: configs.Workload, layout: Layout, model: SyntheticModel, rot:
     """Allocate the cache and fill it to the layout's lengths: sink and recent
     from the GPU generator, history through the library's bulk demotion."""
     cache = PagedKVCache(w.num_q_heads, w.num_kv_heads, w.group_size, w.batch, layout.max_pages,
-                         layout.n_pages, device)
+                         layout.n_pages, device, codebook=w.codebook)
     cache.page_table.copy_(torch.from_numpy(layout.page_table))
     cache.seq_lens.copy_(torch.from_numpy(layout.lens.astype(np.int32)))
     stream = torch.cuda.current_stream().cuda_stream

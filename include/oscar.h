@@ -46,9 +46,30 @@ extern "C" {
 #define OSCAR_EUNSUPPORTED 2  /* a shape this build does not implement */
 #define OSCAR_EHIP 3          /* a HIP runtime call or kernel launch failed */
 
+/* History codebooks (oscar_dims.codebook).  Both store a 2-bit code per
+ * element and a bf16 (scale, zero) pair per group of group_size channels of
+ * one token; a value decodes to zero + scale * level[code].
+ *   UNIFORM    levels 0, 1, 2, 3; zero = group minimum, scale = (max-min)/3,
+ *              code = clamp(rint((y - zero) / scale), 0, 3) (first page,
+ *              section "为什么 INT2 KV 缓存量化很难？"; second page, section
+ *              "OSCAR的另一个关键点是").
+ *   LLOYD_MAX  the 4-level Lloyd-Max levels of the standard normal
+ *              distribution (oscar_codebook); zero = group mean, scale =
+ *              population standard deviation (both in float64, then rounded
+ *              to float32 and to bf16); code = the number of decision
+ *              thresholds below (y - zero) / scale in float32.  The second
+ *              page (its comparison with TurboQuant) says OSCAR's code pairs
+ *              the rotation with a Lloyd-Max codebook; this normalisation is
+ *              this library's reading of it. */
+#define OSCAR_CODEBOOK_UNIFORM 0
+#define OSCAR_CODEBOOK_LLOYD_MAX 1
+
 /* Model and cache geometry.  Supported: head_dim 128, page_size 64,
  * sink_len 64, recent_len 256, group_size in {32, 64, 128},
- * num_q_heads a multiple of num_kv_heads with 1 <= Hq/Hkv <= 8. */
+ * num_q_heads a multiple of num_kv_heads with 1 <= Hq/Hkv <= 8, codebook
+ * OSCAR_CODEBOOK_UNIFORM or OSCAR_CODEBOOK_LLOYD_MAX (zero-initialise the
+ * struct: 0 is the uniform codebook).  The codebook is part of the cache
+ * encoding: demote and decode one cache with the same value. */
 typedef struct oscar_dims {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -57,7 +78,17 @@ typedef struct oscar_dims {
   int32_t page_size;
   int32_t sink_len;
   int32_t recent_len;
+  int32_t codebook;
 } oscar_dims;
+
+/* The levels (ascending, host float32 [4]) and decision thresholds (host
+ * float32 [3]) of a codebook.  For LLOYD_MAX the levels are the fixed point
+ * of Lloyd's conditions for N(0, 1) (each level the mean of its cell, each
+ * threshold the midpoint of its two levels), computed in float64 and rounded
+ * to float32; for UNIFORM they are 0..3 and 0.5, 1.5, 2.5 (the uniform
+ * quantizer rounds ties to even instead).  Host only; either pointer may be
+ * NULL.  Returns OSCAR_EUNSUPPORTED for an unknown codebook. */
+int oscar_codebook(int32_t codebook, float* levels, float* thresholds);
 
 /* Fixed per-layer rotations and clip thresholds, built offline from the
  * query covariance and the score-weighted value covariance
@@ -228,7 +259,8 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
                     size_t workspace_bytes, void* stream);
 
 /* Which history kernel oscar_decode_attn launches: 0 = default (MFMA where
- * available), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
+ * available: group_size 64 or 128 with the uniform codebook), 1 =
+ * vector-ALU kernel (every supported dims), 2 = matrix-core (MFMA) kernel.
  * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
 int oscar_set_history_kernel(int kind);
 

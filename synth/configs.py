@@ -25,6 +25,7 @@ class Workload:
     clip_pct: float = 99.9
     steps: int = 1
     extra: dict = field(default_factory=dict)
+    codebook: int = 0            # history codebook: 0 uniform (min/max), 1 Lloyd-Max
 
     @property
     def gqa(self) -> int:

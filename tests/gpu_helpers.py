@@ -11,6 +11,9 @@ import numpy as np
 from oracle import oscar as O
 from synth import gen
 
+# Oracle names of the library's codebooks (Workload.codebook).
+CODEBOOK_NAMES = {0: "uniform", 1: "lloyd-max"}
+
 # Attention parity bar over the same dequantized cache (absolute max and
 # relative L2 of the output).
 ATOL = 2e-3
@@ -39,7 +42,7 @@ def oracle_request(model, layout, cal, q_bits_b, b: int, L: int, heads=None):
     """Oracle output [Hq][128] and lse [Hq] of request b at length L."""
     k, v = request_tokens(model, layout, b, L)
     return O.request_attention(q_bits_b, k, v, cal["r_k32"], cal["r_v32"], cal["clip_k"],
-                               cal["clip_v"], model.w.group_size)
+                               cal["clip_v"], model.w.group_size, CODEBOOK_NAMES[model.w.codebook])
 
 
 def oracle_request_heads(model, layout, cal, q_bits_b, b: int, L: int, kv_heads):
@@ -56,7 +59,7 @@ def oracle_request_heads(model, layout, cal, q_bits_b, b: int, L: int, kv_heads)
             v[p0:p0 + n, 0] = gen.kv_tokens_bf16(w.seed, "v", src, j, p0, n, model.v_scale[j])
         res[j] = O.request_attention(q_bits_b[j * g:(j + 1) * g], k, v, cal["r_k32"][j:j + 1],
                                      cal["r_v32"][j:j + 1], cal["clip_k"][j:j + 1],
-                                     cal["clip_v"][j:j + 1], w.group_size)
+                                     cal["clip_v"][j:j + 1], w.group_size, CODEBOOK_NAMES[w.codebook])
     return res
 
 

@@ -66,9 +66,9 @@ def check_all(layout, model, cal, out, lse, q_bits, requests=None, what=""):
         assert np.abs(lse[b] - ref_lse).max() < 2e-3, f"{what} lse b={b}"
 
 
-def small(name, seed, hq, hkv, group, lens, paged=True, shared=False, aniso=True):
+def small(name, seed, hq, hkv, group, lens, paged=True, shared=False, aniso=True, codebook=0):
     return configs.Workload(name, seed, hq, hkv, group, len(lens), tuple(lens), paged=paged,
-                            shared_prefix=shared, anisotropic_q=aniso)
+                            shared_prefix=shared, anisotropic_q=aniso, codebook=codebook)
 
 
 def _run_case(w, kind, lens=None):
@@ -100,6 +100,15 @@ EDGE_LENS = [1, 30, 64, 65, 200, 320, 321, 322, 384, 385, 448, 1000, 2047, 4000]
 def test_ragged_edges_gqa4(kernel, group):
     w = small(f"edges-g{group}", 21, 8, 2, group, EDGE_LENS)
     _run_case(w, KERNELS[kernel])
+
+
+@pytest.mark.parametrize("group,hq,hkv", [(32, 8, 2), (64, 8, 2), (128, 8, 2), (64, 16, 2), (128, 2, 2)])
+def test_lloyd_max_codebook_ragged_edges(group, hq, hkv):
+    """The Lloyd-Max codebook (demotion by the library, attention on the
+    vector-ALU kernel the default selection picks) over the ragged edge
+    lengths, GQA 1, 4 and 8."""
+    w = small(f"edges-lm-g{group}", 23, hq, hkv, group, EDGE_LENS, codebook=ok.CODEBOOK_LLOYD_MAX)
+    _run_case(w, 0)
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
@@ -276,13 +285,13 @@ def test_decode_equals_two_phase(kernel, gqa, group):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-@pytest.mark.parametrize("group", [32, 128])
-def test_decode_step_equals_separate_calls(group):
+@pytest.mark.parametrize("group,codebook", [(32, 0), (128, 0), (64, 1)])
+def test_decode_step_equals_separate_calls(group, codebook):
     """oscar_decode_step (demotion inside the rotation launch) against
     oscar_kv_demote + oscar_decode on a copy of the same cache: same output
     bits, same cache bytes afterwards."""
     lens = [2000, 330, 321, 64, 5000]
-    w = small(f"stepfuse{group}", 88, 8, 2, group, lens)
+    w = small(f"stepfuse{group}", 88, 8, 2, group, lens, codebook=codebook)
     layout, model, cal, rot, cache = setup(w)
     lens1 = layout.lens + 1
     cache.seq_lens.copy_(torch.from_numpy(lens1.astype(np.int32)))
@@ -346,6 +355,27 @@ def test_full_step_sequence_matches_oracle():
     for b in range(w.batch):
         ref, _ = oracle_request(model, layout, cal, q_bits[b], b, int(lens[b]))
         assert_close(got[b], ref, f"after {steps} steps b={b}")
+
+
+@pytest.mark.slow
+def test_full_size_batch32_100k_lloyd_max_sampled():
+    """The Lloyd-Max codebook at the benchmark's full size (32 x 100K, G =
+    128) in its launch configuration (default selection: the vector-ALU
+    history kernel); sampled (request, KV head) groups against the oracle."""
+    import dataclasses
+    from gpu_helpers import oracle_request_heads
+    w = dataclasses.replace(configs.qwen3_8b_b32(128), codebook=ok.CODEBOOK_LLOYD_MAX)
+    layout, model, cal, rot, cache = setup(w)
+    assert ok.oscar_history_kernel_for(cache.dims) == 1
+    q_bits = model.queries(0, w.batch)
+    q = W.queries_tensor(model, 0, w.batch)
+    out, lse = run_decode(cache, rot, q, 100_000, 0)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    g = w.gqa
+    for b, j in ((0, 0), (31, 7)):
+        ref = oracle_request_heads(model, layout, cal, q_bits[b], b, 100_000, [j])[j]
+        assert_close(out[b, j * g:(j + 1) * g], ref[0], f"full-size lloyd b={b} kvh={j}")
+        assert np.abs(lse[b, j * g:(j + 1) * g] - ref[1]).max() < 2e-3
 
 
 @pytest.mark.slow

@@ -45,7 +45,10 @@ def make_rot(kind, hkv, rng):
     return rk, rv, ck, cv
 
 
-def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid):
+CODEBOOK_ID = {"uniform": ok.CODEBOOK_UNIFORM, "lloyd-max": ok.CODEBOOK_LLOYD_MAX}
+
+
+def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid, codebook="uniform"):
     """Oracle bytes of one page block whose first n_valid slots hold tokens."""
     ng = 128 // group
     codes_k = np.zeros((64, 128), dtype=np.uint8)
@@ -55,21 +58,22 @@ def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid):
     sv = np.zeros((64, ng), np.float32)
     zv = np.zeros((64, ng), np.float32)
     if n_valid:
-        c, s, z = O.demote(k_bits[:n_valid], rk, ck, group)
+        c, s, z = O.demote(k_bits[:n_valid], rk, ck, group, codebook)
         codes_k[:n_valid], sk[:n_valid], zk[:n_valid] = c, s, z
-        c, s, z = O.demote(v_bits[:n_valid], rv, cv, group)
+        c, s, z = O.demote(v_bits[:n_valid], rv, cv, group, codebook)
         codes_v[:n_valid], sv[:n_valid], zv[:n_valid] = c, s, z
     return O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
 
 
+@pytest.mark.parametrize("codebook", ["uniform", "lloyd-max"])
 @pytest.mark.parametrize("group", [32, 64, 128])
 @pytest.mark.parametrize("kind", ["identity", "signed_perm"])
-def test_fill_bit_exact(group, kind):
+def test_fill_bit_exact(group, kind, codebook):
     rng = np.random.default_rng(group + (7 if kind == "identity" else 9))
     B, hkv, hq = 2, 2, 4
     n_hist = [150, 64]
     max_pages = 3
-    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8)
+    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8, codebook=CODEBOOK_ID[codebook])
     pt = np.array([[5, 0, 3], [7, 2, 6]], dtype=np.int32)
     cache.page_table.copy_(torch.from_numpy(pt))
     cache.seq_lens.copy_(torch.tensor([320 + n for n in n_hist], dtype=torch.int32))
@@ -92,7 +96,7 @@ def test_fill_bit_exact(group, kind):
                 continue
             for j in range(hkv):
                 exp = expected_block(kb[64 * p:64 * p + n_valid, j], vb[64 * p:64 * p + n_valid, j],
-                                     rk[j], rv[j], ck[j], cv[j], group, n_valid)
+                                     rk[j], rv[j], ck[j], cv[j], group, n_valid, codebook)
                 got = pages[pt[b, p], j]
                 assert np.array_equal(got, exp), f"b={b} page={p} kvh={j}"
     # pages no request uses stay zero
@@ -161,8 +165,8 @@ def ring_expect(L, k_all):
     return ring
 
 
-@pytest.mark.parametrize("group", [32, 128])
-def test_decode_steps_append_and_demote(group):
+@pytest.mark.parametrize("group,codebook", [(32, "uniform"), (128, "uniform"), (64, "lloyd-max")])
+def test_decode_steps_append_and_demote(group, codebook):
     """A sequence of decode steps (append + demote) from L = 60 to L = 480
     crosses every region boundary and two page boundaries; the GPU state after
     the last step equals the oracle's: sink and ring bits, packed pages."""
@@ -178,7 +182,7 @@ def test_decode_steps_append_and_demote(group):
     rk, rv, ck, cv = make_rot("signed_perm", hkv, rng)
     rot = Rotation(rk, rv, ck, cv)
     max_pages = 4
-    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8)
+    cache = PagedKVCache(hq, hkv, group, B, max_pages, 8, codebook=CODEBOOK_ID[codebook])
     pt = np.array([[4, 1, 2, 6], [0, 5, 3, 7]], dtype=np.int32)
     cache.page_table.copy_(torch.from_numpy(pt))
     # initial state: positions < start[b] as the state machine leaves them
@@ -213,7 +217,8 @@ def test_decode_steps_append_and_demote(group):
             n_valid = min(64, n_hist - 64 * p)
             for j in range(hkv):
                 sl = slice(64 + 64 * p, 64 + 64 * p + n_valid)
-                exp = expected_block(k_all[sl, j], v_all[sl, j], rk[j], rv[j], ck[j], cv[j], group, n_valid)
+                exp = expected_block(k_all[sl, j], v_all[sl, j], rk[j], rv[j], ck[j], cv[j], group, n_valid,
+                                     codebook)
                 assert np.array_equal(pages[pt[b, p], j], exp), f"b={b} page={p} kvh={j}"
 
 

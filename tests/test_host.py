@@ -81,6 +81,8 @@ def _rot():
     ("recent_len", 128, ok.OSCAR_EUNSUPPORTED),
     ("num_kv_heads", 0, ok.OSCAR_EINVAL),
     ("num_q_heads", 12, ok.OSCAR_EINVAL),     # not a multiple of 8
+    ("codebook", 2, ok.OSCAR_EUNSUPPORTED),
+    ("codebook", -1, ok.OSCAR_EUNSUPPORTED),
 ])
 def test_invalid_dims_rejected(field, value, code):
     d = ok.make_dims(32, 8, 128)
@@ -148,6 +150,37 @@ def test_history_kernel_selector():
     assert ok.oscar_set_history_kernel(prev) == 1
     with pytest.raises(ok.OscarError):
         ok.oscar_set_history_kernel(7)
+
+
+def test_codebook_constants_equal_the_oracle():
+    """The library's Lloyd-Max codebook (bisection on the threshold) and the
+    oracle's (Lloyd's alternation) agree to the last float32 bit."""
+    import numpy as np
+    from oracle import oscar as O
+    lev, thr = ok.oscar_codebook(ok.CODEBOOK_LLOYD_MAX)
+    olev, othr = O.lloyd_max_codebook()
+    assert lev.view(np.uint32).tolist() == olev.view(np.uint32).tolist()
+    assert thr.view(np.uint32).tolist() == othr.view(np.uint32).tolist()
+    lev, thr = ok.oscar_codebook(ok.CODEBOOK_UNIFORM)
+    assert lev.tolist() == [0, 1, 2, 3] and thr.tolist() == [0.5, 1.5, 2.5]
+    with pytest.raises(ok.OscarError):
+        ok.oscar_codebook(5)
+
+
+def test_lloyd_max_codebook_runs_on_the_vector_alu_kernel():
+    d = ok.make_dims(32, 8, 128, codebook=ok.CODEBOOK_LLOYD_MAX)
+    assert ok.oscar_history_kernel_for(d) == 1
+    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 128)) == 2
+    prev = ok.oscar_set_history_kernel(2)
+    try:
+        assert ok.oscar_history_kernel_for(d) == -1
+        # refused before anything is enqueued (the pointers here are not real)
+        with pytest.raises(ok.OscarError) as e:
+            ok.oscar_decode_step(d, _rot(), _cache(), 0x1000, 0x1000, 0x1000, 100, 0x1000, 1 << 30, 0x1000, None,
+                                 0)
+        assert e.value.code == ok.OSCAR_EUNSUPPORTED
+    finally:
+        ok.oscar_set_history_kernel(prev)
 
 
 def test_last_error_is_thread_local():
