@@ -34,6 +34,13 @@
 // the output along the dominant value direction; with the carry the
 // rounded weights of a lane add up to the exact ones within half a unit.
 //
+// The Lloyd-Max codebook (levels -hi, -lo, lo, hi for codes 0..3) splits a
+// code c = 2 b1 + b0 into bit planes: level(c) = -hi + (hi - lo) c +
+// (3 lo - hi) b1.  The c plane is the uniform kernel's operand; the b1 plane
+// is the same masked word ANDed down to its high bits (2 b1 4^j), one more
+// matrix-core product against the same A operand.  The -hi term joins the
+// zero point (zero - hi * scale per token and group).
+//
 // One wave per workgroup; the workgroup owns (history split, KV head,
 // request), and five more workgroups per (KV head, request) run the bf16
 // sink/recent chunks (decode_bf16.h) alongside the history splits.  Per 64-token page a lane loads 4 x 16 B of codes and the
@@ -62,6 +69,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_HIST_MIN_WAVES
 #define OSCAR_HIST_MIN_WAVES 2
 #endif
+// the Lloyd-Max form holds a second set of value accumulators
+#ifndef OSCAR_HIST_BUFFERS_LM
+#define OSCAR_HIST_BUFFERS_LM 3
+#endif
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
@@ -83,6 +94,16 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
   r.z = static_cast<int>(w & 0x30303030u);
   r.w = static_cast<int>((w >> 6) & 0x03030303u);
   return r;
+}
+
+// High bits of the masked codes of unpack16: 2 b1 4^j in place of c 4^j.
+__device__ __forceinline__ v4i high_bits(const v4i& r) {
+  v4i h;
+  h.x = r.x & 0x02020202;
+  h.y = r.y & 0x08080808;
+  h.z = r.z & 0x20202020;
+  h.w = r.w & 0x02020202;
+  return h;
 }
 
 // value of the signed base-256 digit rows of q . code
@@ -158,6 +179,9 @@ struct MfmaParams {
   int32_t hq;
   int32_t gq;
   int32_t slots;          // history workgroups per KV head in the grid
+  float lm_hi;            // Lloyd-Max: the outer level hi
+  float lm_ka;            // hi - lo: weight of the code plane
+  float lm_kb;            // (3 lo - hi) / 2: weight of the 2 b1 plane
   Bf16Params bf;          // the bf16 sink/recent chunks, run as extra workgroups
 };
 
@@ -199,6 +223,7 @@ struct WaveState {
   float unit[NHB][NG];     // P' fixed-point unit
   float inv[NHB][NG];      // 4^-j / unit for this lane's token residue j
   v4i dacc[NHB][8];        // int32 digit accumulators of P' . code, channel block cb
+  v4i dacc1[NHB][8];       // Lloyd-Max only: the same for the 2 b1 plane
   float accf[NHB][8];      // folded float accumulators
   float ls[NHB];           // per-lane partial sum of p
   float carry[NHB][NG];    // rounding carry of this lane's P' digits, in [0, 1) units
@@ -219,10 +244,18 @@ struct HistSmem {
 
 // Fold the int32 accumulators of flagged heads into float, rescale to the
 // new reference max and take a new P' unit from the current page.
-template <int NHB, int G>
+// Float value, in units of the head's P' unit, of the accumulated P' .
+// level products of channel block cb.
+template <bool LM, int NHB, int G>
+__device__ __forceinline__ float acc_value(const WaveState<NHB, G>& st, int hb, int cb, float ka, float kb) {
+  if constexpr (LM) return ka * p_digits(st.dacc[hb][cb]) + kb * p_digits(st.dacc1[hb][cb]);
+  else return p_digits(st.dacc[hb][cb]);
+}
+
+template <bool LM, int NHB, int G>
 __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[NHB][4],
                                     const PageRegs<G>& cur, const bool (&need)[NHB],
-                                    HistSmem<NHB, kDim / G>& sm, int lane) {
+                                    HistSmem<NHB, kDim / G>& sm, int lane, float ka, float kb) {
   constexpr int NG = kDim / G;
   // P' of this lane's tokens (residue j = n % 4 in the K-slot order) meets
   // codes masked in place, i.e. times 4^j for j < 3: carry 4^-j here
@@ -236,10 +269,11 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const int gi = (16 * cb) / G;
-      const float folded = (st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb])) * alpha;
+      const float folded = (st.accf[hb][cb] + st.unit[hb][gi] * acc_value<LM>(st, hb, cb, ka, kb)) * alpha;
       st.accf[hb][cb] = need[hb] ? folded : st.accf[hb][cb];
       const v4i z = {0, 0, 0, 0};
       st.dacc[hb][cb] = need[hb] ? z : st.dacc[hb][cb];
+      if constexpr (LM) st.dacc1[hb][cb] = need[hb] ? z : st.dacc1[hb][cb];
     }
     st.ls[hb] *= alpha;
 #pragma unroll
@@ -261,9 +295,10 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
   }
 }
 
-template <int NHB, int G>
+template <bool LM, int NHB, int G>
 __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
-                                             int n_hist, int lane, HistSmem<NHB, kDim / G>& sm) {
+                                             int n_hist, int lane, HistSmem<NHB, kDim / G>& sm,
+                                             float lm_hi, float ka, float kb) {
   constexpr int NG = kDim / G;
   const int n = lane & 15, lg = lane >> 4;
   // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n
@@ -276,7 +311,33 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
     for (int hb = 0; hb < NHB; ++hb) {
       const v4i zero = {0, 0, 0, 0};
       float s;
-      if constexpr (NG == 1) {
+      if constexpr (LM) {
+        // level sum = ka * (q . c) + kb * (q . 2 b1); zero - hi * scale for the rest
+        const v4i h0 = high_bits(b0), h1 = high_bits(b1);
+        if constexpr (NG == 1) {
+          v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
+          v4i e = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], h0, zero, 0, 0, 0);
+          e = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], h1, e, 0, 0, 0);
+          const uint32_t sz = cur.ksz[m];
+          const float ks = __uint_as_float(sz << 16);
+          const float kz = __builtin_fmaf(-lm_hi, ks, __uint_as_float(sz & 0xFFFF0000u));
+          s = __builtin_fmaf(ks * st.qs[hb], __builtin_fmaf(ka, q_digits(d), kb * q_digits(e)), kz * st.qz[hb][0]);
+        } else {
+          const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+          const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
+          const v4i e0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], h0, zero, 0, 0, 0);
+          const v4i e1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], h1, zero, 0, 0, 0);
+          const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
+          const float ks0 = __uint_as_float(s0 << 16), ks1 = __uint_as_float(s1 << 16);
+          const float kz0 = __builtin_fmaf(-lm_hi, ks0, __uint_as_float(s0 & 0xFFFF0000u));
+          const float kz1 = __builtin_fmaf(-lm_hi, ks1, __uint_as_float(s1 & 0xFFFF0000u));
+          s = __builtin_fmaf(ks0 * st.qs[hb], __builtin_fmaf(ka, q_digits(d0), kb * q_digits(e0)),
+                             kz0 * st.qz[hb][0]) +
+              __builtin_fmaf(ks1 * st.qs[hb], __builtin_fmaf(ka, q_digits(d1), kb * q_digits(e1)),
+                             kz1 * st.qz[hb][1]);
+        }
+      } else if constexpr (NG == 1) {
         v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
         const uint32_t sz = cur.ksz[m];
@@ -328,7 +389,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) need[hb] = force || ((mask >> (16 * lg)) & 0xFFFFull) != 0;
     if (force) st.since_fold = 0;
-    rebase<NHB, G>(st, sc, cur, need, sm, lane);
+    rebase<LM, NHB, G>(st, sc, cur, need, sm, lane, ka, kb);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -351,7 +412,9 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t sz = cur.vsz[m * NG + gi];
-        zpage = __builtin_fmaf(pr[hb][m], __uint_as_float(sz & 0xFFFF0000u), zpage);
+        float vz = __uint_as_float(sz & 0xFFFF0000u);
+        if constexpr (LM) vz = __builtin_fmaf(-lm_hi, __uint_as_float(sz << 16), vz);
+        zpage = __builtin_fmaf(pr[hb][m], vz, zpage);
         // floor with the carried fraction: the lane's rounded weights add up
         // to its exact ones within one unit
         const float t = xv[hb][gi][m] + st.carry[hb][gi];
@@ -382,13 +445,19 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
       st.dacc[hb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], bv, st.dacc[hb][cb], 0, 0, 0);
+    if constexpr (LM) {
+      const v4i bh = high_bits(bv);
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        st.dacc1[hb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], bh, st.dacc1[hb][cb], 0, 0, 0);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int G, int WAVES, int BUF, int MINW>
+template <int G, int WAVES, int BUF, int MINW, bool LM>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(MINW)))
 hist_mfma_kernel(MfmaParams a) {
   constexpr int NHB = 1;
@@ -451,6 +520,7 @@ hist_mfma_kernel(MfmaParams a) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       st.dacc[hb][cb] = v4i{0, 0, 0, 0};
+      if constexpr (LM) st.dacc1[hb][cb] = v4i{0, 0, 0, 0};
       st.accf[hb][cb] = 0.f;
     }
   }
@@ -480,7 +550,7 @@ hist_mfma_kernel(MfmaParams a) {
 #pragma unroll
     for (int k = 0; k < BUF; ++k) {
       if (p + k + BUF - 1 < p1) load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(p + k + BUF - 1), lane);
-      process_page<NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm);
+      process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
       if (p + k + 1 >= p1) break;
     }
   }
@@ -502,16 +572,18 @@ hist_mfma_kernel(MfmaParams a) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const int gi = (16 * cb) / G;
-      const double o = static_cast<double>(st.accf[hb][cb] + st.unit[hb][gi] * p_digits(st.dacc[hb][cb])) + zsum[gi];
+      const double o =
+          static_cast<double>(st.accf[hb][cb] + st.unit[hb][gi] * acc_value<LM>(st, hb, cb, a.lm_ka, a.lm_kb)) +
+          zsum[gi];
       a.po[pidx * kDim + 16 * cb + n] = static_cast<float>(o) * inv_l;
     }
     if (n == 0) a.plse[pidx] = any ? (st.m_ref[hb] + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
-template <int G, int WAVES>
+template <int G, int WAVES, bool LM>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int BUF = OSCAR_HIST_BUFFERS;
+  constexpr int BUF = LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS;
   constexpr int MINW = OSCAR_HIST_MIN_WAVES;
   const oscar_dims& d = *a.dims;
   MfmaParams p;
@@ -528,13 +600,18 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.hq = d.num_q_heads;
   p.gq = d.num_q_heads / d.num_kv_heads;
   p.slots = a.lay.slots;
+  const Codebook* cbk = codebook_of(d.codebook);
+  p.lm_hi = cbk->lev[3];
+  p.lm_ka = cbk->lev[3] - cbk->lev[2];
+  p.lm_kb = (3.f * cbk->lev[2] - cbk->lev[3]) * 0.5f;
   p.bf = make_bf16_params(a);
   const dim3 grid((a.lay.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
   const dim3 block(64 * WAVES);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
-    hipExtLaunchKernelGGL(hist_mfma_kernel<G, WAVES, BUF, MINW>, grid, block, 0, s, a.ev_start, a.ev_stop, 0, p);
+    hipExtLaunchKernelGGL(hist_mfma_kernel<G, WAVES, BUF, MINW, LM>, grid, block, 0, s, a.ev_start, a.ev_stop, 0,
+                          p);
   else
-    hist_mfma_kernel<G, WAVES, BUF, MINW><<<grid, block, 0, s>>>(p);
+    hist_mfma_kernel<G, WAVES, BUF, MINW, LM><<<grid, block, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -542,14 +619,18 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 
 bool hist_mfma_supported(const oscar_dims& d) {
   const int g = d.num_q_heads / d.num_kv_heads;
-  return (d.group_size == 64 || d.group_size == 128) && d.codebook == OSCAR_CODEBOOK_UNIFORM && g >= 1 && g <= 8;
+  return (d.group_size == 64 || d.group_size == 128) && g >= 1 && g <= 8;
 }
 
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s) {
   const int g = a.dims->num_q_heads / a.dims->num_kv_heads;
   const bool two = g > 4;
-  if (a.dims->group_size == 64) return two ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
-  return two ? launch_t<128, 2>(a, s) : launch_t<128, 1>(a, s);
+  if (a.dims->codebook == OSCAR_CODEBOOK_LLOYD_MAX) {
+    if (a.dims->group_size == 64) return two ? launch_t<64, 2, true>(a, s) : launch_t<64, 1, true>(a, s);
+    return two ? launch_t<128, 2, true>(a, s) : launch_t<128, 1, true>(a, s);
+  }
+  if (a.dims->group_size == 64) return two ? launch_t<64, 2, false>(a, s) : launch_t<64, 1, false>(a, s);
+  return two ? launch_t<128, 2, false>(a, s) : launch_t<128, 1, false>(a, s);
 }
 
 }  // namespace oscar

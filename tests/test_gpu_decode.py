@@ -102,13 +102,13 @@ def test_ragged_edges_gqa4(kernel, group):
     _run_case(w, KERNELS[kernel])
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("group,hq,hkv", [(32, 8, 2), (64, 8, 2), (128, 8, 2), (64, 16, 2), (128, 2, 2)])
-def test_lloyd_max_codebook_ragged_edges(group, hq, hkv):
-    """The Lloyd-Max codebook (demotion by the library, attention on the
-    vector-ALU kernel the default selection picks) over the ragged edge
-    lengths, GQA 1, 4 and 8."""
+def test_lloyd_max_codebook_ragged_edges(group, hq, hkv, kernel):
+    """The Lloyd-Max codebook (demotion by the library, attention on either
+    history kernel) over the ragged edge lengths, GQA 1, 4 and 8."""
     w = small(f"edges-lm-g{group}", 23, hq, hkv, group, EDGE_LENS, codebook=ok.CODEBOOK_LLOYD_MAX)
-    _run_case(w, 0)
+    _run_case(w, KERNELS[kernel])
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
@@ -318,8 +318,9 @@ def test_decode_step_equals_separate_calls(group, codebook):
     assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
 
 
-def test_valu_and_mfma_agree():
-    w = small("agree", 70, 8, 2, 128, [7000, 321, 2000])
+@pytest.mark.parametrize("codebook", [0, 1])
+def test_valu_and_mfma_agree(codebook):
+    w = small("agree", 70, 8, 2, 128, [7000, 321, 2000], codebook=codebook)
     layout, model, cal, rot, cache = setup(w)
     q = W.queries_tensor(model, 0, w.batch)
     a, _ = run_decode(cache, rot, q, 7000, KERNELS["valu"])
@@ -360,13 +361,13 @@ def test_full_step_sequence_matches_oracle():
 @pytest.mark.slow
 def test_full_size_batch32_100k_lloyd_max_sampled():
     """The Lloyd-Max codebook at the benchmark's full size (32 x 100K, G =
-    128) in its launch configuration (default selection: the vector-ALU
+    128) in its launch configuration (default selection: the matrix-core
     history kernel); sampled (request, KV head) groups against the oracle."""
     import dataclasses
     from gpu_helpers import oracle_request_heads
     w = dataclasses.replace(configs.qwen3_8b_b32(128), codebook=ok.CODEBOOK_LLOYD_MAX)
     layout, model, cal, rot, cache = setup(w)
-    assert ok.oscar_history_kernel_for(cache.dims) == 1
+    assert ok.oscar_history_kernel_for(cache.dims) == 2
     q_bits = model.queries(0, w.batch)
     q = W.queries_tensor(model, 0, w.batch)
     out, lse = run_decode(cache, rot, q, 100_000, 0)

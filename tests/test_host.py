@@ -167,17 +167,19 @@ def test_codebook_constants_equal_the_oracle():
         ok.oscar_codebook(5)
 
 
-def test_lloyd_max_codebook_runs_on_the_vector_alu_kernel():
-    d = ok.make_dims(32, 8, 128, codebook=ok.CODEBOOK_LLOYD_MAX)
-    assert ok.oscar_history_kernel_for(d) == 1
-    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 128)) == 2
+def test_history_kernel_choice_by_codebook_and_group():
+    lm = ok.CODEBOOK_LLOYD_MAX
+    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 128, codebook=lm)) == 2
+    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 64, codebook=lm)) == 2
+    d32 = ok.make_dims(32, 8, 32, codebook=lm)
+    assert ok.oscar_history_kernel_for(d32) == 1
     prev = ok.oscar_set_history_kernel(2)
     try:
-        assert ok.oscar_history_kernel_for(d) == -1
+        assert ok.oscar_history_kernel_for(d32) == -1
         # refused before anything is enqueued (the pointers here are not real)
         with pytest.raises(ok.OscarError) as e:
-            ok.oscar_decode_step(d, _rot(), _cache(), 0x1000, 0x1000, 0x1000, 100, 0x1000, 1 << 30, 0x1000, None,
-                                 0)
+            ok.oscar_decode_step(d32, _rot(), _cache(), 0x1000, 0x1000, 0x1000, 100, 0x1000, 1 << 30, 0x1000,
+                                 None, 0)
         assert e.value.code == ok.OSCAR_EUNSUPPORTED
     finally:
         ok.oscar_set_history_kernel(prev)
