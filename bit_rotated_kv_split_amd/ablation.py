@@ -20,6 +20,9 @@ Rotation sets (every one clipped per channel at the calibration data's
   hadamard-bitrev R = H P (H then the 7-bit bit-reversal permutation)
   oscar           R_K = U_Q H P, R_V = U_S H P from oscar_calibrate
   oscar-noclip    the same rotations, no clipping
+  oscar-lloyd-max OSCAR's rotations with the Lloyd-Max codebook (levels of
+                  N(0, 1) on mean/deviation-normalised groups) in place of
+                  the uniform min/max levels
 
 The generator's raw queries (q-scale 1) give attention logits with a
 standard deviation near 10 over a 32K context, so each head attends to a
@@ -128,14 +131,17 @@ def run(batch: int = 4, context: int = 32768, seed: int = 11, q_heads: int = 32,
         torch.cuda.synchronize()
         del cws
         big = np.full((hkv, 128), 3.0e38, dtype=np.float32)
-        sets = fixed_sets + [("oscar", rk, rv, ck, cv), ("oscar-noclip", rk, rv, big, big)]
-        for name, r_k, r_v, c_k, c_v in sets:
+        sets = [s + (ok.CODEBOOK_UNIFORM,) for s in fixed_sets]
+        sets += [("oscar", rk, rv, ck, cv, ok.CODEBOOK_UNIFORM), ("oscar-noclip", rk, rv, big, big, ok.CODEBOOK_UNIFORM),
+                 ("oscar-lloyd-max", rk, rv, ck, cv, ok.CODEBOOK_LLOYD_MAX)]
+        for name, r_k, r_v, c_k, c_v, cb in sets:
             rot = Rotation(r_k, r_v, c_k, c_v)
-            cache = W.build_cache(w, layout, model, rot)
-            ws = DecodeWorkspace(dims, B, L)
+            wc = dataclasses.replace(w, codebook=cb)
+            cache = W.build_cache(wc, layout, model, rot)
+            ws = DecodeWorkspace(cache.dims, B, L)
             out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
             lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
-            ok.oscar_decode(dims, rot.struct, cache.struct(), q, L, ws.buf, ws.nbytes, out, lse)
+            ok.oscar_decode(cache.dims, rot.struct, cache.struct(), q, L, ws.buf, ws.nbytes, out, lse)
             torch.cuda.synchronize()
             o = out.cpu().numpy().astype(np.float64)
             rel = np.linalg.norm(o - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
