@@ -163,6 +163,8 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads in the oracle sample")
     ap.add_argument("--bf16-baseline", choices=["auto", "on", "off"], default="auto",
                     help="also time the all-bf16 cache decode step (auto: on for the 32 x 100K workloads)")
+    ap.add_argument("--history-target", type=int, default=0,
+                    help="history workgroups the split schedule aims for (0: the library default)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="accepted for older command lines; the 2 GiB copy probe always runs")
     args = ap.parse_args()
@@ -227,6 +229,7 @@ def main() -> int:
     kn_all = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).cuda()
     vn_all = torch.from_numpy(vn.view(np.int16)).view(torch.bfloat16).cuda()
     max_len = int(lens_t.max())
+    ok.oscar_set_history_target(args.history_target)
     ws = DecodeWorkspace(dims, B, max_len)
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     structs = [[ok.make_cache(c.pages, c.n_pages, c.sink_k, c.sink_v, c.recent_k, c.recent_v, c.page_table,
@@ -334,7 +337,7 @@ def main() -> int:
         "config": {"workload": w.name, "batch": B, "context": int(layout.lens.max()),
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
                    "group_size": w.group_size, "codebook": ("uniform", "lloyd-max")[w.codebook],
-                   "page_size": 64, "history_split_slots": ws.splits,
+                   "page_size": 64, "history_split_slots": ws.splits, "history_target": args.history_target,
                    "layer_caches": n_layers, "history_kernel": kname, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(k3_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(k3_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,

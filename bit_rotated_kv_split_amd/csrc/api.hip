@@ -98,11 +98,10 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len) {
   (void)max_seq_len;
   WsLayout w;
-  // About as many history workgroups as the history kernel keeps resident
-  // (256 compute units x 4 SIMDs x 2 waves; one wave per SIMD for the
-  // eight-head kernel), unless set with oscar_set_history_target.
+  // About as many history workgroups as the matrix-core history kernel keeps
+  // resident, unless set with oscar_set_history_target.
   int target_wg = g_hist_target.load();
-  if (target_wg == 0) target_wg = d.num_q_heads / d.num_kv_heads > 4 ? kDefaultTargetWg / 2 : kDefaultTargetWg;
+  if (target_wg == 0) target_wg = hist_default_target(d);
   const int t = (target_wg + d.num_kv_heads - 1) / d.num_kv_heads;
   w.target = t;
   w.slots = t + batch;

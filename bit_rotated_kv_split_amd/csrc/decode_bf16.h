@@ -7,6 +7,8 @@
 //   q . k: lane = token, its 256-byte key row in sixteen 16-byte loads;
 //   p . v: lane = (8-channel group, token residue mod 4), 16-byte loads
 //          coalesced along each value row, reduced over the residues.
+// Rows are read a quarter at a time (four 16-byte loads in flight per lane)
+// to keep the register count low.
 #pragma once
 
 #include <math.h>
@@ -77,32 +79,37 @@ __device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int h_lo
   const uint16_t* vb = chunk == 0 ? a.sink_v + kv0 * kSink * kDim
                                   : a.recent_v + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
   const bool valid = lane < n_valid;
-  // key row of this lane's token (a valid row is read either way)
-  uint4 krow[kDim / 8];
-  const uint4* row = reinterpret_cast<const uint4*>(kb + (valid ? lane : 0) * kDim);
-#pragma unroll
-  for (int v8 = 0; v8 < kDim / 8; ++v8) krow[v8] = row[v8];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // key row of this lane's token (a valid row is read either way), a
+  // quarter (64 bytes) at a time: the chunk runs inside the matrix-core
+  // history kernel, whose register budget it must not raise
   float sc[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
+  const uint4* row = reinterpret_cast<const uint4*>(kb + (valid ? lane : 0) * kDim);
+#pragma unroll 1
+  for (int qt = 0; qt < 4; ++qt) {
+    uint4 krow[4];
 #pragma unroll
-  for (int v8 = 0; v8 < kDim / 8; ++v8) {
-    const uint32_t ws[4] = {krow[v8].x, krow[v8].y, krow[v8].z, krow[v8].w};
+    for (int i = 0; i < 4; ++i) krow[i] = row[4 * qt + i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = __uint_as_float(ws[j] << 16);
-      const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
-      const int ch = v8 * 8 + 2 * j;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ws[4] = {krow[i].x, krow[i].y, krow[i].z, krow[i].w};
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        sc[h] = __builtin_fmaf(sm.q[h][ch], lo, sc[h]);
-        sc[h] = __builtin_fmaf(sm.q[h][ch + 1], hi, sc[h]);
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(ws[j] << 16);
+        const float hi = __uint_as_float(ws[j] & 0xFFFF0000u);
+        const int ch = (4 * qt + i) * 8 + 2 * j;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          sc[h] = __builtin_fmaf(sm.q[h][ch], lo, sc[h]);
+          sc[h] = __builtin_fmaf(sm.q[h][ch + 1], hi, sc[h]);
+        }
       }
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float mx[GQ], lsum[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -116,28 +123,32 @@ __device__ __forceinline__ void bf16_chunk(const Bf16Params& a, int gq, int h_lo
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int cg = lane & 15, res = lane >> 4;
-  uint4 vrow[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = res + 4 * i;
-    vrow[i] = *reinterpret_cast<const uint4*>(vb + (t < n_valid ? t : 0) * kDim + cg * 8);
-  }
   float acc[GQ][8];
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  // value rows a quarter (four tokens per lane) at a time, as for the keys
+#pragma unroll 1
+  for (int qt = 0; qt < 4; ++qt) {
+    uint4 vrow[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = res + 4 * i;
-    const uint32_t ws[4] = {vrow[i].x, vrow[i].y, vrow[i].z, vrow[i].w};
+    for (int i = 0; i < 4; ++i) {
+      const int t = res + 4 * (4 * qt + i);
+      vrow[i] = *reinterpret_cast<const uint4*>(vb + (t < n_valid ? t : 0) * kDim + cg * 8);
+    }
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const float pt = t < n_valid ? sm.p[h][t] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int t = res + 4 * (4 * qt + i);
+      const uint32_t ws[4] = {vrow[i].x, vrow[i].y, vrow[i].z, vrow[i].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[h][2 * j] = __builtin_fmaf(pt, __uint_as_float(ws[j] << 16), acc[h][2 * j]);
-        acc[h][2 * j + 1] = __builtin_fmaf(pt, __uint_as_float(ws[j] & 0xFFFF0000u), acc[h][2 * j + 1]);
+      for (int h = 0; h < GQ; ++h) {
+        const float pt = t < n_valid ? sm.p[h][t] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[h][2 * j] = __builtin_fmaf(pt, __uint_as_float(ws[j] << 16), acc[h][2 * j]);
+          acc[h][2 * j + 1] = __builtin_fmaf(pt, __uint_as_float(ws[j] & 0xFFFF0000u), acc[h][2 * j + 1]);
+        }
       }
     }
   }

@@ -69,9 +69,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_HIST_MIN_WAVES
 #define OSCAR_HIST_MIN_WAVES 2
 #endif
+// order of a page step: load the page BUF-1 ahead, then process (1), or
+// process, then reload the freed buffer with the page BUF ahead (0)
+#ifndef OSCAR_HIST_LOAD_FIRST
+#define OSCAR_HIST_LOAD_FIRST 1
+#endif
 // the Lloyd-Max form holds a second set of value accumulators
 #ifndef OSCAR_HIST_BUFFERS_LM
 #define OSCAR_HIST_BUFFERS_LM 3
+#endif
+#ifndef OSCAR_HIST_MIN_WAVES_LM
+#define OSCAR_HIST_MIN_WAVES_LM OSCAR_HIST_MIN_WAVES
 #endif
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
@@ -240,6 +248,7 @@ template <int NHB, int NG>
 struct HistSmem {
   int32_t pop[NHB * NG][16][16];   // P' operand rows: [head block x group][4 h + digit][16 dwords]
   double zacc[NHB * NG][64];
+  int32_t pt[64];                  // page-table entries pt_base .. pt_base + 63 of the split
 };
 
 // Fold the int32 accumulators of flagged heads into float, rescale to the
@@ -524,35 +533,57 @@ hist_mfma_kernel(MfmaParams a) {
       st.accf[hb][cb] = 0.f;
     }
   }
-  // Page-table entries of the split, 64 at a time in one register (lane i
-  // holds entry base + i) and broadcast with readlane: page addresses need
-  // no dependent load inside the loop.
+  // Page-table entries of the split, 64 at a time in LDS (lane i writes
+  // entry base + i), read back at a uniform address: the page addresses need
+  // no dependent global load inside the loop, and the only wait on a global
+  // load for them is at the refill every 64 pages.  (Holding them in a
+  // register and broadcasting with readlane made the compiler wait for every
+  // outstanding load before each page's address.)
   const int32_t* pt = a.page_table + static_cast<size_t>(b) * a.max_pages;
   const size_t blk_stride = static_cast<size_t>(a.hkv) * block_bytes(G);
   const uint8_t* base = a.pages + static_cast<size_t>(kvh) * block_bytes(G);
   int pt_base = p0;
-  int pt_reg = p0 + lane < p1 ? pt[p0 + lane] : 0;
+  sm.pt[lane] = p0 + lane < p1 ? pt[p0 + lane] : 0;
   auto page_ptr = [&](int p) -> const uint8_t* {
     if (p - pt_base >= 64) {   // uniform: every lane sees the same p
       pt_base += 64;
-      pt_reg = pt_base + lane < p1 ? pt[pt_base + lane] : 0;
+      sm.pt[lane] = pt_base + lane < p1 ? pt[pt_base + lane] : 0;
     }
-    const int phys = __builtin_amdgcn_readlane(pt_reg, p - pt_base);
+    const int phys = __builtin_amdgcn_readfirstlane(sm.pt[p - pt_base]);
     return base + static_cast<size_t>(phys) * blk_stride;
   };
   // BUF register page buffers: pages p+1 .. p+BUF-1 are in flight while p
   // is processed.  The inner loop is unrolled, so buffer indices are static.
-  PageRegs<G> buf[BUF];
+  // Every step issues its loads (past the split's end it reloads the last
+  // page, which the cache serves), so the count of loads between a page's
+  // loads and its use is the same on every path and the compiler's wait
+  // before a page can leave the younger pages in flight.
+  if (p0 < p1) {   // uniform
+    const int p_last = p1 - 1;
+    PageRegs<G> buf[BUF];
+#if OSCAR_HIST_LOAD_FIRST
 #pragma unroll
-  for (int k = 0; k < BUF - 1; ++k)
-    if (p0 + k < p1) load_page<G>(buf[k], page_ptr(p0 + k), lane);
-  for (int p = p0; p < p1; p += BUF) {
+    for (int k = 0; k < BUF - 1; ++k) load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+    for (int p = p0; p < p1; p += BUF) {
 #pragma unroll
-    for (int k = 0; k < BUF; ++k) {
-      if (p + k + BUF - 1 < p1) load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(p + k + BUF - 1), lane);
-      process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
-      if (p + k + 1 >= p1) break;
+      for (int k = 0; k < BUF; ++k) {
+        load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
+        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+        if (p + k + 1 >= p1) break;
+      }
     }
+#else
+#pragma unroll
+    for (int k = 0; k < BUF; ++k) load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+    for (int p = p0; p < p1; p += BUF) {
+#pragma unroll
+      for (int k = 0; k < BUF; ++k) {
+        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+        if (p + k + 1 >= p1) break;
+        load_page<G>(buf[k], page_ptr(min(p + k + BUF, p_last)), lane);
+      }
+    }
+#endif
   }
 
   // ---- partial output of this split (rotated value domain)
@@ -581,10 +612,22 @@ hist_mfma_kernel(MfmaParams a) {
   }
 }
 
+// Register page buffers and waves per SIMD of each instantiation.  The
+// two-wave (GQA-8) G = 128 uniform kernel fits three waves per SIMD with two
+// buffers (168 VGPRs, no spills) and runs about 7 % faster that way; the
+// others keep three buffers at two waves per SIMD (at three waves they spill,
+// and without the third buffer they ran slower).
+template <int G, int WAVES, bool LM>
+struct HistShape {
+  static constexpr bool kThreeWaves = G == 128 && WAVES == 2 && !LM;
+  static constexpr int BUF = kThreeWaves ? 2 : (LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS);
+  static constexpr int MINW = kThreeWaves ? 3 : (LM ? OSCAR_HIST_MIN_WAVES_LM : OSCAR_HIST_MIN_WAVES);
+};
+
 template <int G, int WAVES, bool LM>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int BUF = LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS;
-  constexpr int MINW = OSCAR_HIST_MIN_WAVES;
+  constexpr int BUF = HistShape<G, WAVES, LM>::BUF;
+  constexpr int MINW = HistShape<G, WAVES, LM>::MINW;
   const oscar_dims& d = *a.dims;
   MfmaParams p;
   p.pages = a.cache->pages;
@@ -616,6 +659,22 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int hist_default_target(const oscar_dims& d) {
+  // the workgroups the matrix-core kernel for these dims keeps resident:
+  // SIMDs x waves per SIMD / waves per workgroup
+  const bool two = d.num_q_heads / d.num_kv_heads > 4;
+  const bool lm = d.codebook == OSCAR_CODEBOOK_LLOYD_MAX;
+  int waves;
+  if (d.group_size == 128) {
+    if (lm) waves = two ? HistShape<128, 2, true>::MINW : HistShape<128, 1, true>::MINW;
+    else waves = two ? HistShape<128, 2, false>::MINW : HistShape<128, 1, false>::MINW;
+  } else {
+    if (lm) waves = two ? HistShape<64, 2, true>::MINW : HistShape<64, 1, true>::MINW;
+    else waves = two ? HistShape<64, 2, false>::MINW : HistShape<64, 1, false>::MINW;
+  }
+  return kSimds * waves / (two ? 2 : 1);
+}
 
 bool hist_mfma_supported(const oscar_dims& d) {
   const int g = d.num_q_heads / d.num_kv_heads;

@@ -17,9 +17,12 @@ constexpr int kBf16Parts = 5;
 constexpr int kMaxSplits = 251;
 // Smallest history split, in pages.
 constexpr int kMinSplitPages = 8;
-// History workgroups the split schedule aims for by default (halved for
-// query groups wider than four heads, whose workgroups take two waves):
-// about what the chip keeps resident, so the splits run in one round.
+// SIMDs of the chip (256 compute units x 4); the history split schedule aims
+// by default for the workgroups the matrix-core history kernel keeps
+// resident on them (hist_default_target), so the splits run in one round.
+constexpr int kSimds = 1024;
+// Default target of the all-bf16 baseline (two one-wave workgroups per
+// SIMD; halved for query groups wider than four heads).
 constexpr int kDefaultTargetWg = 2048;
 // Largest settable target (bounds the workspace).
 constexpr int kMaxTargetWg = 8192;
@@ -112,6 +115,7 @@ hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_hist_valu(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s);
 bool hist_mfma_supported(const oscar_dims& d);
+int hist_default_target(const oscar_dims& d);
 hipError_t launch_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,

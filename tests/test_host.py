@@ -43,8 +43,12 @@ def test_workspace_and_splits():
     assert ok.oscar_history_splits(d, 32, 1000) == s        # lengths decide on the device
     # partials for 8192 / 8 + B history splits and five bf16 chunks per head
     assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= (1056 * 32 + 32 * 32 * 5) * 129 * 4
+    # 8-wide groups take two-wave workgroups: three waves per SIMD at G = 128
+    # (1536 workgroups), two at G = 64 and with the Lloyd-Max codebook (1024)
     gqa8 = ok.make_dims(64, 8, 128)
-    assert ok.oscar_history_splits(gqa8, 4, 1000) == 128 + 4  # 1024 workgroups for 8-wide groups
+    assert ok.oscar_history_splits(gqa8, 4, 1000) == 192 + 4
+    assert ok.oscar_history_splits(ok.make_dims(64, 8, 64), 4, 1000) == 128 + 4
+    assert ok.oscar_history_splits(ok.make_dims(64, 8, 128, codebook=ok.CODEBOOK_LLOYD_MAX), 4, 1000) == 128 + 4
     prev = ok.oscar_set_history_target(64)
     try:
         assert ok.oscar_history_splits(d, 32, 100_000) == 8 + 32
