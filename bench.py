@@ -153,7 +153,9 @@ def pct(xs, q):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0: the workload's own count, 100 for b1-100k and 200 for "
+                         "b32-ragged-gqa8, else 20)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b32-100k-g128", choices=sorted(workloads()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
@@ -182,7 +184,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     w = workloads()[args.workload]()
-    steps, warmup = args.steps, args.warmup
+    steps, warmup = args.steps or (w.steps if w.steps > 1 else 20), args.warmup
     total = steps + warmup
     n_layers = args.layers or default_layers(args.workload)
     appends = -(-total // n_layers)          # tokens each layer cache receives
