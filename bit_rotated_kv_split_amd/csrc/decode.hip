@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(256)
 qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int hq, int hkv, int G,
             float* __restrict__ qrot, float* __restrict__ qsum, uint8_t* __restrict__ qpack,
             const int32_t* __restrict__ seq_lens, int batch, int target, int32_t* __restrict__ sched,
-            int32_t* __restrict__ req, DemoteStep dm) {
+            int32_t* __restrict__ req, float lm_ratio, DemoteStep dm) {
   // Row 0 of the grid (dispatched first) holds the split scheduler; rows
   // 1 .. B rotate the queries of request blockIdx.y - 1; rows B+1 .. 2B, when
   // launched, demote the step's oldest recent token of request
@@ -96,7 +96,7 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     }
     if (lane == 0) {
       float* sc = reinterpret_cast<float*>(qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes +
-                                           kQPackOperandBytes);
+                                           kQPackScaleOffset);
       sc[h] = mx > 0.f ? mx / kQFixMax : 0.f;
     }
   }
@@ -107,34 +107,40 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   // 2-bit code masked in place, i.e. multiplied by 4^j for j < 3, so the
   // operand holds q / 4^j for those slots (rounded on its own, coarser grid).
   uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
-  uint32_t* qpw = reinterpret_cast<uint32_t*>(qp);
-  for (int widx = tid; widx < 2 * 4 * kQPackRows * 4; widx += 256) {
-    const int j = widx & 3;                     // dword j = bytes 4j .. 4j+3 of the row
-    const int row = (widx >> 2) & (kQPackRows - 1);
-    const int kg = (widx >> 7) & 3;
-    const int hf = widx >> 9;
-    const int h = row >> 2, digit = row & 3;
-    uint32_t word = 0;
-    if (h < GQ) {
-      const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : 1.f);
+  // the second operand (Lloyd-Max codebook only) holds q * lm_ratio on the
+  // same fixed-point grid, so both code planes accumulate into one result
+  const int n_ops = lm_ratio != 0.f ? 2 : 1;
+  for (int op = 0; op < n_ops; ++op) {
+    uint32_t* qpw = reinterpret_cast<uint32_t*>(qp + op * kQPackOperandBytes);
+    const float mul = op == 0 ? 1.f : lm_ratio;
+    for (int widx = tid; widx < 2 * 4 * kQPackRows * 4; widx += 256) {
+      const int j = widx & 3;                     // dword j = bytes 4j .. 4j+3 of the row
+      const int row = (widx >> 2) & (kQPackRows - 1);
+      const int kg = (widx >> 7) & 3;
+      const int hf = widx >> 9;
+      const int h = row >> 2, digit = row & 3;
+      uint32_t word = 0;
+      if (h < GQ) {
+        const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : 1.f);
 #pragma unroll
-      for (int b2 = 0; b2 < 4; ++b2) {
-        const int ch = 16 * (4 * hf + kg) + 4 * b2 + j;
-        const int qi = static_cast<int>(rintf(qr[h][ch] * qinv[h] * slot));
-        const int d0 = ((qi + 128) & 255) - 128;
-        const int q1 = (qi - d0) >> 8;
-        const int d1 = ((q1 + 128) & 255) - 128;
-        const int q2 = (q1 - d1) >> 8;
-        const int d2 = ((q2 + 128) & 255) - 128;
-        const int d3 = (q2 - d2) >> 8;
-        const int dv = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
-        word |= static_cast<uint32_t>(dv & 255) << (8 * b2);
+        for (int b2 = 0; b2 < 4; ++b2) {
+          const int ch = 16 * (4 * hf + kg) + 4 * b2 + j;
+          const int qi = static_cast<int>(rintf(qr[h][ch] * mul * qinv[h] * slot));
+          const int d0 = ((qi + 128) & 255) - 128;
+          const int q1 = (qi - d0) >> 8;
+          const int d1 = ((q1 + 128) & 255) - 128;
+          const int q2 = (q1 - d1) >> 8;
+          const int d2 = ((q2 + 128) & 255) - 128;
+          const int d3 = (q2 - d2) >> 8;
+          const int dv = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
+          word |= static_cast<uint32_t>(dv & 255) << (8 * b2);
+        }
       }
+      qpw[widx] = word;
     }
-    qpw[widx] = word;
   }
   if (tid >= GQ && tid < 8) {
-    float* sc = reinterpret_cast<float*>(qp + kQPackOperandBytes);
+    float* sc = reinterpret_cast<float*>(qp + kQPackScaleOffset);
     sc[tid] = 0.f;
   }
 }
@@ -574,6 +580,15 @@ hipError_t dispatch_gq(int gq, Args... args) {
   }
 }
 
+// Weight ratio of the Lloyd-Max high-bit plane to the code plane in the
+// matrix-core kernel ((3 lo - hi) / 2 over hi - lo); 0 for the uniform
+// codebook (no second operand).
+inline float lm_ratio(const oscar_dims& d) {
+  if (d.codebook != OSCAR_CODEBOOK_LLOYD_MAX) return 0.f;
+  const Codebook* c = codebook_of(d.codebook);
+  return (3.f * c->lev[2] - c->lev[3]) * 0.5f / (c->lev[3] - c->lev[2]);
+}
+
 template <int GQ>
 struct QrotRun {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
@@ -585,7 +600,7 @@ struct QrotRun {
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
         a.ws + a.lay.off_qpack, a.cache->seq_lens, batch, a.lay.target,
         reinterpret_cast<int32_t*>(a.ws + a.lay.off_sched), reinterpret_cast<int32_t*>(a.ws + a.lay.off_req),
-        a.demote != nullptr ? *a.demote : DemoteStep{});
+        lm_ratio(d), a.demote != nullptr ? *a.demote : DemoteStep{});
     return hipGetLastError();
   }
 };

@@ -37,9 +37,11 @@
 // The Lloyd-Max codebook (levels -hi, -lo, lo, hi for codes 0..3) splits a
 // code c = 2 b1 + b0 into bit planes: level(c) = -hi + (hi - lo) c +
 // (3 lo - hi) b1.  The c plane is the uniform kernel's operand; the b1 plane
-// is the same masked word ANDed down to its high bits (2 b1 4^j), one more
-// matrix-core product against the same A operand.  The -hi term joins the
-// zero point (zero - hi * scale per token and group).
+// is the same masked word ANDed down to its high bits (2 b1 4^j).  For keys
+// the plane goes against a second query operand holding q (3 lo - hi) /
+// (2 (hi - lo)), accumulating into the same result; for values it has its
+// own accumulators against the same P' operand.  The -hi term joins the zero
+// point (zero - hi * scale per token and group).
 //
 // One wave per workgroup; the workgroup owns (history split, KV head,
 // request), and five more workgroups per (KV head, request) run the bf16
@@ -225,6 +227,7 @@ template <int NHB, int G>
 struct WaveState {
   static constexpr int NG = kDim / G;
   v4i qa[NHB][2];          // query digit operands
+  v4i qb[NHB][2];          // Lloyd-Max only: the same for q times the high-bit weight ratio
   float qs[NHB];           // query fixed-point unit of this lane's head
   float qz[NHB][NG];       // per-group query sums (zero-point term of the score)
   float m_ref[NHB];        // reference maximum (log2 units)
@@ -321,30 +324,30 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       const v4i zero = {0, 0, 0, 0};
       float s;
       if constexpr (LM) {
-        // level sum = ka * (q . c) + kb * (q . 2 b1); zero - hi * scale for the rest
+        // level sum = ka * (q . c + (kb / ka) * q . 2 b1): the second operand
+        // carries kb / ka, so both planes accumulate into one result, and qs
+        // carries ka; zero - hi * scale takes the rest
         const v4i h0 = high_bits(b0), h1 = high_bits(b1);
         if constexpr (NG == 1) {
           v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
           d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
-          v4i e = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], h0, zero, 0, 0, 0);
-          e = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], h1, e, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][0], h0, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][1], h1, d, 0, 0, 0);
           const uint32_t sz = cur.ksz[m];
           const float ks = __uint_as_float(sz << 16);
           const float kz = __builtin_fmaf(-lm_hi, ks, __uint_as_float(sz & 0xFFFF0000u));
-          s = __builtin_fmaf(ks * st.qs[hb], __builtin_fmaf(ka, q_digits(d), kb * q_digits(e)), kz * st.qz[hb][0]);
+          s = __builtin_fmaf(ks * st.qs[hb], q_digits(d), kz * st.qz[hb][0]);
         } else {
-          const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
-          const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
-          const v4i e0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], h0, zero, 0, 0, 0);
-          const v4i e1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], h1, zero, 0, 0, 0);
+          v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+          v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
+          d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][0], h0, d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][1], h1, d1, 0, 0, 0);
           const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
           const float ks0 = __uint_as_float(s0 << 16), ks1 = __uint_as_float(s1 << 16);
           const float kz0 = __builtin_fmaf(-lm_hi, ks0, __uint_as_float(s0 & 0xFFFF0000u));
           const float kz1 = __builtin_fmaf(-lm_hi, ks1, __uint_as_float(s1 & 0xFFFF0000u));
-          s = __builtin_fmaf(ks0 * st.qs[hb], __builtin_fmaf(ka, q_digits(d0), kb * q_digits(e0)),
-                             kz0 * st.qz[hb][0]) +
-              __builtin_fmaf(ks1 * st.qs[hb], __builtin_fmaf(ka, q_digits(d1), kb * q_digits(e1)),
-                             kz1 * st.qz[hb][1]);
+          s = __builtin_fmaf(ks0 * st.qs[hb], q_digits(d0), kz0 * st.qz[hb][0]) +
+              __builtin_fmaf(ks1 * st.qs[hb], q_digits(d1), kz1 * st.qz[hb][1]);
         }
       } else if constexpr (NG == 1) {
         v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
@@ -504,17 +507,20 @@ hist_mfma_kernel(MfmaParams a) {
 
   WaveState<NHB, G> st;
   const uint8_t* qp = a.qpack + (static_cast<size_t>(b) * a.hkv + kvh) * kQPackBytes;
-  const float* qscale = reinterpret_cast<const float*>(qp + kQPackOperandBytes);
+  const float* qscale = reinterpret_cast<const float*>(qp + kQPackScaleOffset);
   const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * a.gq;
   bool head_ok[NHB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + ((hf * 4 + lg) * kQPackRows + (wave + hb) * 16 + n) * 16);
+    for (int hf = 0; hf < 2; ++hf) {
+      const size_t off = ((hf * 4 + lg) * kQPackRows + (wave + hb) * 16 + n) * 16;
+      st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + off);
+      if constexpr (LM) st.qb[hb][hf] = *reinterpret_cast<const v4i*>(qp + kQPackOperandBytes + off);
+    }
     const int h = 4 * (wave + hb) + lg;
     head_ok[hb] = h < a.gq;
-    st.qs[hb] = qscale[h];
+    st.qs[hb] = LM ? qscale[h] * a.lm_ka : qscale[h];
     st.m_ref[hb] = -INFINITY;
     st.ls[hb] = 0.f;
     st.since_fold = 0;

@@ -51,12 +51,14 @@ struct WsLayout {
   size_t total = 0;
 };
 
-// Matrix-core query operand of one (request, KV head): for each channel half
-// (64 channels) and lane group, 32 rows x 16 int8 limb bytes, then per-head
-// dequantization scales.
+// Matrix-core query operands of one (request, KV head): for each channel
+// half (64 channels) and lane group, 32 rows x 16 int8 limb bytes; then the
+// same for the query times the Lloyd-Max high-bit weight ratio (written for
+// that codebook only); then per-head dequantization scales.
 constexpr int kQPackRows = 32;
 constexpr size_t kQPackOperandBytes = 2 * 4 * kQPackRows * 16;  // 4096
-constexpr size_t kQPackBytes = kQPackOperandBytes + 256;
+constexpr size_t kQPackScaleOffset = 2 * kQPackOperandBytes;
+constexpr size_t kQPackBytes = kQPackScaleOffset + 256;
 
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len);
 
