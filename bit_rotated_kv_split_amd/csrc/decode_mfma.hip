@@ -116,10 +116,13 @@ __device__ __forceinline__ v4i high_bits(const v4i& r) {
   return h;
 }
 
-// value of the signed base-256 digit rows of q . code
+// value of the signed base-256 digit rows of q . code: each row sums at most
+// four products of 64 digits (|digit| <= 128) and bytes (<= 48), so both
+// two-row integer sums fit in int32
 __device__ __forceinline__ float q_digits(const v4i& d) {
-  const int lo = d.x + (d.y << 8);   // |d.x|, |d.y| <= 128 * 128 * 48: fits
-  return static_cast<float>(lo) + 65536.f * static_cast<float>(d.z) + 16777216.f * static_cast<float>(d.w);
+  const int lo = d.x + (d.y << 8);
+  const int hi = d.z + (d.w << 8);
+  return __builtin_fmaf(65536.f, static_cast<float>(hi), static_cast<float>(lo));
 }
 
 // value of the signed base-256 digit rows of P' . code (accumulated)
