@@ -1,0 +1,54 @@
+"""bench.py's host-side pieces: algorithmic byte accounting, workloads and
+the one-GPU guard (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_history_unit_bytes():
+    # 2 x 32 code bytes + 2 x (128 / G) bf16 (scale, zero) pairs per token and KV head
+    assert bench.hist_unit_bytes(128) == 72
+    assert bench.hist_unit_bytes(64) == 80
+    assert bench.hist_unit_bytes(32) == 96
+
+
+def test_step_bytes_by_hand():
+    lens = np.array([100, 320, 1000])
+    hkv, hq, g = 2, 8, 128
+    hist, total = bench.step_bytes(lens, hkv, hq, g)
+    n_hist = 0 + 0 + 680
+    assert hist == n_hist * hkv * 72
+    bf16 = (100 + 320 + 320) * hkv * 512
+    qo = 3 * hq * 128 * 6
+    demoted = 1 * hkv * (512 + 72)          # only the request past 320 tokens demotes
+    appended = 3 * hkv * 512
+    assert total == hist + bf16 + qo + demoted + appended
+    assert bench.bf16_bytes(lens, hkv) == bf16
+
+
+def test_workloads_and_default_steps():
+    wl = bench.workloads()
+    assert {"b32-100k-g128", "b32-100k-g64", "b32-100k-g128-lloyd", "b1-100k", "b16-128k",
+            "b32-ragged-gqa8"} <= set(wl)
+    w = wl["b32-100k-g128"]()
+    assert (w.batch, w.num_q_heads, w.num_kv_heads, w.group_size) == (32, 32, 8, 128)
+    assert set(w.seq_lens) == {100_000} and w.paged and w.codebook == 0
+    assert wl["b32-100k-g128-lloyd"]().codebook == 1
+    assert wl["b1-100k"]().steps == 100
+    r = wl["b32-ragged-gqa8"]()
+    assert r.steps == 200 and r.num_q_heads == 64 and r.shared_prefix
+    assert min(r.seq_lens) >= 4096 and max(r.seq_lens) <= 131072
+    assert bench.default_layers("b1-100k") == 10 and bench.default_layers("b32-100k-g128") == 1
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
