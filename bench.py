@@ -90,22 +90,36 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 10.0):
+def _host_cpu():
+    """CPU model name and logical core count of this host."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 10.0,
+                 single_budget_s: float = 4.0):
     """Time the oracle (as it stands) on whole requests of the same workload
     at their final length, request 0 first, until about budget_s seconds of
-    oracle work; scaled to GB/s of the same algorithmic bytes.  The sample's
-    tokens come from the GPU twin of the seeded generator (bit-identical to
-    synth.gen; not timed)."""
+    oracle work with numpy's default threads, then again single-threaded
+    (BLAS limited to one thread) for about single_budget_s; each scaled to
+    GB/s of the same algorithmic bytes.  The sample's tokens come from the GPU
+    twin of the seeded generator (bit-identical to synth.gen; not timed)."""
     import torch
     from oracle import oscar as O
     from synth import gpu as synth_gpu
     w = model.w
     g = w.gqa
     stream = torch.cuda.current_stream().cuda_stream
-    spent = 0.0
-    done_bytes = 0
-    reqs = 0
-    for b in range(w.batch):
+    codebook = ("uniform", "lloyd-max")[w.codebook]
+
+    def request_inputs(b):
         L = int(lens[b])
         host = {}
         for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
@@ -117,26 +131,41 @@ def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 
             torch.cuda.synchronize()
             host[which] = buf.cpu().numpy().view(np.uint16)
             del buf
-        q = model.queries(0, w.batch)[b][: n_heads * g]
-        t0 = time.perf_counter()
-        O.request_attention(q, host["k"], host["v"], cal_host["r_k32"][:n_heads], cal_host["r_v32"][:n_heads],
-                            cal_host["clip_k"][:n_heads], cal_host["clip_v"][:n_heads], w.group_size,
-                            ("uniform", "lloyd-max")[w.codebook])
-        spent += time.perf_counter() - t0
-        done_bytes += step_bytes(np.array([L]), n_heads, n_heads * g, w.group_size)[1]
-        reqs += 1
-        if spent >= budget_s:
-            break
+        return L, host
+
+    def run(budget, heads):
+        spent, done_bytes, reqs = 0.0, 0, 0
+        for b in range(w.batch):
+            L, host = request_inputs(b)
+            q = model.queries(0, w.batch)[b][: heads * g]
+            t0 = time.perf_counter()
+            O.request_attention(q, host["k"][:, :heads], host["v"][:, :heads], cal_host["r_k32"][:heads],
+                                cal_host["r_v32"][:heads], cal_host["clip_k"][:heads], cal_host["clip_v"][:heads],
+                                w.group_size, codebook)
+            spent += time.perf_counter() - t0
+            done_bytes += step_bytes(np.array([L]), heads, heads * g, w.group_size)[1]
+            reqs += 1
+            if spent >= budget:
+                break
+        return spent, done_bytes, reqs
+
+    spent, done_bytes, reqs = run(budget_s, n_heads)
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+        with threadpool_limits(limits=1):
+            s1, b1, r1 = run(single_budget_s, 1)
+        single = {"value": round(b1 / s1 / 1e9, 4), "seconds": round(s1, 3),
+                  "sample": f"requests 0..{r1 - 1}, KV head 0 only, one thread"}
     except Exception:
-        cores = 1
+        cores, single = 1, None
+    cpu_model, nproc = _host_cpu()
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "seconds": round(spent, 3),
             "sample": f"requests 0..{reqs - 1} of {w.batch}, {n_heads} of {w.num_kv_heads} KV heads each, "
                       f"at their final lengths: the oracle demotes each history and attends in float64 "
-                      f"(numpy); {done_bytes / 1e9:.3f} GB of the step's algorithmic bytes"}
+                      f"(numpy); {done_bytes / 1e9:.3f} GB of the step's algorithmic bytes",
+            "single_thread": single, "host_cpu": cpu_model, "host_logical_cores": nproc}
 
 
 def default_layers(workload: str) -> int:
@@ -156,7 +185,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (0: the workload's own count, 100 for b1-100k and 200 for "
                          "b32-ragged-gqa8, else 20)")
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="b32-100k-g128", choices=sorted(workloads()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--layers", type=int, default=0,

@@ -488,6 +488,25 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
 #pragma unroll
   for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  // partials of the first 16 splits and the bf16 chunks, loaded together
+  // with the log-sum-exps (they do not depend on the weights), so the kernel
+  // waits on memory once for all three
+  constexpr int kItems = (GQ * kDim + 255) / 256;   // (head, channel) items per thread
+  constexpr int kEarly = 16;
+  const size_t hstride = static_cast<size_t>(a.hq) * kDim;
+  float vh[kItems][kEarly], vb[kItems][kBf16Parts];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int x = tid + 256 * it;
+    const int h = x / kDim, k = x % kDim;
+    const bool live = x < GQ * kDim;
+    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u) vh[it][u] = live && u < count ? hb[static_cast<size_t>(u) * hstride] : 0.f;
+    const float* bb = a.bo + ((bhead0 + h) * kBf16Parts) * kDim + k;
+#pragma unroll
+    for (int c = 0; c < kBf16Parts; ++c) vb[it][c] = live ? bb[c * kDim] : 0.f;
+  }
   for (int x = tid; x < GQ * count; x += 256) {
     const int h = x / count, sp = x % count;
     wh[h][sp] = a.hlse[static_cast<size_t>(first + sp) * a.hq + h0 + h];
@@ -515,13 +534,19 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
     }
   }
   __syncthreads();
-  // weighted sums of the partials, up to 16 loads in flight per thread
-  for (int x = tid; x < GQ * kDim; x += 256) {
+  // weighted sums of the partials: the first 16 splits from registers, the
+  // rest (long single requests) 16 loads at a time
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int x = tid + 256 * it;
+    if (x >= GQ * kDim) break;
     const int h = x / kDim, k = x % kDim;
-    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
-    const size_t hstride = static_cast<size_t>(a.hq) * kDim;
     float oh = 0.f;
-    for (int s0 = 0; s0 < count; s0 += 16) {
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u)
+      if (u < count) oh = __builtin_fmaf(wh[h][u], vh[it][u], oh);
+    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
+    for (int s0 = kEarly; s0 < count; s0 += 16) {
       float v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) v[u] = s0 + u < count ? hb[static_cast<size_t>(s0 + u) * hstride] : 0.f;
@@ -529,10 +554,9 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
       for (int u = 0; u < 16; ++u)
         if (s0 + u < count) oh = __builtin_fmaf(wh[h][s0 + u], v[u], oh);
     }
-    const float* bb = a.bo + ((bhead0 + h) * kBf16Parts) * kDim + k;
     float ob = 0.f;
 #pragma unroll
-    for (int c = 0; c < kBf16Parts; ++c) ob = __builtin_fmaf(wb[h][c], bb[c * kDim], ob);
+    for (int c = 0; c < kBf16Parts; ++c) ob = __builtin_fmaf(wb[h][c], vb[it][c], ob);
     orot[h][k] = oh;
     obf[h][k] = ob;
   }
