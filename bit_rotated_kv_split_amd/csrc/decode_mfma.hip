@@ -9,7 +9,7 @@
 // exact integer products here:
 //   q . code   A = the rotated query as 4-digit signed base-256 fixed point
 //              (rows = head x digit), B = 2-bit codes as int8;
-//   P' . code  A = p * value-scale per token as 4 unsigned base-128 digits
+//   P' . code  A = p * value-scale per token as 4 signed base-256 digits
 //              (rows = head x digit), B = value codes as int8.
 // A word of sixteen 2-bit codes gives the four int8 operand registers as
 // w & 0x03030303 << 2j (j = 0, 1, 2: the code times 4^j, masked in place)
@@ -43,13 +43,15 @@
 // own accumulators against the same P' operand.  The -hi term joins the zero
 // point (zero - hi * scale per token and group).
 //
-// One wave per workgroup; the workgroup owns (history split, KV head,
-// request), and five more workgroups per (KV head, request) run the bf16
-// sink/recent chunks (decode_bf16.h) alongside the history splits.  Per 64-token page a lane loads 4 x 16 B of codes and the
-// scale/zero entries of its tokens (the page layout puts each lane's MFMA
-// operands in one 16-byte load); the loads of pages p+1 and p+2 are in
-// flight while page p is processed (three register buffers, no copies).  Query heads are
-// handled in blocks of four (16 MFMA rows = 4 heads x 4 digit rows).
+// A workgroup owns (history split, KV head, request) with one wave per four
+// query heads (two waves for eight-head groups), and five more workgroups
+// per (KV head, request) run the bf16 sink/recent chunks (decode_bf16.h)
+// alongside the history splits.  Per 64-token page a lane loads 4 x 16 B of
+// codes and the scale/zero entries of its tokens (the page layout puts each
+// lane's MFMA operands in one 16-byte load); the loads of the next BUF-1
+// pages are in flight while a page is processed (register buffers, no
+// copies; BUF per instantiation in HistShape).  Query heads are handled in
+// blocks of four (16 MFMA rows = 4 heads x 4 digit rows).
 #include <math.h>
 
 #include <hip/hip_ext.h>
@@ -70,11 +72,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #endif
 #ifndef OSCAR_HIST_MIN_WAVES
 #define OSCAR_HIST_MIN_WAVES 2
-#endif
-// order of a page step: load the page BUF-1 ahead, then process (1), or
-// process, then reload the freed buffer with the page BUF ahead (0)
-#ifndef OSCAR_HIST_LOAD_FIRST
-#define OSCAR_HIST_LOAD_FIRST 1
 #endif
 // the Lloyd-Max form holds a second set of value accumulators
 #ifndef OSCAR_HIST_BUFFERS_LM
@@ -570,7 +567,6 @@ hist_mfma_kernel(MfmaParams a) {
   if (p0 < p1) {   // uniform
     const int p_last = p1 - 1;
     PageRegs<G> buf[BUF];
-#if OSCAR_HIST_LOAD_FIRST
 #pragma unroll
     for (int k = 0; k < BUF - 1; ++k) load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
     for (int p = p0; p < p1; p += BUF) {
@@ -581,18 +577,6 @@ hist_mfma_kernel(MfmaParams a) {
         if (p + k + 1 >= p1) break;
       }
     }
-#else
-#pragma unroll
-    for (int k = 0; k < BUF; ++k) load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
-    for (int p = p0; p < p1; p += BUF) {
-#pragma unroll
-      for (int k = 0; k < BUF; ++k) {
-        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
-        if (p + k + 1 >= p1) break;
-        load_page<G>(buf[k], page_ptr(min(p + k + BUF, p_last)), lane);
-      }
-    }
-#endif
   }
 
   // ---- partial output of this split (rotated value domain)
