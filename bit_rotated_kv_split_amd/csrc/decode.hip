@@ -346,12 +346,13 @@ __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
 // merge_group_kernel: workgroup = (KV head, request), sharing R_V across the
 // group's heads.
 //
-// merge_head_kernel (256 threads): the request's
-// history splits (from the schedule) are merged in the rotated value domain,
-// rotated back by R_V^T, and merged with the five bf16 partials.  Thread t
-// weighs split t; the weighted sum over splits runs on both halves of the
-// workgroup (channel t % 128, every other split); the rotation gives each
-// thread half a row of R_V, loaded before anything else.
+// merge_head_kernel (512 threads): the request's history splits (from the
+// schedule) are merged in the rotated value domain, rotated back by R_V^T,
+// and merged with the five bf16 partials.  Thread t weighs split t; the
+// weighted sum over splits runs on four threads per channel (channel
+// t % 128, every fourth split), so a long request's up to 251 splits take
+// four rounds of loads; threads 0..255 hold half a row of R_V each, loaded
+// before anything else.
 struct MergeParams {
   const float* ho;        // [slots][Hq][128]
   const float* hlse;      // [slots][Hq]
@@ -365,42 +366,54 @@ struct MergeParams {
   int32_t gq;
 };
 
-__device__ __forceinline__ float block_max_f(float v, float* red) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
+constexpr int kMergeHeadThreads = 512;
+static_assert(kMaxSplits < kMergeHeadThreads, "one thread weighs each split");
 
-__device__ __forceinline__ float block_sum_f(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-__global__ void __launch_bounds__(256) merge_head_kernel(MergeParams a) {
+__global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergeParams a) {
+  constexpr int kWaves = kMergeHeadThreads / 64;
+  constexpr int kPar = kMergeHeadThreads / kDim;   // threads per channel
   const int head = blockIdx.x, b = blockIdx.y, kvh = head / a.gq;
   const int tid = threadIdx.x;
-  __shared__ float red[4];
+  __shared__ float red[kWaves];
   __shared__ float w[kMaxSplits + 1];
-  __shared__ float ypart[2][kDim];
+  __shared__ float ypart[kPar][kDim];
   __shared__ float y[kDim];
+  auto bmax = [&](float v) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
+    return r;
+  };
+  auto bsum = [&](float v) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r += red[i];
+    return r;
+  };
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
   const size_t bh = static_cast<size_t>(b) * a.hq + head;
-  // row i of R_V, columns 64 kh .. 64 kh + 63
-  const int i = tid >> 1, kh = tid & 1;
+  // threads 0..255: row i of R_V, columns 64 kh .. 64 kh + 63
+  const int i = (tid >> 1) & (kDim - 1), kh = tid & 1;
   float4 rr[16];
-  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+  if (tid < 2 * kDim) {
+    const float4* rrow =
+        reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
-  // history split weights e^{lse - M} / sum (count <= kMaxSplits < 256)
+    for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  }
+  // history split weights e^{lse - M} / sum (count <= kMaxSplits < threads)
   const float l = tid < count ? a.hlse[static_cast<size_t>(first + tid) * a.hq + head] : -INFINITY;
-  const float mh = block_max_f(l, red);
+  const float mh = bmax(l);
   const float e = mh == -INFINITY || tid >= count ? 0.f : expf(l - mh);
-  const float dh = block_sum_f(e, red);
+  const float dh = bsum(e);
   if (tid < count) w[tid] = dh > 0.f ? e / dh : 0.f;
   const float lse_h = dh > 0.f ? mh + logf(dh) : -INFINITY;
   // bf16 partial weights (every thread computes the five)
@@ -415,30 +428,37 @@ __global__ void __launch_bounds__(256) merge_head_kernel(MergeParams a) {
   for (int c = 0; c < kBf16Parts; ++c) db += lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb);
   const float lse_b = mb + logf(db);   // the sink chunk always holds a token
   __syncthreads();
-  // weighted sum over the splits: channel k, splits of parity par
+  // weighted sum over the splits: channel k, the splits congruent to par
+  // modulo kPar, 16 loads in flight
   {
-    const int k = tid & (kDim - 1), par = tid >> 7;
+    const int k = tid & (kDim - 1), par = tid / kDim;
     const float* hp = a.ho + (static_cast<size_t>(first) * a.hq + head) * kDim + k;
     const size_t stride = static_cast<size_t>(a.hq) * kDim;
     float acc = 0.f;
-    for (int s0 = par; s0 < count; s0 += 32) {
+    for (int s0 = par; s0 < count; s0 += 16 * kPar) {
       float v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int sp = s0 + 2 * u;
+        const int sp = s0 + kPar * u;
         v[u] = sp < count ? hp[static_cast<size_t>(sp) * stride] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int sp = s0 + 2 * u;
+        const int sp = s0 + kPar * u;
         if (sp < count) acc = __builtin_fmaf(w[sp], v[u], acc);
       }
     }
     ypart[par][k] = acc;
   }
   __syncthreads();
-  if (tid < kDim) y[tid] = ypart[0][tid] + ypart[1][tid];
+  if (tid < kDim) {
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < kPar; ++p) t += ypart[p][tid];
+    y[tid] = t;
+  }
   __syncthreads();
+  if (tid >= 2 * kDim) return;   // whole waves
   // back to the model domain: x_i = sum_k y_k R_V[i][k]
   float acc = 0.f;
 #pragma unroll
@@ -726,7 +746,7 @@ hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t 
   p.hq = d.num_q_heads;
   p.gq = d.num_q_heads / d.num_kv_heads;
   if (static_cast<int64_t>(batch) * d.num_kv_heads < kMergeGroupMinWgs) {
-    merge_head_kernel<<<dim3(d.num_q_heads, batch), 256, 0, s>>>(p);
+    merge_head_kernel<<<dim3(d.num_q_heads, batch), kMergeHeadThreads, 0, s>>>(p);
     return hipGetLastError();
   }
   return dispatch_gq<MergeGroupRun>(p.gq, p, d.num_kv_heads, batch, s);
