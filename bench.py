@@ -40,6 +40,7 @@ def workloads():
     return {
         "b32-100k-g128": lambda: configs.qwen3_8b_b32(128),
         "b32-100k-g64": lambda: configs.qwen3_8b_b32(64),
+        "b32-100k-g32": lambda: configs.qwen3_8b_b32(32),
         "b32-100k-g128-lloyd": lambda: dataclasses.replace(configs.qwen3_8b_b32(128),
                                                            name="qwen3-8b-b32-100k-lloyd-max", codebook=1),
         "b1-100k": lambda: configs.qwen3_8b_b1(),

@@ -80,6 +80,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_HIST_MIN_WAVES_LM
 #define OSCAR_HIST_MIN_WAVES_LM OSCAR_HIST_MIN_WAVES
 #endif
+// G = 32 pages carry four scale/zero pairs per token and K/V (48 VGPRs a
+// buffer); its Lloyd-Max form keeps one buffer (two spill)
+#ifndef OSCAR_HIST_BUFFERS_32
+#define OSCAR_HIST_BUFFERS_32 2
+#endif
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
@@ -228,6 +233,10 @@ struct WaveState {
   static constexpr int NG = kDim / G;
   v4i qa[NHB][2];          // query digit operands
   v4i qb[NHB][2];          // Lloyd-Max only: the same for q times the high-bit weight ratio
+  // G = 32 only: the operands of each half masked to one of its two groups
+  // (lane groups 2 sub, 2 sub + 1 hold the group's 32 channels)
+  v4i qam[NHB][2][2];
+  v4i qbm[NHB][2][2];
   float qs[NHB];           // query fixed-point unit of this lane's head
   float qz[NHB][NG];       // per-group query sums (zero-point term of the score)
   float m_ref[NHB];        // reference maximum (log2 units)
@@ -323,7 +332,28 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
     for (int hb = 0; hb < NHB; ++hb) {
       const v4i zero = {0, 0, 0, 0};
       float s;
-      if constexpr (LM) {
+      if constexpr (NG == 4) {
+        // two groups per half: one product per group against the operand
+        // masked to its channels (and, Lloyd-Max, the high-bit plane against
+        // the masked second operand, as below)
+        s = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const v4i& bc = hf ? b1 : b0;
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qam[hb][hf][sub], bc, zero, 0, 0, 0);
+            if constexpr (LM)
+              d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qbm[hb][hf][sub], high_bits(bc), d, 0, 0, 0);
+            const int gi = 2 * hf + sub;
+            const uint32_t sz = cur.ksz[m * NG + gi];
+            const float ks = __uint_as_float(sz << 16);
+            float kz = __uint_as_float(sz & 0xFFFF0000u);
+            if constexpr (LM) kz = __builtin_fmaf(-lm_hi, ks, kz);
+            s += __builtin_fmaf(ks * st.qs[hb], q_digits(d), kz * st.qz[hb][gi]);
+          }
+        }
+      } else if constexpr (LM) {
         // level sum = ka * (q . c + (kb / ka) * q . 2 b1): the second operand
         // carries kb / ka, so both planes accumulate into one result, and qs
         // carries ka; zero - hi * scale takes the rest
@@ -517,6 +547,14 @@ hist_mfma_kernel(MfmaParams a) {
       const size_t off = ((hf * 4 + lg) * kQPackRows + (wave + hb) * 16 + n) * 16;
       st.qa[hb][hf] = *reinterpret_cast<const v4i*>(qp + off);
       if constexpr (LM) st.qb[hb][hf] = *reinterpret_cast<const v4i*>(qp + kQPackOperandBytes + off);
+      if constexpr (NG == 4) {
+        const v4i z = {0, 0, 0, 0};
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          st.qam[hb][hf][sub] = (lg >> 1) == sub ? st.qa[hb][hf] : z;
+          if constexpr (LM) st.qbm[hb][hf][sub] = (lg >> 1) == sub ? st.qb[hb][hf] : z;
+        }
+      }
     }
     const int h = 4 * (wave + hb) + lg;
     head_ok[hb] = h < a.gq;
@@ -613,7 +651,8 @@ hist_mfma_kernel(MfmaParams a) {
 template <int G, int WAVES, bool LM>
 struct HistShape {
   static constexpr bool kThreeWaves = G == 128 && WAVES == 2 && !LM;
-  static constexpr int BUF = kThreeWaves ? 2 : (LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS);
+  static constexpr int BUF = G == 32 ? (LM ? 1 : OSCAR_HIST_BUFFERS_32) : kThreeWaves ? 2
+                                     : (LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS);
   static constexpr int MINW = kThreeWaves ? 3 : (LM ? OSCAR_HIST_MIN_WAVES_LM : OSCAR_HIST_MIN_WAVES);
 };
 
@@ -662,6 +701,9 @@ int hist_default_target(const oscar_dims& d) {
   if (d.group_size == 128) {
     if (lm) waves = two ? HistShape<128, 2, true>::MINW : HistShape<128, 1, true>::MINW;
     else waves = two ? HistShape<128, 2, false>::MINW : HistShape<128, 1, false>::MINW;
+  } else if (d.group_size == 32) {
+    if (lm) waves = two ? HistShape<32, 2, true>::MINW : HistShape<32, 1, true>::MINW;
+    else waves = two ? HistShape<32, 2, false>::MINW : HistShape<32, 1, false>::MINW;
   } else {
     if (lm) waves = two ? HistShape<64, 2, true>::MINW : HistShape<64, 1, true>::MINW;
     else waves = two ? HistShape<64, 2, false>::MINW : HistShape<64, 1, false>::MINW;
@@ -671,16 +713,18 @@ int hist_default_target(const oscar_dims& d) {
 
 bool hist_mfma_supported(const oscar_dims& d) {
   const int g = d.num_q_heads / d.num_kv_heads;
-  return (d.group_size == 64 || d.group_size == 128) && g >= 1 && g <= 8;
+  return (d.group_size == 32 || d.group_size == 64 || d.group_size == 128) && g >= 1 && g <= 8;
 }
 
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s) {
   const int g = a.dims->num_q_heads / a.dims->num_kv_heads;
   const bool two = g > 4;
   if (a.dims->codebook == OSCAR_CODEBOOK_LLOYD_MAX) {
+    if (a.dims->group_size == 32) return two ? launch_t<32, 2, true>(a, s) : launch_t<32, 1, true>(a, s);
     if (a.dims->group_size == 64) return two ? launch_t<64, 2, true>(a, s) : launch_t<64, 1, true>(a, s);
     return two ? launch_t<128, 2, true>(a, s) : launch_t<128, 1, true>(a, s);
   }
+  if (a.dims->group_size == 32) return two ? launch_t<32, 2, false>(a, s) : launch_t<32, 1, false>(a, s);
   if (a.dims->group_size == 64) return two ? launch_t<64, 2, false>(a, s) : launch_t<64, 1, false>(a, s);
   return two ? launch_t<128, 2, false>(a, s) : launch_t<128, 1, false>(a, s);
 }

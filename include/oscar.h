@@ -258,9 +258,9 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
                     float* clip_v, double* r_k_host, double* r_v_host, void* workspace,
                     size_t workspace_bytes, void* stream);
 
-/* Which history kernel oscar_decode_attn launches: 0 = default (MFMA where
- * available: group_size 64 or 128 with the uniform codebook), 1 =
- * vector-ALU kernel (every supported dims), 2 = matrix-core (MFMA) kernel.
+/* Which history kernel oscar_decode_attn launches: 0 = default (the
+ * matrix-core kernel), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
+ * Both cover every supported dims.
  * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
 int oscar_set_history_kernel(int kind);
 

@@ -380,13 +380,15 @@ def test_full_size_batch32_100k_lloyd_max_sampled():
 
 
 @pytest.mark.slow
-def test_full_size_batch32_100k_sampled():
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_full_size_batch32_100k_sampled(group):
     """The benchmark's workload at full size (32 requests x 100K tokens,
-    32 q / 8 kv heads, G = 128, paged) in its launch configuration (default
-    history kernel, max_seq_len 100K); sampled (request, KV head) groups
-    checked against the oracle, every output checked finite."""
+    32 q / 8 kv heads, paged; G = 128 and the G = 64 and 32 variants) in its
+    launch configuration (default history kernel, max_seq_len 100K); sampled
+    (request, KV head) groups checked against the oracle, every output
+    checked finite."""
     from gpu_helpers import oracle_request_heads
-    w = configs.qwen3_8b_b32(128)
+    w = configs.qwen3_8b_b32(group)
     layout, model, cal, rot, cache = setup(w)
     q_bits = model.queries(0, w.batch)
     q = W.queries_tensor(model, 0, w.batch)

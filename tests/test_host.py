@@ -172,19 +172,15 @@ def test_codebook_constants_equal_the_oracle():
 
 
 def test_history_kernel_choice_by_codebook_and_group():
-    lm = ok.CODEBOOK_LLOYD_MAX
-    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 128, codebook=lm)) == 2
-    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 64, codebook=lm)) == 2
-    d32 = ok.make_dims(32, 8, 32, codebook=lm)
-    assert ok.oscar_history_kernel_for(d32) == 1
-    prev = ok.oscar_set_history_kernel(2)
+    """The matrix-core kernel covers every supported group size and both
+    codebooks; the selector still forces the vector-ALU one."""
+    for g in (32, 64, 128):
+        for cb in (ok.CODEBOOK_UNIFORM, ok.CODEBOOK_LLOYD_MAX):
+            for hq in (8, 32, 64):
+                assert ok.oscar_history_kernel_for(ok.make_dims(hq, 8, g, codebook=cb)) == 2
+    prev = ok.oscar_set_history_kernel(1)
     try:
-        assert ok.oscar_history_kernel_for(d32) == -1
-        # refused before anything is enqueued (the pointers here are not real)
-        with pytest.raises(ok.OscarError) as e:
-            ok.oscar_decode_step(d32, _rot(), _cache(), 0x1000, 0x1000, 0x1000, 100, 0x1000, 1 << 30, 0x1000,
-                                 None, 0)
-        assert e.value.code == ok.OSCAR_EUNSUPPORTED
+        assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 32, codebook=ok.CODEBOOK_LLOYD_MAX)) == 1
     finally:
         ok.oscar_set_history_kernel(prev)
 
