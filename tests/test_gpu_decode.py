@@ -437,3 +437,20 @@ def test_full_size_ragged_shared_prefix_gqa8_sampled():
     for b, j in picks:
         ref = oracle_request_heads(model, layout, cal, q_bits[b], b, lens[b], [j])[j]
         assert_close(out[b, j * g:(j + 1) * g], ref[0], f"ragged b={b} L={lens[b]} kvh={j}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("codebook", [0, 1])
+def test_zero_query_gives_uniform_attention(kernel, codebook):
+    """A zero query scores every token 0: the output is the plain mean of the
+    (dequantized, un-rotated) values and the LSE is ln L, through the
+    matrix-core fixed point (zero digits, unit from the largest |q| = 0)
+    as well as the vector ALU."""
+    lens = [321, 700, 4000, 64]
+    w = small(f"zeroq{codebook}", 31, 8, 2, 64, lens, codebook=codebook)
+    layout, model, cal, rot, cache = setup(w)
+    q_bits = np.zeros((w.batch, w.num_q_heads, 128), dtype=np.uint16)
+    q = torch.zeros((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    out, lse = run_decode(cache, rot, q, int(layout.lens.max()), KERNELS[kernel])
+    check_all(layout, model, cal, out, lse, q_bits, what="zero query")
+    assert np.allclose(lse, np.log(np.array(lens, dtype=np.float64))[:, None], atol=1e-5)

@@ -239,3 +239,36 @@ def test_demote_only_leaves_ring_alone():
     slot = (320 - 256 - 64) % 256   # position 64 -> slot 0
     exp = expected_block(ring[slot:slot + 1], ring[slot:slot + 1], rk[0], rv[0], ck[0], cv[0], 64, 1)
     assert np.array_equal(cache.pages[1, 0].cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("codebook", ["uniform", "lloyd-max"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_fill_degenerate_tokens_bit_exact(group, codebook):
+    """Degenerate tokens: all zero, constant within every group (scale 0),
+    two-valued groups, values far beyond the clip thresholds (clipped to
+    +-c), tiny magnitudes and half-zero tokens.  R = I keeps the rotated
+    values exact, so the page bytes must equal the oracle's."""
+    rng = np.random.default_rng(50 + group)
+    hkv, n = 1, 64
+    x = rng.standard_normal((n, hkv, 128)).astype(np.float32)
+    x[0] = 0.0
+    x[1] *= 1e-3
+    x[2] = 1.5
+    for gi in range(128 // group):
+        x[3, :, gi * group:(gi + 1) * group] = gi - 1.25        # constant per group
+    x[4, :, ::2] = 3.0
+    x[4, :, 1::2] = -3.0                                          # two-valued groups
+    x[5] *= 1e4                                                    # every channel clipped
+    x[6, :, :64] = 0.0                                             # half zero
+    bits = gen.bf16_bits(x)
+    rk, rv, ck, cv = make_rot("identity", hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    cache = PagedKVCache(4, hkv, group, 1, 1, 2, codebook=CODEBOOK_ID[codebook])
+    cache.page_table.copy_(torch.tensor([[1]], dtype=torch.int32))
+    cache.seq_lens.fill_(320 + n)
+    ok.oscar_kv_fill_history(cache.dims, rot.struct, cache.struct(), 0, 0, n, bits_tensor(bits),
+                             bits_tensor(bits[::-1].copy()))
+    torch.cuda.synchronize()
+    exp = expected_block(bits[:, 0], bits[::-1, 0].copy(), rk[0], rv[0], ck[0], cv[0], group, n, codebook)
+    assert np.array_equal(cache.pages[1, 0].cpu().numpy(), exp)
+    assert not cache.pages[0].cpu().numpy().any()
