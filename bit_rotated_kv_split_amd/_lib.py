@@ -70,6 +70,8 @@ _SIGS = [
     ("oscar_kv_fill_history", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_kv_read_history", ctypes.c_int, [_P(OscarDims), _P(OscarCache), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_history_splits", ctypes.c_int32, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
     ("oscar_decode_workspace_bytes", ctypes.c_size_t, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
     ("oscar_decode_attn", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
@@ -214,6 +216,12 @@ def oscar_kv_fill_history(dims, rot, cache, request: int, hist_begin: int, n_tok
     _check(lib().oscar_kv_fill_history(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
                                        request, hist_begin, n_tokens, _ptr(k_tokens),
                                        _ptr(v_tokens), _stream(stream)))
+
+
+def oscar_kv_read_history(dims, cache, request: int, hist_begin: int, n_tokens: int, k_out, v_out,
+                          stream=None) -> None:
+    _check(lib().oscar_kv_read_history(ctypes.byref(dims), ctypes.byref(cache), request, hist_begin, n_tokens,
+                                       _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 def oscar_history_splits(dims, batch: int, max_seq_len: int) -> int:

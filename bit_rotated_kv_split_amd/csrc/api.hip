@@ -236,6 +236,27 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
   return OSCAR_OK;
 }
 
+int oscar_kv_read_history(const oscar_dims* dims, const oscar_cache* cache, int32_t request, int32_t hist_begin,
+                          int32_t n_tokens, float* k_out, float* v_out, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_cache(cache, true))) return rc;
+  if (request < 0 || request >= cache->batch)
+    return fail(OSCAR_EINVAL, "request %d outside batch %d", request, cache->batch);
+  if (hist_begin < 0 || n_tokens < 0)
+    return fail(OSCAR_EINVAL, "hist_begin %d / n_tokens %d must be >= 0", hist_begin, n_tokens);
+  if (n_tokens == 0) return OSCAR_OK;
+  if (k_out == nullptr || v_out == nullptr) return fail(OSCAR_EINVAL, "output pointers are NULL");
+  const int64_t last_page = (static_cast<int64_t>(hist_begin) + n_tokens - 1) / kPage;
+  if (last_page >= cache->max_pages_per_req)
+    return fail(OSCAR_EINVAL, "history index %lld beyond max_pages_per_req %d",
+                static_cast<long long>(hist_begin) + n_tokens - 1, cache->max_pages_per_req);
+  const hipError_t e = launch_read_history(*dims, *cache, request, hist_begin, n_tokens, k_out, v_out,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read-history launch");
+  return OSCAR_OK;
+}
+
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
   if (check_dims(dims) || batch < 0 || max_seq_len < 0) return -1;
   return workspace_layout(*dims, batch, max_seq_len).slots;

@@ -59,6 +59,44 @@ fill_kernel(DemoteArgs kk, DemoteArgs vv, int32_t request, int32_t hist_begin, i
   store_tokens<G, kMaxChunk>(sm, nt, blk, j0 & 63, is_v, k);
 }
 
+// Dequantized history values of one (request, KV head, K or V) for up to 64
+// consecutive history indices starting at hist_begin + 64 * blockIdx.x
+// (128 threads, thread = channel).  Uniform codebook: one float32 rounding
+// of code * scale + zero; Lloyd-Max: zero + scale * level in float64 (the
+// product and the sum each rounded, not fused), then rounded to float32.
+__global__ void __launch_bounds__(128)
+read_history_kernel(const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int32_t max_pages,
+                    int32_t hkv, int32_t group, int32_t codebook, Codebook cb, int32_t request, int32_t hist_begin,
+                    int32_t n_tokens, float* __restrict__ k_out, float* __restrict__ v_out) {
+  const int kvh = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int c = threadIdx.x;
+  const int ng = kDim / group, gi = c / group;
+  const int t0 = 64 * blockIdx.x;
+  const int t1 = min(t0 + 64, n_tokens);
+  float* out = is_v ? v_out : k_out;
+  for (int t = t0; t < t1; ++t) {
+    const int j = hist_begin + t;
+    const int phys = page_table[static_cast<size_t>(request) * max_pages + (j >> 6)];
+    const uint8_t* blk = pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(group);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(blk);
+    const int slot = j & 63;
+    uint32_t code;
+    if (!is_v) code = (words[(c >> 4) * 64 + qk_order(slot)] >> (2 * (c & 15))) & 3u;
+    else code = (words[512 + v_word_index(c, slot >> 4)] >> (2 * (slot & 15))) & 3u;
+    const uint16_t* sz = reinterpret_cast<const uint16_t*>(blk + kCodesBytes + (is_v ? kPage * ng * 4 : 0)) +
+                         (qk_order(slot) * ng + gi) * 2;
+    const float s = bf16_to_f32(sz[0]), z = bf16_to_f32(sz[1]);
+    float y;
+    if (codebook == OSCAR_CODEBOOK_LLOYD_MAX)
+      y = static_cast<float>(__dadd_rn(static_cast<double>(z),
+                                       __dmul_rn(static_cast<double>(s), static_cast<double>(cb.lev[code]))));
+    else
+      y = __builtin_fmaf(static_cast<float>(code), s, z);   // code * s is exact: one rounding
+    out[(static_cast<size_t>(t) * hkv + kvh) * kDim + c] = y;
+  }
+}
+
 DemoteArgs make_args(const oscar_dims& d, const oscar_cache& c, const float* r, const float* clip) {
   DemoteArgs a;
   a.r = r;
@@ -120,6 +158,15 @@ hipError_t launch_fill(const oscar_dims& d, const oscar_rotation& rot, const osc
       fill_kernel<128><<<grid, 128, 0, s>>>(kk, vv, request, hist_begin, n_tokens, k_tokens, v_tokens);
       break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_read_history(const oscar_dims& d, const oscar_cache& c, int32_t request, int32_t hist_begin,
+                               int32_t n_tokens, float* k_out, float* v_out, hipStream_t s) {
+  const dim3 grid((n_tokens + 63) / 64, d.num_kv_heads, 2);
+  read_history_kernel<<<grid, 128, 0, s>>>(c.pages, c.page_table, c.max_pages_per_req, d.num_kv_heads, d.group_size,
+                                           d.codebook, *codebook_of(d.codebook), request, hist_begin, n_tokens, k_out,
+                                           v_out);
   return hipGetLastError();
 }
 

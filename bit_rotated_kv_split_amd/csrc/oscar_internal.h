@@ -100,6 +100,8 @@ hipError_t launch_demote(const oscar_dims& d, const oscar_rotation& rot, const o
 hipError_t launch_fill(const oscar_dims& d, const oscar_rotation& rot, const oscar_cache& c,
                        int32_t request, int32_t hist_begin, int32_t n_tokens,
                        const uint16_t* k_tokens, const uint16_t* v_tokens, hipStream_t s);
+hipError_t launch_read_history(const oscar_dims& d, const oscar_cache& c, int32_t request, int32_t hist_begin,
+                               int32_t n_tokens, float* k_out, float* v_out, hipStream_t s);
 
 struct DecodeArgs {
   const oscar_dims* dims;

@@ -167,6 +167,17 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
                           int32_t n_tokens, const uint16_t* k_tokens,
                           const uint16_t* v_tokens, void* stream);
 
+/* Read history back: the dequantized stored (rotated-domain) values of
+ * history indices hist_begin .. hist_begin+n_tokens-1 of request `request`,
+ * zero + scale * level[code] per element, into k_out and v_out (device
+ * float32 [n_tokens][Hkv][128]).  Uniform codebook: code * scale + zero with
+ * one float32 rounding; Lloyd-Max: the float64 value rounded once to
+ * float32.  For inspection, tests and quality metrics (the decode path never
+ * forms these values).  Asynchronous on `stream`; OSCAR_EINVAL for indices
+ * outside the request's page table. */
+int oscar_kv_read_history(const oscar_dims* dims, const oscar_cache* cache, int32_t request,
+                          int32_t hist_begin, int32_t n_tokens, float* k_out, float* v_out, void* stream);
+
 /* Upper bound on the history splits per KV head that oscar_decode_attn
  * schedules for a batch of this size.  The splits themselves are chosen on
  * the device from the lengths: with T = ceil(W / Hkv) and W the

@@ -272,3 +272,31 @@ def test_fill_degenerate_tokens_bit_exact(group, codebook):
     exp = expected_block(bits[:, 0], bits[::-1, 0].copy(), rk[0], rv[0], ck[0], cv[0], group, n, codebook)
     assert np.array_equal(cache.pages[1, 0].cpu().numpy(), exp)
     assert not cache.pages[0].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("codebook", ["uniform", "lloyd-max"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_read_history_equals_oracle_dequantization(group, codebook):
+    """oscar_kv_read_history returns the oracle's dequantized values bit for
+    bit (R a signed permutation, so the codes themselves are exact): float32
+    code * scale + zero, or the float64 Lloyd-Max value rounded once."""
+    rng = np.random.default_rng(70 + group)
+    B, hkv, n = 1, 2, 150
+    cache = PagedKVCache(4, hkv, group, B, 3, 4, codebook=CODEBOOK_ID[codebook])
+    cache.page_table.copy_(torch.tensor([[2, 0, 3]], dtype=torch.int32))
+    cache.seq_lens.fill_(320 + n)
+    rk, rv, ck, cv = make_rot("signed_perm", hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    kb, vb = random_tokens(rng, n, hkv), random_tokens(rng, n, hkv)
+    ok.oscar_kv_fill_history(cache.dims, rot.struct, cache.struct(), 0, 0, n, bits_tensor(kb), bits_tensor(vb))
+    a, m = 17, 120                                    # an unaligned range across pages
+    ko = torch.full((m, hkv, 128), float("nan"), dtype=torch.float32, device="cuda")
+    vo = torch.full_like(ko, float("nan"))
+    ok.oscar_kv_read_history(cache.dims, cache.struct(), 0, a, m, ko, vo)
+    torch.cuda.synchronize()
+    ko, vo = ko.cpu().numpy(), vo.cpu().numpy()
+    for j in range(hkv):
+        for bits, r, c, got in ((kb, rk[j], ck[j], ko), (vb, rv[j], cv[j], vo)):
+            codes, s, z = O.demote(bits[a:a + m, j], r, c, group, codebook)
+            exp = O.dequantize_any(codes, s, z, group, codebook).astype(np.float32)
+            assert np.array_equal(got[:, j], exp), f"kvh={j}"

@@ -128,6 +128,13 @@ def test_null_and_inconsistent_arguments():
         ok.oscar_kv_fill_history(d, _rot(), _cache(), 1, 0, 10, 0x1000, 0x1000, 0)
     with pytest.raises(ok.OscarError):
         ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 250, 10, 0x1000, 0x1000, 0)
+    # read-back outside the batch, beyond the page table, or with no outputs
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_read_history(d, _cache(), 1, 0, 10, 0x1000, 0x1000, 0)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_read_history(d, _cache(), 0, 250, 10, 0x1000, 0x1000, 0)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_kv_read_history(d, _cache(), 0, 0, 10, None, 0x1000, 0)
     with pytest.raises(ok.OscarError):
         ok.oscar_merge_lse(d, _rot(), 1, 100, None, 1 << 30, 0x1000, None, 0)
     # fused decode needs an output
