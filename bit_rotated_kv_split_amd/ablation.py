@@ -68,8 +68,34 @@ def clips_for(x: np.ndarray, r: np.ndarray, pct: float) -> np.ndarray:
                      for j in range(hkv)]).astype(np.float32)
 
 
+def logit_error(ok, W, cache, w, layout, model, r_k, q_bits, q_scale: float, n_tok: int) -> float:
+    """Mean over (request, KV head) of ||Q (K_hat - K)^T||^2 / ||Q K^T||^2 on
+    history indices 0 .. n_tok-1 (float64 on the host)."""
+    import torch
+    from synth import gen
+    B, hkv, g = w.batch, w.num_kv_heads, w.gqa
+    ko = torch.empty((n_tok, hkv, 128), dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    r = r_k.cpu().numpy() if hasattr(r_k, "cpu") else np.asarray(r_k)
+    ratios = []
+    for b in range(B):
+        ok.oscar_kv_read_history(cache.dims, cache.struct(), b, 0, n_tok, ko, vo)
+        torch.cuda.synchronize()
+        kh = ko.cpu().numpy().astype(np.float64)
+        for j in range(hkv):
+            k = np.zeros((n_tok, 128), dtype=np.uint16)
+            for src, p0, n in layout.src_ranges(b, ok.SINK, n_tok):
+                k[p0 - ok.SINK:p0 - ok.SINK + n] = gen.kv_tokens_bf16(w.seed, "k", src, j, p0, n, model.k_scale[j])
+            kf = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            k_hat = kh[:, j] @ r[j].astype(np.float64).T
+            q = (q_bits[b, j * g:(j + 1) * g].astype(np.uint32) << 16).view(np.float32).astype(np.float64) * q_scale
+            ref = q @ kf.T
+            ratios.append(float(np.sum((q @ k_hat.T - ref) ** 2) / np.sum(ref ** 2)))
+    return float(np.mean(ratios))
+
+
 def run(batch: int = 4, context: int = 32768, seed: int = 11, q_heads: int = 32, kv_heads: int = 8,
-        groups=(128, 64, 32), q_scales=(0.0625, 0.25, 1.0)):
+        groups=(128, 64, 32), q_scales=(0.0625, 0.25, 1.0), logit_tokens: int = 4096):
     """Yield one dict of error metrics per (query scale, group size, rotation set)."""
     import torch
     from synth import configs
@@ -87,6 +113,7 @@ def run(batch: int = 4, context: int = 32768, seed: int = 11, q_heads: int = 32,
     layout = W.Layout(base)
     B, hq, hkv = base.batch, base.num_q_heads, base.num_kv_heads
     qc, kc, vc = model.calibration()
+    q_bits = model.queries(0, B)
     q1 = W.queries_tensor(model, 0, B)
     L = int(layout.lens.max())
 
@@ -146,11 +173,14 @@ def run(batch: int = 4, context: int = 32768, seed: int = 11, q_heads: int = 32,
             o = out.cpu().numpy().astype(np.float64)
             rel = np.linalg.norm(o - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
             lerr = np.abs(lse.cpu().numpy() - ref_lse)
+            n_tok = min(logit_tokens, L - W.BF16_TOKENS)
+            logit = logit_error(ok, W, cache, wc, layout, model, r_k, q_bits, qs, n_tok) if n_tok > 0 else 0.0
             del cache, ws
             yield {"q_scale": qs, "group_size": g, "rotation": name, "out_rel_l2_mean": float(rel.mean()),
                    "out_rel_l2_p95": float(np.percentile(rel, 95)), "out_rel_l2_max": float(rel.max()),
                    "lse_abs_err_mean": float(lerr.mean()), "lse_abs_err_max": float(lerr.max()),
                    "ref_lse_minus_log_len_mean": float((ref_lse - np.log(L)).mean()),
+                   "logit_rel_err": logit, "logit_tokens": n_tok,
                    "batch": B, "context": L, "q_heads": hq, "kv_heads": hkv, "seed": seed}
 
 
@@ -163,9 +193,11 @@ def main(argv=None) -> int:
     ap.add_argument("--kv-heads", type=int, default=8)
     ap.add_argument("--groups", default="128,64,32")
     ap.add_argument("--q-scales", default="0.0625,0.25,1")
+    ap.add_argument("--logit-tokens", type=int, default=4096)
     args = ap.parse_args(argv)
     for rec in run(args.batch, args.context, args.seed, args.q_heads, args.kv_heads,
-                   [int(g) for g in args.groups.split(",")], [float(x) for x in args.q_scales.split(",")]):
+                   [int(g) for g in args.groups.split(",")], [float(x) for x in args.q_scales.split(",")],
+                   args.logit_tokens):
         print(json.dumps(rec), flush=True)
     return 0
 

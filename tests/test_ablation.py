@@ -28,9 +28,14 @@ def test_clips_are_percentiles_of_rotated_magnitudes():
 
 @pytest.mark.gpu
 def test_rotation_ablation_orders_naive_int2_last():
-    recs = {r["rotation"]: r for r in ablation.run(batch=2, context=8192, groups=(64,), q_scales=(0.0625,))}
+    recs = {r["rotation"]: r for r in ablation.run(batch=2, context=8192, groups=(64,), q_scales=(0.0625,),
+                                                   logit_tokens=1024)}
     assert set(recs) == {"identity", "hadamard", "hadamard-bitrev", "oscar", "oscar-noclip", "oscar-lloyd-max"}
     for name in ("hadamard", "hadamard-bitrev", "oscar", "oscar-lloyd-max"):
         assert recs[name]["out_rel_l2_mean"] < 0.75 * recs["identity"]["out_rel_l2_mean"], name
         assert recs[name]["lse_abs_err_mean"] < recs["identity"]["lse_abs_err_mean"], name
     assert all(np.isfinite(r["out_rel_l2_max"]) for r in recs.values())
+    # the pages' key objective: rotation lowers the relative logit error too
+    for name in ("hadamard", "oscar", "oscar-lloyd-max"):
+        assert recs[name]["logit_rel_err"] < 0.5 * recs["identity"]["logit_rel_err"], name
+    assert all(0 < r["logit_rel_err"] < 10 for r in recs.values())
