@@ -454,3 +454,58 @@ def test_zero_query_gives_uniform_attention(kernel, codebook):
     out, lse = run_decode(cache, rot, q, int(layout.lens.max()), KERNELS[kernel])
     check_all(layout, model, cal, out, lse, q_bits, what="zero query")
     assert np.allclose(lse, np.log(np.array(lens, dtype=np.float64))[:, None], atol=1e-5)
+
+
+def _step_sequence(w, steps, lens0):
+    """Run `steps` decode steps (append + demotion + attention) from lengths
+    lens0; return the layout at the final lengths, the model, calibration and
+    the final step's output and LSE."""
+    layout, model, cal, rot, cache = setup(w, lens=lens0, extra=steps)
+    ws = DecodeWorkspace(cache.dims, w.batch, int(layout.lens.max()) + steps)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device="cuda")
+    lens = layout.lens.copy()
+    for s in range(1, steps + 1):
+        lens = lens + 1
+        cache.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        kn = W.new_tokens_tensor(model, layout, lens, "k")
+        vn = W.new_tokens_tensor(model, layout, lens, "v")
+        q = W.queries_tensor(model, s, w.batch)
+        decode_step(cache, rot, ws, q, out, lse, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    layout.lens = lens
+    return layout, model, cal, out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_tiny_config_one_step(kernel):
+    """The tiny configuration as specified: L = 1023, one decode step with
+    append and demotion to L = 1024 (64 | 704 | 256), G = 32, against the
+    oracle at the final length."""
+    base = configs.tiny()
+    prev = ok.oscar_set_history_kernel(KERNELS[kernel])
+    try:
+        layout, model, cal, out, lse = _step_sequence(base, 1, [1023])
+    finally:
+        ok.oscar_set_history_kernel(prev)
+    assert int(layout.lens[0]) == 1024
+    ref, ref_lse = oracle_request(model, layout, cal, model.queries(1, 1)[0], 0, 1024)
+    assert_close(out[0], ref, "tiny one step")
+    assert np.abs(lse[0] - ref_lse).max() < 2e-3
+
+
+@pytest.mark.slow
+def test_batch1_100k_hundred_steps_sampled():
+    """The batch-1 configuration: 100 steps with append and demotion ending
+    at L = 100,000 (contiguous history, G = 128), the last step's output for
+    two KV heads against the oracle replaying the same token sequence."""
+    from gpu_helpers import oracle_request_heads
+    w = configs.qwen3_8b_b1()
+    layout, model, cal, out, lse = _step_sequence(w, 100, [100_000 - 100])
+    assert int(layout.lens[0]) == 100_000 and np.isfinite(out).all()
+    g = w.gqa
+    q_bits = model.queries(100, 1)[0]
+    res = oracle_request_heads(model, layout, cal, q_bits, 0, 100_000, [0, 5])
+    for j, (ref, ref_lse) in res.items():
+        assert_close(out[0, j * g:(j + 1) * g], ref, f"b1 100 steps kvh={j}")
+        assert np.abs(lse[0, j * g:(j + 1) * g] - ref_lse).max() < 2e-3
