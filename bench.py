@@ -185,8 +185,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (0: the workload's own count, 100 for b1-100k and 200 for "
-                         "b32-ragged-gqa8, else 20)")
-    ap.add_argument("--warmup", type=int, default=10)
+                         "b32-ragged-gqa8, else 100)")
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the GPU's clocks settle over the first tens of steps)")
     ap.add_argument("--workload", default="b32-100k-g128", choices=sorted(workloads()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--layers", type=int, default=0,
@@ -214,7 +215,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     w = workloads()[args.workload]()
-    steps, warmup = args.steps or (w.steps if w.steps > 1 else 20), args.warmup
+    steps, warmup = args.steps or (w.steps if w.steps > 1 else 100), args.warmup
     total = steps + warmup
     n_layers = args.layers or default_layers(args.workload)
     appends = -(-total // n_layers)          # tokens each layer cache receives

@@ -90,9 +90,12 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     if (lane == 0) qinv[h] = mx > 0.f ? kQFixMax / mx : 0.f;
     for (int gi = 0; gi < 4; ++gi) {
       const int lo = gi * G, hi = lo + G;
-      float sgi = (lane >= lo && lane < hi ? v0 : 0.f) + (lane + 64 >= lo && lane + 64 < hi ? v1 : 0.f);
-      sgi = wave_sum(sgi);
-      if (lane == 0) qsum[(head0 + h) * 4 + gi] = gi * G < kDim ? sgi : 0.f;
+      float sgi = 0.f;
+      if (lo < kDim) {   // uniform: groups past the head dimension hold 0
+        sgi = (lane >= lo && lane < hi ? v0 : 0.f) + (lane + 64 >= lo && lane + 64 < hi ? v1 : 0.f);
+        sgi = wave_sum(sgi);
+      }
+      if (lane == 0) qsum[(head0 + h) * 4 + gi] = sgi;
     }
     if (lane == 0) {
       float* sc = reinterpret_cast<float*>(qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes +
