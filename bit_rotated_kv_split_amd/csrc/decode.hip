@@ -59,16 +59,17 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   __shared__ float qr[GQ][kDim];
   __shared__ float qinv[GQ];
   const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
-  for (int i = tid; i < GQ * kDim; i += 256) qs[i / kDim][i % kDim] = bf16_to_f32(q[head0 * kDim + i]);
-  __syncthreads();
-  // q . R_K: thread (k, half) sums rows i of its half
+  // q . R_K: thread (k, half) sums rows i of its half; its rotation values
+  // are requested together with the queries, so the rows wait on memory once
   const float* r = r_k + static_cast<size_t>(kvh) * kDim * kDim;
-  float acc[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
   float rv[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) rv[i] = r[(64 * half + i) * kDim + k];
+  for (int i = tid; i < GQ * kDim; i += 256) qs[i / kDim][i % kDim] = bf16_to_f32(q[head0 * kDim + i]);
+  __syncthreads();
+  float acc[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
 #pragma unroll
   for (int i = 0; i < 64; ++i)
 #pragma unroll

@@ -48,10 +48,7 @@ __device__ __forceinline__ void group_sum_f64(double (&v)[NT], double (&xd)[2][N
   }
 }
 
-// Rotate, clip and quantize nt (<= NT) tokens held in sm.x.  Called by the
-// 128 threads of one unit (k = 0..127, two whole waves); every thread of the
-// workgroup passes the same barriers (the codebook is uniform across it).
-// Leaves codes, scale and zero in sm.
+// The quantizers:
 //   OSCAR_CODEBOOK_UNIFORM: zero = bf16(min), scale = bf16((max - min) / 3),
 //     code = clamp(rint((y - zero) / scale), 0, 3).
 //   OSCAR_CODEBOOK_LLOYD_MAX: zero = bf16(float(mean)), scale =
@@ -59,33 +56,35 @@ __device__ __forceinline__ void group_sum_f64(double (&v)[NT], double (&xd)[2][N
 //     float64; code = number of thresholds (-thr, 0, thr) below
 //     (y - zero) / scale.
 // A group whose scale is 0 gets code 0.
+// Channel k of x . R for one token held in sm.x[0], with the rotation
+// column already in registers (rv[i] = R[i][k]): float64 products and four
+// float64 partial sums, rounded once to float32.
+__device__ __forceinline__ float rotate_one(const QuantSmem<1>& sm, const float (&rv)[kDim]) {
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < kDim; ++i)
+    acc[i & 3] = fma(static_cast<double>(sm.x[0][i]), static_cast<double>(rv[i]), acc[i & 3]);
+  return static_cast<float>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
+template <int G, int NT>
+__device__ void quantize_rotated(QuantSmem<NT>& sm, int nt, float (&y)[NT], int k, int codebook, float thr);
+
+// Rotate, clip and quantize nt tokens held in sm.x (see quantize_rotated).
 template <int G, int NT>
 __device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restrict__ r,
                                 const float* __restrict__ clipv, int k, int codebook, float thr) {
-  constexpr int WG = G < 64 ? G : 64;   // group lanes inside one wave
-  const int lane = k & 63, wave = k >> 6;
-  auto& xw = sm.xw;
   double acc[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
-  if constexpr (NT == 1) {
-    // one token: every load of the rotation column in flight at once
-    float rv[kDim];
+  for (int i = 0; i < kDim; i += 4) {
 #pragma unroll
-    for (int i = 0; i < kDim; ++i) rv[i] = r[i * kDim + k];
+    for (int u = 0; u < 4; ++u) {
+      const double rik = static_cast<double>(r[(i + u) * kDim + k]);
 #pragma unroll
-    for (int i = 0; i < kDim; ++i)
-      acc[0][i & 3] = fma(static_cast<double>(sm.x[0][i]), static_cast<double>(rv[i]), acc[0][i & 3]);
-  } else {
-    for (int i = 0; i < kDim; i += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const double rik = static_cast<double>(r[(i + u) * kDim + k]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
-      }
+      for (int t = 0; t < NT; ++t) acc[t][u] = fma(static_cast<double>(sm.x[t][i + u]), rik, acc[t][u]);
     }
   }
   const float c = clipv[k];
@@ -94,8 +93,21 @@ __device__ void quantize_tokens(QuantSmem<NT>& sm, int nt, const float* __restri
   for (int t = 0; t < NT; ++t) {
     const double sum = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
     y[t] = fminf(fmaxf(static_cast<float>(sum), -c), c);
-    sm.y[t][k] = y[t];
   }
+  quantize_rotated<G, NT>(sm, nt, y, k, codebook, thr);
+}
+
+// Quantize nt (<= NT) rotated, clipped tokens, channel k of token t in y[t].
+// Called by the 128 threads of one unit (k = 0..127, two whole waves);
+// every thread of the workgroup passes the same barriers (the codebook is
+// uniform across it).  Leaves codes, scale and zero in sm.
+template <int G, int NT>
+__device__ void quantize_rotated(QuantSmem<NT>& sm, int nt, float (&y)[NT], int k, int codebook, float thr) {
+  constexpr int WG = G < 64 ? G : 64;   // group lanes inside one wave
+  const int lane = k & 63, wave = k >> 6;
+  auto& xw = sm.xw;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sm.y[t][k] = y[t];
   const int gi = k / G;
   if (codebook == OSCAR_CODEBOOK_LLOYD_MAX) {
     double mean[NT], sq[NT];
@@ -213,28 +225,62 @@ __device__ void store_tokens(const QuantSmem<NT>& sm, int nt, uint8_t* __restric
 // Demotion of one (request, KV head, K or V) for a decode step, by one
 // 128-thread unit (thread k): the token at position L-257 leaves the recent
 // ring for history index L-321, then the new token (if given) takes its
-// sink or recent slot.
+// sink or recent slot.  Everything the unit reads is requested right after
+// the length, so the unit waits on memory about twice (the length, then
+// the token, its rotation column, the clip threshold, the page-table entry
+// and the new token together); the value word's other fifteen slots are
+// kept by an atomic AND/OR pair instead of a read-modify-write.
 template <int G>
 __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int k, QuantSmem<1>& sm) {
+  constexpr int NG = kDim / G;
   const DemoteArgs& a = is_v ? d.vv : d.kk;
   const int hkv = a.hkv;
   const int L = d.seq_lens[b];
   uint16_t* recent = (is_v ? d.recent_v : d.recent_k) + (static_cast<size_t>(b) * hkv + kvh) * kRecent * kDim;
+  const uint16_t* src = is_v ? d.v_new : d.k_new;
+  const bool append = src != nullptr && L >= 1;   // uniform across the workgroup
+  const uint16_t val = append ? src[(static_cast<size_t>(b) * hkv + kvh) * kDim + k] : uint16_t{0};
   if (L > kBf16Tokens) {   // uniform across the workgroup
     const int j = L - kBf16Tokens - 1;            // history index of position L-257
     const int ring = (L - 1 - kSink) & (kRecent - 1);
-    sm.x[0][k] = bf16_to_f32(recent[ring * kDim + k]);
-    __syncthreads();
-    quantize_tokens<G, 1>(sm, 1, a.r + static_cast<size_t>(kvh) * kDim * kDim, a.clip + kvh * kDim, k,
-                          a.codebook, a.thr);
+    const float* r = a.r + static_cast<size_t>(kvh) * kDim * kDim;
+    const uint16_t xk = recent[ring * kDim + k];
+    float rv[kDim];
+#pragma unroll
+    for (int i = 0; i < kDim; ++i) rv[i] = r[i * kDim + k];
+    const float c = a.clip[kvh * kDim + k];
     const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + (j >> 6)];
+    sm.x[0][k] = bf16_to_f32(xk);
+    __syncthreads();
+    float y[1] = {fminf(fmaxf(rotate_one(sm, rv), -c), c)};
+    quantize_rotated<G, 1>(sm, 1, y, k, a.codebook, a.thr);
     uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
-    store_tokens<G, 1>(sm, 1, blk, j & 63, is_v, k);
+    const int slot = j & 63;
+    uint32_t* words = reinterpret_cast<uint32_t*>(blk);
+    if (!is_v) {
+      if (k < 8) {   // key word d = k: channels 16k .. 16k+15 of this slot
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w |= static_cast<uint32_t>(sm.code[0][16 * k + i]) << (2 * i);
+        words[k * 64 + qk_order(slot)] = w;
+      }
+    } else {
+      // channel k's value word holds slots 16w .. 16w+15: clear this slot's
+      // two bits, then set them (same address, same thread: in order)
+      uint32_t* wp = words + 512 + v_word_index(k, slot >> 4);
+      const int sh = 2 * (slot & 15);
+      atomicAnd(wp, ~(3u << sh));
+      atomicOr(wp, static_cast<uint32_t>(sm.code[0][k]) << sh);
+    }
+    if (k < NG) {
+      uint16_t* e = reinterpret_cast<uint16_t*>(blk + kCodesBytes + (is_v ? kPage * NG * 4 : 0)) +
+                    (qk_order(slot) * NG + k) * 2;
+      e[0] = f32_to_bf16_rne(sm.scale[0][k]);
+      e[1] = f32_to_bf16_rne(sm.zero[0][k]);
+    }
   }
-  const uint16_t* src = is_v ? d.v_new : d.k_new;
-  if (src != nullptr && L >= 1) {
+  if (append) {
     const int p = L - 1;
-    const uint16_t val = src[(static_cast<size_t>(b) * hkv + kvh) * kDim + k];
     if (p < kSink) {
       uint16_t* sink = (is_v ? d.sink_v : d.sink_k) + (static_cast<size_t>(b) * hkv + kvh) * kSink * kDim;
       sink[p * kDim + k] = val;
