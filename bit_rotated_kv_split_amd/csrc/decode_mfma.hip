@@ -68,14 +68,15 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Launch-shape knobs (compile-time): register page buffers per wave (2 or 3)
 // and the waves per SIMD the register budget is sized for.
 #ifndef OSCAR_HIST_BUFFERS
-#define OSCAR_HIST_BUFFERS 3
+#define OSCAR_HIST_BUFFERS 2
 #endif
 #ifndef OSCAR_HIST_MIN_WAVES
 #define OSCAR_HIST_MIN_WAVES 2
 #endif
-// the Lloyd-Max form holds a second set of value accumulators
+// the Lloyd-Max form holds a second set of value accumulators (two
+// buffers measured 3 % faster than three)
 #ifndef OSCAR_HIST_BUFFERS_LM
-#define OSCAR_HIST_BUFFERS_LM 3
+#define OSCAR_HIST_BUFFERS_LM 2
 #endif
 #ifndef OSCAR_HIST_MIN_WAVES_LM
 #define OSCAR_HIST_MIN_WAVES_LM OSCAR_HIST_MIN_WAVES
@@ -527,12 +528,14 @@ hist_mfma_kernel(MfmaParams a) {
   }
   const int split = id / a.hkv, kvh = id % a.hkv;
   if (split >= a.sched[0]) return;
-  const int b = a.sched[1 + 3 * split];
-  const int p0 = a.sched[2 + 3 * split];
-  const int p1 = a.sched[3 + 3 * split];
+  // the split's request and page range, and the request's length, are
+  // uniform: held in scalar registers so every branch on them is uniform
+  const int b = __builtin_amdgcn_readfirstlane(a.sched[1 + 3 * split]);
+  const int p0 = __builtin_amdgcn_readfirstlane(a.sched[2 + 3 * split]);
+  const int p1 = __builtin_amdgcn_readfirstlane(a.sched[3 + 3 * split]);
   HistSmem<NHB, NG>& sm = smem.hist[wave];
 
-  const int L = a.seq_lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
   const int n_hist = max(0, L - kBf16Tokens);
 
   WaveState<NHB, G> st;
@@ -601,20 +604,34 @@ hist_mfma_kernel(MfmaParams a) {
   // Every step issues its loads (past the split's end it reloads the last
   // page, which the cache serves), so the count of loads between a page's
   // loads and its use is the same on every path and the compiler's wait
-  // before a page can leave the younger pages in flight.
+  // before a page can leave the younger pages in flight.  The loop leaves
+  // only at its latch: an exit after any page would give the loop head a
+  // path on which the youngest loads are the ones it needs first, and the
+  // wait there would drain every page in flight.
   if (p0 < p1) {   // uniform
     const int p_last = p1 - 1;
     PageRegs<G> buf[BUF];
 #pragma unroll
-    for (int k = 0; k < BUF - 1; ++k) load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
-    for (int p = p0; p < p1; p += BUF) {
+    for (int k = 0; k < BUF - 1; ++k) {
+      load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole groups of BUF pages: one exit, at the latch, so the loads in
+    // flight at the loop head are the same on every path into it
+    const int groups = (p1 - p0) / BUF;
+    int p = p0;
+    for (int it = 0; it < groups; ++it, p += BUF) {
 #pragma unroll
       for (int k = 0; k < BUF; ++k) {
         load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
         process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
-        if (p + k + 1 >= p1) break;
       }
     }
+    // the last (p1 - p0) % BUF pages are already in buf[0 ..]
+#pragma unroll
+    for (int k = 0; k < BUF - 1; ++k)
+      if (p + k < p1)
+        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
   }
 
   // ---- partial output of this split (rotated value domain)
@@ -646,8 +663,9 @@ hist_mfma_kernel(MfmaParams a) {
 // Register page buffers and waves per SIMD of each instantiation.  The
 // two-wave (GQA-8) G = 128 uniform kernel fits three waves per SIMD with two
 // buffers (168 VGPRs, no spills) and runs about 7 % faster that way; the
-// others keep three buffers at two waves per SIMD (at three waves they spill,
-// and without the third buffer they ran slower).
+// uniform G = 64 / 128 kernels keep two buffers at two waves per SIMD (with
+// the loop's single exit, a third buffer or a third wave measured 1-2 %
+// slower); the Lloyd-Max kernels keep three.
 template <int G, int WAVES, bool LM>
 struct HistShape {
   static constexpr bool kThreeWaves = G == 128 && WAVES == 2 && !LM;
