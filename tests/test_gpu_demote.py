@@ -300,3 +300,57 @@ def test_read_history_equals_oracle_dequantization(group, codebook):
             codes, s, z = O.demote(bits[a:a + m, j], r, c, group, codebook)
             exp = O.dequantize_any(codes, s, z, group, codebook).astype(np.float32)
             assert np.array_equal(got[:, j], exp), f"kvh={j}"
+
+
+@pytest.mark.parametrize("group,codebook", [(64, "uniform"), (128, "lloyd-max")])
+def test_demote_keeps_other_slots_of_reused_pages(group, codebook):
+    """Demotion into pages that hold stale bytes (pages reused from an
+    earlier request): each step writes exactly its own slot (its key words,
+    its two bits in every value word, its scale/zero entries) and leaves
+    every other bit as it was, across value-word boundaries."""
+    rng = np.random.default_rng(23 + group)
+    hkv, hq, L0, steps = 2, 4, 330, 30   # history indices 10 .. 39 are demoted
+    total = L0 + steps
+    k_all = random_tokens(rng, total, hkv).reshape(total, hkv, 128)
+    v_all = random_tokens(rng, total, hkv).reshape(total, hkv, 128)
+    rk, rv, ck, cv = make_rot("signed_perm", hkv, rng)
+    rot = Rotation(rk, rv, ck, cv)
+    cache = PagedKVCache(hq, hkv, group, 1, 2, 4, codebook=CODEBOOK_ID[codebook])
+    pt = np.array([[3, 1]], dtype=np.int32)
+    cache.page_table.copy_(torch.from_numpy(pt))
+    stale = rng.integers(0, 256, size=tuple(cache.pages.shape), dtype=np.uint8)
+    cache.pages.copy_(torch.from_numpy(stale))
+    cache.recent_k[0] = bits_tensor(np.stack([ring_expect(L0, k_all[:, j]) for j in range(hkv)]))
+    cache.recent_v[0] = bits_tensor(np.stack([ring_expect(L0, v_all[:, j]) for j in range(hkv)]))
+    L = L0
+    for _ in range(steps):
+        L += 1
+        cache.seq_lens.fill_(L)
+        ok.oscar_kv_demote(cache.dims, rot.struct, cache.struct(), bits_tensor(k_all[L - 1][None]),
+                           bits_tensor(v_all[L - 1][None]))
+    torch.cuda.synchronize()
+    got = cache.pages.cpu().numpy()
+    j0, j1 = L0 + 1 - 321, L - 321 + 1          # demoted history indices [j0, j1)
+    ng = 128 // group
+    for j in range(hkv):
+        sl = slice(64 + j0, 64 + j1)              # their positions
+        codes_k = np.zeros((64, 128), np.uint8)
+        codes_v = np.zeros((64, 128), np.uint8)
+        sk, zk, sv, zv = (np.zeros((64, ng), np.float32) for _ in range(4))
+        codes_k[j0:j1], sk[j0:j1], zk[j0:j1] = O.demote(k_all[sl, j], rk[j], ck[j], group, codebook)
+        codes_v[j0:j1], sv[j0:j1], zv[j0:j1] = O.demote(v_all[sl, j], rv[j], cv[j], group, codebook)
+        new = O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
+        mine = np.zeros((64, 128), np.uint8)
+        mine[j0:j1] = 3
+        mask = O.pack_block(mine, sk * 0, zk * 0, mine, sv * 0, zv * 0, group)   # code bits of the slots
+        exp = stale[pt[0, 0], j].copy()
+        exp[:4096] = (exp[:4096] & ~mask[:4096]) | new[:4096]
+        for t in range(j0, j1):                  # scale/zero entries of the slots
+            for half in range(2):
+                a = 4096 + half * 64 * ng * 4 + O.qk_order(t) * ng * 4
+                exp[a:a + ng * 4] = new[a:a + ng * 4]
+        assert np.array_equal(got[pt[0, 0], j], exp), f"kvh={j}"
+        assert np.array_equal(got[pt[0, 1], j], stale[pt[0, 1], j]), f"kvh={j}: untouched page changed"
+        others = np.ones(got.shape[0], bool)
+        others[pt[0]] = False
+        assert np.array_equal(got[others], stale[others])
