@@ -376,6 +376,8 @@ static_assert(kMaxSplits < kMergeHeadThreads, "one thread weighs each split");
 __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergeParams a) {
   constexpr int kWaves = kMergeHeadThreads / 64;
   constexpr int kPar = kMergeHeadThreads / kDim;   // threads per channel
+  constexpr int kPer = (kMaxSplits + kPar - 1) / kPar;   // history partials per thread
+  static_assert(kPer * kPar >= kMaxSplits, "every split has a thread");
   const int head = blockIdx.x, b = blockIdx.y, kvh = head / a.gq;
   const int tid = threadIdx.x;
   __shared__ float red[kWaves];
@@ -404,6 +406,11 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   };
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
   const size_t bh = static_cast<size_t>(b) * a.hq + head;
+  // the log-sum-exps first: the weights need only these
+  const float l = tid < count ? a.hlse[static_cast<size_t>(first + tid) * a.hq + head] : -INFINITY;
+  float lb[kBf16Parts];
+#pragma unroll
+  for (int c = 0; c < kBf16Parts; ++c) lb[c] = a.blse[bh * kBf16Parts + c];
   // threads 0..255: row i of R_V, columns 64 kh .. 64 kh + 63
   const int i = (tid >> 1) & (kDim - 1), kh = tid & 1;
   float4 rr[16];
@@ -413,44 +420,44 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 #pragma unroll
     for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
   }
+  // every history partial this thread sums (channel k, the splits congruent
+  // to par modulo kPar) and its bf16 partials are requested now, before the
+  // weights are known, so the kernel waits on memory once
+  const int k = tid & (kDim - 1), par = tid / kDim;
+  const float* hp = a.ho + (static_cast<size_t>(first) * a.hq + head) * kDim + k;
+  const size_t stride = static_cast<size_t>(a.hq) * kDim;
+  float v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int sp = par + kPar * u;
+    v[u] = sp < count ? hp[static_cast<size_t>(sp) * stride] : 0.f;
+  }
+  float vb[kBf16Parts];
+#pragma unroll
+  for (int c = 0; c < kBf16Parts; ++c)
+    vb[c] = tid < 2 * kDim && kh == 0 ? a.bo[(bh * kBf16Parts + c) * kDim + i] : 0.f;
   // history split weights e^{lse - M} / sum (count <= kMaxSplits < threads)
-  const float l = tid < count ? a.hlse[static_cast<size_t>(first + tid) * a.hq + head] : -INFINITY;
   const float mh = bmax(l);
   const float e = mh == -INFINITY || tid >= count ? 0.f : expf(l - mh);
   const float dh = bsum(e);
   if (tid < count) w[tid] = dh > 0.f ? e / dh : 0.f;
   const float lse_h = dh > 0.f ? mh + logf(dh) : -INFINITY;
   // bf16 partial weights (every thread computes the five)
-  float lb[kBf16Parts], mb = -INFINITY;
+  float mb = -INFINITY;
 #pragma unroll
-  for (int c = 0; c < kBf16Parts; ++c) {
-    lb[c] = a.blse[bh * kBf16Parts + c];
-    mb = fmaxf(mb, lb[c]);
-  }
+  for (int c = 0; c < kBf16Parts; ++c) mb = fmaxf(mb, lb[c]);
   float db = 0.f;
 #pragma unroll
   for (int c = 0; c < kBf16Parts; ++c) db += lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb);
   const float lse_b = mb + logf(db);   // the sink chunk always holds a token
   __syncthreads();
-  // weighted sum over the splits: channel k, the splits congruent to par
-  // modulo kPar, 16 loads in flight
+  // weighted sum over the splits, in ascending split order
   {
-    const int k = tid & (kDim - 1), par = tid / kDim;
-    const float* hp = a.ho + (static_cast<size_t>(first) * a.hq + head) * kDim + k;
-    const size_t stride = static_cast<size_t>(a.hq) * kDim;
     float acc = 0.f;
-    for (int s0 = par; s0 < count; s0 += 16 * kPar) {
-      float v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int sp = s0 + kPar * u;
-        v[u] = sp < count ? hp[static_cast<size_t>(sp) * stride] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int sp = s0 + kPar * u;
-        if (sp < count) acc = __builtin_fmaf(w[sp], v[u], acc);
-      }
+    for (int u = 0; u < kPer; ++u) {
+      const int sp = par + kPar * u;
+      if (sp < count) acc = __builtin_fmaf(w[sp], v[u], acc);
     }
     ypart[par][k] = acc;
   }
@@ -467,11 +474,11 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
-    const int k = 64 * kh + 4 * c;
-    acc = __builtin_fmaf(y[k + 0], rr[c].x, acc);
-    acc = __builtin_fmaf(y[k + 1], rr[c].y, acc);
-    acc = __builtin_fmaf(y[k + 2], rr[c].z, acc);
-    acc = __builtin_fmaf(y[k + 3], rr[c].w, acc);
+    const int kc = 64 * kh + 4 * c;
+    acc = __builtin_fmaf(y[kc + 0], rr[c].x, acc);
+    acc = __builtin_fmaf(y[kc + 1], rr[c].y, acc);
+    acc = __builtin_fmaf(y[kc + 2], rr[c].z, acc);
+    acc = __builtin_fmaf(y[kc + 3], rr[c].w, acc);
   }
   const float xh = acc + __shfl_xor(acc, 1, 64);
   if (kh == 0) {
@@ -479,7 +486,7 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 #pragma unroll
     for (int c = 0; c < kBf16Parts; ++c) {
       const float wc = lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb) / db;
-      ob = __builtin_fmaf(wc, a.bo[(bh * kBf16Parts + c) * kDim + i], ob);
+      ob = __builtin_fmaf(wc, vb[c], ob);
     }
     const float mx = fmaxf(lse_h, lse_b);
     const float eh = lse_h == -INFINITY ? 0.f : expf(lse_h - mx), eb = expf(lse_b - mx);
