@@ -152,7 +152,10 @@ size_t oscar_block_bytes(int32_t group_size);
  * Then the new token k_new/v_new (bf16 [B][Hkv][128]) is written to its sink
  * or recent slot, which for L > 320 is the slot just freed.  k_new and v_new
  * may both be NULL (demote only).  The page holding index L-321 must be
- * allocated in page_table and owned by this request alone. */
+ * allocated in page_table and owned by this request alone.  Only that slot's
+ * bits change: its key words and scale/zero entries are stored whole, and
+ * its two bits in each value word are cleared and set with device atomics,
+ * so the page's other slots keep whatever they hold. */
 int oscar_kv_demote(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                     const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
