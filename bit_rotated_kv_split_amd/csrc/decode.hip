@@ -499,7 +499,10 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 // merge_group_kernel (256 threads): the request's history splits are
 // merged per head in the rotated value domain, rotated back by R_V^T, and
 // merged with the five bf16 partials.  Loads are issued early: each
-// thread's half-row of R_V before anything else, then the partials.
+// thread's half-row of R_V before anything else, then the partials.  A
+// workgroup takes GQ heads of one (request, KV head): heads
+// GQ * blockIdx.z .. of the group (eight-head groups run as two four-head
+// workgroups).
 template <int GQ>
 __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
@@ -511,7 +514,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   __shared__ float orot[GQ][kDim];     // merged history output, rotated domain
   __shared__ float obf[GQ][kDim];      // merged bf16 output
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
-  const int h0 = kvh * GQ;             // first head of this KV head's group
+  const int h0 = kvh * a.gq + GQ * static_cast<int>(blockIdx.z);   // first head of this workgroup's block
   const size_t bhead0 = static_cast<size_t>(b) * a.hq + h0;
   // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
   const int i = tid >> 1, kh = tid & 1;
@@ -758,6 +761,10 @@ hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t 
   p.gq = d.num_q_heads / d.num_kv_heads;
   if (static_cast<int64_t>(batch) * d.num_kv_heads < kMergeGroupMinWgs) {
     merge_head_kernel<<<dim3(d.num_q_heads, batch), kMergeHeadThreads, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  if (p.gq % 4 == 0 && p.gq > 4) {   // four heads per workgroup: more, shorter workgroups
+    merge_group_kernel<4><<<dim3(d.num_kv_heads, batch, p.gq / 4), 256, 0, s>>>(p);
     return hipGetLastError();
   }
   return dispatch_gq<MergeGroupRun>(p.gq, p, d.num_kv_heads, batch, s);
