@@ -365,7 +365,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int2+bf16 storage, f32 accumulate",
+        # arithmetic: int8 x int8 -> int32 matrix-core products (query and
+        # softmax-weight digits against 2-bit codes) and float32 softmax,
+        # scales and accumulation; the cache holds 2-bit codes and bf16
+        "dtype": "i8-mfma+f32" if kname == "mfma" else "f32",
+        "storage": "int2 history (bf16 scale/zero) + bf16 sink/recent",
         "data": "synthetic (seeded generator; library-calibrated rotations)",
         "config": {"workload": w.name, "batch": B, "context": int(layout.lens.max()),
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128,
