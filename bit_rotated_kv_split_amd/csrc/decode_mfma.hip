@@ -614,6 +614,8 @@ hist_mfma_kernel(MfmaParams a) {
 #pragma unroll
     for (int k = 0; k < BUF - 1; ++k) {
       load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+      // keep the pages' loads in page order, the order the loop issues them
+      // in: the loop head's wait then covers only the page it needs first
       __builtin_amdgcn_sched_barrier(0);
     }
     // whole groups of BUF pages: one exit, at the latch, so the loads in

@@ -11,8 +11,8 @@ of the history kernel into bytes per launch.  Each counter is scaled by
 what it reads for the 2 GiB device copy that `bench.py --copy-probe` runs in
 the same process (copy bytes / counter bytes), so a counter that covers
 only part of the memory channels is corrected.  The record carries a hash of
-the decode kernel sources (csrc/decode*, csrc/*.h); `bench.py` reports it
-only while that hash matches the sources it runs.
+the decode kernels' code (csrc/decode*, csrc/*.h, comments excluded);
+`bench.py` reports it only while that hash matches the code it runs.
 """
 from __future__ import annotations
 
@@ -21,6 +21,7 @@ import collections
 import csv
 import json
 import os
+import re
 import sys
 
 COPY_BYTES = 2 << 30
@@ -67,13 +68,29 @@ def counters(path: str, kernel: str) -> dict:
     return {k: sum(v) / len(v) for k, v in res.items()}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, blank lines or indentation, so
+    that editing a comment does not retire the traffic records.  Text after
+    // is dropped line by line (no string literal in the hashed files holds
+    //)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = []
+    for ln in text.splitlines():
+        ln = re.sub(r"//.*$", "", ln).strip()
+        if ln:
+            lines.append(ln)
+    return "\n".join(lines)
+
+
 def source_sha(root: str) -> str:
+    """Hash of the decode kernels' code (csrc/decode*, csrc/*.h), comments
+    excluded."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(root, "bit_rotated_kv_split_amd", "csrc")
     for name in sorted(os.listdir(d)):
         if name.startswith("decode") or name.endswith(".h"):
-            h.update(open(os.path.join(d, name), "rb").read())
+            h.update(_code_only(open(os.path.join(d, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -52,3 +52,18 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_source_sha_ignores_comments_but_not_code(tmp_path):
+    from bit_rotated_kv_split_amd.profiling import source_sha
+    d = tmp_path / "bit_rotated_kv_split_amd" / "csrc"
+    d.mkdir(parents=True)
+    (d / "decode_x.hip").write_text("int f() {\n  return 1;  // one\n}\n")
+    (d / "other.hip").write_text("int g();\n")
+    base = source_sha(str(tmp_path))
+    (d / "decode_x.hip").write_text("// header\nint f() {\n  /* the\n     value */ return 1;   // uno\n\n}\n")
+    assert source_sha(str(tmp_path)) == base
+    (d / "other.hip").write_text("int g(); int h();\n")      # not a decode source
+    assert source_sha(str(tmp_path)) == base
+    (d / "decode_x.hip").write_text("int f() {\n  return 2;\n}\n")
+    assert source_sha(str(tmp_path)) != base
