@@ -83,6 +83,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #endif
 // G = 32 pages carry four scale/zero pairs per token and K/V (48 VGPRs a
 // buffer); its Lloyd-Max form keeps one buffer (two spill)
+// scale/zero entries loaded non-temporally too (one-wave kernels); off:
+// with them ordinary the 32 x 100K launch took 282.5 against 287.9 us
+#ifndef OSCAR_STREAM_SZ
+#define OSCAR_STREAM_SZ 0
+#endif
 #ifndef OSCAR_HIST_BUFFERS_32
 #define OSCAR_HIST_BUFFERS_32 2
 #endif
@@ -210,20 +215,32 @@ struct PageRegs {
   uint32_t vsz[4 * NG];
 };
 
-template <int G>
+// 16-byte load; STREAM marks it non-temporal.  A one-wave kernel reads its
+// code words once, and with non-temporal loads HBM streams them faster
+// (32 x 100K, G = 128: 326 -> 283 us; 16 x 128K: 218 -> 190 us).  The
+// two-wave kernels read every page twice, the second wave mostly from
+// cache, and keep ordinary loads (non-temporal: 284 -> 323 us on the ragged
+// GQA-8 batch).
+template <bool STREAM>
+__device__ __forceinline__ v4i load16(const uint8_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  else return *reinterpret_cast<const v4i*>(p);
+}
+
+template <int G, bool STREAM>
 __device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ blk, int lane) {
   constexpr int NG = kDim / G;
   const int n = lane & 15;
-  r.kw[0] = *reinterpret_cast<const v4i*>(blk + lane * 16);
-  r.kw[1] = *reinterpret_cast<const v4i*>(blk + 1024 + lane * 16);
-  r.vw[0] = *reinterpret_cast<const v4i*>(blk + 2048 + lane * 16);
-  r.vw[1] = *reinterpret_cast<const v4i*>(blk + 3072 + lane * 16);
-  const uint32_t* ks = reinterpret_cast<const uint32_t*>(blk + kCodesBytes) + n * 4 * NG;
-  const uint32_t* vs = reinterpret_cast<const uint32_t*>(blk + kCodesBytes + kPage * NG * 4) + n * 4 * NG;
+  r.kw[0] = load16<STREAM>(blk + lane * 16);
+  r.kw[1] = load16<STREAM>(blk + 1024 + lane * 16);
+  r.vw[0] = load16<STREAM>(blk + 2048 + lane * 16);
+  r.vw[1] = load16<STREAM>(blk + 3072 + lane * 16);
+  const uint8_t* ks = blk + kCodesBytes + n * 16 * NG;
+  const uint8_t* vs = blk + kCodesBytes + kPage * NG * 4 + n * 16 * NG;
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    const v4i a = reinterpret_cast<const v4i*>(ks)[i];
-    const v4i b = reinterpret_cast<const v4i*>(vs)[i];
+    const v4i a = load16<STREAM && OSCAR_STREAM_SZ>(ks + 16 * i);
+    const v4i b = load16<STREAM && OSCAR_STREAM_SZ>(vs + 16 * i);
     r.ksz[4 * i + 0] = a.x; r.ksz[4 * i + 1] = a.y; r.ksz[4 * i + 2] = a.z; r.ksz[4 * i + 3] = a.w;
     r.vsz[4 * i + 0] = b.x; r.vsz[4 * i + 1] = b.y; r.vsz[4 * i + 2] = b.z; r.vsz[4 * i + 3] = b.w;
   }
@@ -613,7 +630,7 @@ hist_mfma_kernel(MfmaParams a) {
     PageRegs<G> buf[BUF];
 #pragma unroll
     for (int k = 0; k < BUF - 1; ++k) {
-      load_page<G>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+      load_page<G, WAVES == 1>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
       // keep the pages' loads in page order, the order the loop issues them
       // in: the loop head's wait then covers only the page it needs first
       __builtin_amdgcn_sched_barrier(0);
@@ -625,7 +642,7 @@ hist_mfma_kernel(MfmaParams a) {
     for (int it = 0; it < groups; ++it, p += BUF) {
 #pragma unroll
       for (int k = 0; k < BUF; ++k) {
-        load_page<G>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
+        load_page<G, WAVES == 1>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
         process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
       }
     }
