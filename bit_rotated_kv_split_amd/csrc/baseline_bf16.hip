@@ -78,10 +78,18 @@ __global__ void __launch_bounds__(64) base_hist_kernel(BaseParams a) {
 #pragma unroll
     for (int v8 = 0; v8 < kDim / 8; ++v8) krow[v8] = row[v8];
   };
+  // value rows are read whole by each load (16 lanes per 256-byte row) and
+  // once per page: non-temporal, as in the INT2 kernel.  The key loads stay
+  // ordinary: a lane reads its own token's row, so each cache line serves
+  // eight consecutive loads (non-temporal key loads doubled the traffic).
   auto load_v = [&](int p) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const uint16_t* vb = block(p) + kPage * kDim;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vrow[i] = *reinterpret_cast<const uint4*>(vb + (res + 4 * i) * kDim + 8 * cg);
+    for (int i = 0; i < 16; ++i) {
+      const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(vb + (res + 4 * i) * kDim + 8 * cg));
+      vrow[i] = make_uint4(w.x, w.y, w.z, w.w);
+    }
   };
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
