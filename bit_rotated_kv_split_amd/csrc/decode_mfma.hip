@@ -83,11 +83,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #endif
 // G = 32 pages carry four scale/zero pairs per token and K/V (48 VGPRs a
 // buffer); its Lloyd-Max form keeps one buffer (two spill)
-// scale/zero entries loaded non-temporally too (one-wave kernels); off:
-// with them ordinary the 32 x 100K launch took 282.5 against 287.9 us
-#ifndef OSCAR_STREAM_SZ
-#define OSCAR_STREAM_SZ 0
-#endif
 #ifndef OSCAR_HIST_BUFFERS_32
 #define OSCAR_HIST_BUFFERS_32 2
 #endif
@@ -227,7 +222,9 @@ __device__ __forceinline__ v4i load16(const uint8_t* p) {
   else return *reinterpret_cast<const v4i*>(p);
 }
 
-template <int G, bool STREAM>
+// STREAM_SZ: the scale/zero entries non-temporal too (the kernel decides
+// per instantiation)
+template <int G, bool STREAM, bool STREAM_SZ>
 __device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ blk, int lane) {
   constexpr int NG = kDim / G;
   const int n = lane & 15;
@@ -239,8 +236,8 @@ __device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restr
   const uint8_t* vs = blk + kCodesBytes + kPage * NG * 4 + n * 16 * NG;
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    const v4i a = load16<STREAM && OSCAR_STREAM_SZ>(ks + 16 * i);
-    const v4i b = load16<STREAM && OSCAR_STREAM_SZ>(vs + 16 * i);
+    const v4i a = load16<STREAM_SZ>(ks + 16 * i);
+    const v4i b = load16<STREAM_SZ>(vs + 16 * i);
     r.ksz[4 * i + 0] = a.x; r.ksz[4 * i + 1] = a.y; r.ksz[4 * i + 2] = a.z; r.ksz[4 * i + 3] = a.w;
     r.vsz[4 * i + 0] = b.x; r.vsz[4 * i + 1] = b.y; r.vsz[4 * i + 2] = b.z; r.vsz[4 * i + 3] = b.w;
   }
@@ -522,6 +519,10 @@ __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu
 hist_mfma_kernel(MfmaParams a) {
   constexpr int NHB = 1;
   constexpr int NG = kDim / G;
+  // non-temporal scale/zero loads pay only for the one-wave uniform G = 64
+  // kernel (32 x 100K: 326.7 -> 320.9 us); at G = 128 (282.5 -> 287.9 us),
+  // G = 32 (457 -> 471 us) and with the Lloyd-Max codebook they cost time
+  constexpr bool kStreamSz = WAVES == 1 && G == 64 && !LM;
   // 1-D grid: every history split slot first (workgroups are dispatched in
   // id order, so these are the resident ones), then the bf16 chunks, which
   // fill the slots freed as history splits finish.  Slots beyond the
@@ -630,7 +631,7 @@ hist_mfma_kernel(MfmaParams a) {
     PageRegs<G> buf[BUF];
 #pragma unroll
     for (int k = 0; k < BUF - 1; ++k) {
-      load_page<G, WAVES == 1>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
+      load_page<G, WAVES == 1, kStreamSz>(buf[k], page_ptr(min(p0 + k, p_last)), lane);
       // keep the pages' loads in page order, the order the loop issues them
       // in: the loop head's wait then covers only the page it needs first
       __builtin_amdgcn_sched_barrier(0);
@@ -642,7 +643,7 @@ hist_mfma_kernel(MfmaParams a) {
     for (int it = 0; it < groups; ++it, p += BUF) {
 #pragma unroll
       for (int k = 0; k < BUF; ++k) {
-        load_page<G, WAVES == 1>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
+        load_page<G, WAVES == 1, kStreamSz>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
         process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
       }
     }
