@@ -180,6 +180,106 @@ def test_rotations_orthogonal(tiny_calibration):
         assert np.abs(r.T @ r - np.eye(128)).max() <= 1e-6
 
 
+def _brute_value_outputs(q, k, v):
+    """Causal softmax attention outputs, one query row at a time (explicit
+    two-pass softmax), for the calibration-wiring pin."""
+    n = q.shape[0]
+    out = np.zeros((n, 128))
+    for i in range(n):
+        sc = np.array([float(np.dot(q[i], k[t])) for t in range(i + 1)]) / math.sqrt(128)
+        w = np.exp(sc - sc.max())
+        out[i] = (w[:, None] * v[:i + 1]).sum(axis=0) / w.sum()
+    return out
+
+
+def _wiring_inputs():
+    """A small GQA-2 calibration set whose query covariance and score-weighted
+    value covariance differ strongly: queries with log-normal channel scales
+    and a mean, values with two x10 channels, keys correlated with queries."""
+    r = rng(41)
+    n, g, hkv = 96, 2, 2
+    qs = np.exp(r.standard_normal(128))
+    q = r.standard_normal((n, g * hkv, 128)) * qs + 0.2 * qs
+    k = r.standard_normal((n, hkv, 128)) + 0.3 * q[:, ::g, :] / qs.max()
+    v = r.standard_normal((n, hkv, 128))
+    v[:, :, 5] *= 10
+    v[:, :, 77] *= 10
+    return q, k, v, g
+
+
+def _wiring_failures(cal, q, k, v, g):
+    """What P2 and the clip definition fix about calibrate()'s outputs, per KV
+    head j, with C_Q and C_S recomputed here from their definitions:
+    diag(R_K^T C_Q R_K) and diag(R_V^T C_S R_V) are uniform at tr/128, the
+    crossed pairings are not, and clip_k / clip_v are the 99.9th percentiles
+    of |k R_K| / |v R_V| per channel."""
+    bad = []
+    for j in range(k.shape[1]):
+        rows = q[:, j * g:(j + 1) * g, :].reshape(-1, 128)
+        c_q = rows.T @ rows / rows.shape[0]
+        outs = np.concatenate([_brute_value_outputs(q[:, h, :], k[:, j], v[:, j])
+                               for h in range(j * g, (j + 1) * g)])
+        c_s = outs.T @ outs / outs.shape[0]
+        rk, rv = cal["r_k"][j], cal["r_v"][j]
+
+        def spread(r, c):
+            return np.abs(np.diag(r.T @ c @ r) - np.trace(c) / 128).max() / np.trace(c)
+
+        if spread(rk, c_q) > 1e-10:
+            bad.append(f"kvh {j}: diag(R_K^T C_Q R_K) not uniform")
+        if spread(rv, c_s) > 1e-10:
+            bad.append(f"kvh {j}: diag(R_V^T C_S R_V) not uniform")
+        if spread(rk, c_s) < 1e-3 or spread(rv, c_q) < 1e-3:
+            bad.append(f"kvh {j}: a crossed pairing is uniform too (inputs do not separate them)")
+        ck = np.percentile(np.abs(k[:, j] @ rk), 99.9, axis=0).astype(np.float32)
+        cv = np.percentile(np.abs(v[:, j] @ rv), 99.9, axis=0).astype(np.float32)
+        if not np.array_equal(cal["clip_k"][j], ck):
+            bad.append(f"kvh {j}: clip_k is not the p99.9 of |k R_K|")
+        if not np.array_equal(cal["clip_v"][j], cv):
+            bad.append(f"kvh {j}: clip_v is not the p99.9 of |v R_V|")
+    return bad
+
+
+def test_calibrate_pairs_each_rotation_with_its_covariance():
+    """P2 on calibrate() as a whole ([A] section "OSCAR 的不同之处": R_K from
+    the eigenvectors of C_Q, R_V from those of C_S = V^T S^T S V / N), GQA 2,
+    and the clip thresholds from the matching rotation."""
+    q, k, v, g = _wiring_inputs()
+    cal = O.calibrate(q, k, v, 99.9)
+    assert _wiring_failures(cal, q, k, v, g) == []
+
+
+def test_calibrate_wiring_pin_catches_planted_mistakes():
+    """Copies of calibrate_head with one plausible mistake each fail the
+    wiring pin: U_Q and U_S swapped, clip_v taken from the keys, C_S built
+    from pre-softmax scores, and the query group of the wrong KV head."""
+    q, k, v, g = _wiring_inputs()
+
+    def variant(mistake):
+        heads = []
+        for j in range(k.shape[1]):
+            jq = (j + 1) % k.shape[1] if mistake == "group" else j
+            qj, kj, vj = q[:, jq * g:(jq + 1) * g, :], k[:, j, :], v[:, j, :]
+            _, u_q = O.eig_descending(O.query_covariance(qj))
+            if mistake == "scores":
+                s = np.concatenate([np.tril(qj[:, h] @ kj.T / math.sqrt(128)) @ vj for h in range(g)])
+                c_s = s.T @ s / s.shape[0]
+            else:
+                c_s = O.score_weighted_value_covariance(qj, kj, vj)
+            _, u_s = O.eig_descending(c_s)
+            if mistake == "swap":
+                u_q, u_s = u_s, u_q
+            r_k, r_v = O.composite_rotation(u_q), O.composite_rotation(u_s)
+            clip_v = O.clip_thresholds(kj if mistake == "clip" else vj, r_v, 99.9)
+            heads.append({"r_k": r_k, "r_v": r_v, "clip_k": O.clip_thresholds(kj, r_k, 99.9),
+                          "clip_v": clip_v})
+        return {key: np.stack([h[key] for h in heads]) for key in heads[0]}
+
+    for mistake in ("swap", "clip", "scores", "group"):
+        assert _wiring_failures(variant(mistake), q, k, v, g), mistake
+    assert _wiring_failures(variant("none"), q, k, v, g) == []
+
+
 def test_calibration_spreads_outlier_channels(tiny_calibration):
     cal, (_, k, _) = tiny_calibration
     raw_max = np.percentile(np.abs(k[:, 0]), 99.9, axis=0)
