@@ -290,7 +290,7 @@ __device__ __forceinline__ float acc_value(const WaveState<NHB, G>& st, int hb, 
 
 template <bool LM, int NHB, int G>
 __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[NHB][4],
-                                    const PageRegs<G>& cur, const bool (&need)[NHB],
+                                    const uint32_t (&vsz)[4 * (kDim / G)], const bool (&need)[NHB],
                                     HistSmem<NHB, kDim / G>& sm, int lane, float ka, float kb) {
   constexpr int NG = kDim / G;
   // P' of this lane's tokens (residue j = n % 4 in the K-slot order) meets
@@ -319,7 +319,7 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float p = exp2f(sc[hb][m] - m_new);
-        wmax = fmaxf(wmax, p * __uint_as_float(cur.vsz[m * NG + gi] << 16));
+        wmax = fmaxf(wmax, p * __uint_as_float(vsz[m * NG + gi] << 16));
       }
       wmax = row_reduce(wmax, MaxOp());
       const float u = fmaxf(wmax, 1e-30f) * (kHeadroom / kDigitUnitMax);
@@ -412,12 +412,21 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       sc[hb][m] = s;
     }
   }
+  // value scale/zero of this lane's tokens; on the request's last page the
+  // slots past its end hold whatever the page held before (stale or never
+  // written bytes, NaN or Inf included): their pairs are zeroed with their
+  // scores, so a weight of 0 never meets them (0 * Inf and 0 * NaN are NaN)
+  uint32_t vsz[4 * NG];
+#pragma unroll
+  for (int i = 0; i < 4 * NG; ++i) vsz[i] = cur.vsz[i];
   if (tok_base + kPage > n_hist) {   // the request's last page (uniform)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const bool valid = tok_base + 16 * (n >> 2) + 4 * m + (n & 3) < n_hist;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) sc[hb][m] = valid ? sc[hb][m] : -INFINITY;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) vsz[m * NG + gi] = valid ? vsz[m * NG + gi] : 0u;
     }
   }
   // ---- p against the reference max, P' in units of the head's fixed point
@@ -431,7 +440,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
-        xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
+        xv[hb][gi][m] = pr[hb][m] * __uint_as_float(vsz[m * NG + gi] << 16) * st.inv[hb][gi];
         xmax = fmaxf(xmax, xv[hb][gi][m]);
       }
     }
@@ -446,7 +455,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) need[hb] = force || ((mask >> (16 * lg)) & 0xFFFFull) != 0;
     if (force) st.since_fold = 0;
-    rebase<LM, NHB, G>(st, sc, cur, need, sm, lane, ka, kb);
+    rebase<LM, NHB, G>(st, sc, vsz, need, sm, lane, ka, kb);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -454,7 +463,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
         pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
-          xv[hb][gi][m] = pr[hb][m] * __uint_as_float(cur.vsz[m * NG + gi] << 16) * st.inv[hb][gi];
+          xv[hb][gi][m] = pr[hb][m] * __uint_as_float(vsz[m * NG + gi] << 16) * st.inv[hb][gi];
       }
   }
   // ---- P' digits into the operand rows, l and zero-point partial sums
@@ -468,7 +477,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       float zpage = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t sz = cur.vsz[m * NG + gi];
+        const uint32_t sz = vsz[m * NG + gi];
         float vz = __uint_as_float(sz & 0xFFFF0000u);
         if constexpr (LM) vz = __builtin_fmaf(-lm_hi, __uint_as_float(sz << 16), vz);
         zpage = __builtin_fmaf(pr[hb][m], vz, zpage);
@@ -730,7 +739,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int hist_default_target(const oscar_dims& d) {
+int hist_default_target(const oscar_dims& d, int simds) {
   // the workgroups the matrix-core kernel for these dims keeps resident:
   // SIMDs x waves per SIMD / waves per workgroup
   const bool two = d.num_q_heads / d.num_kv_heads > 4;
@@ -746,7 +755,7 @@ int hist_default_target(const oscar_dims& d) {
     if (lm) waves = two ? HistShape<64, 2, true>::MINW : HistShape<64, 1, true>::MINW;
     else waves = two ? HistShape<64, 2, false>::MINW : HistShape<64, 1, false>::MINW;
   }
-  return kSimds * waves / (two ? 2 : 1);
+  return simds * waves / (two ? 2 : 1);
 }
 
 bool hist_mfma_supported(const oscar_dims& d) {

@@ -110,11 +110,17 @@ def new_tokens_tensor(model: SyntheticModel, layout: Layout, step_lens, which: s
 
 
 def build_cache(w: configs.Workload, layout: Layout, model: SyntheticModel, rot: Rotation,
-                device: str = "cuda", chunk_tokens: int = 16384) -> PagedKVCache:
+                device: str = "cuda", chunk_tokens: int = 16384, stale_byte=None) -> PagedKVCache:
     """Allocate the cache and fill it to the layout's lengths: sink and recent
-    from the GPU generator, history through the library's bulk demotion."""
+    from the GPU generator, history through the library's bulk demotion.
+    With stale_byte set, every byte of the pages and of the sink/recent
+    buffers holds that value before the fill, so the slots past each
+    request's end keep it (0xFF: bf16 NaN scale/zero pairs, code 3)."""
     cache = PagedKVCache(w.num_q_heads, w.num_kv_heads, w.group_size, w.batch, layout.max_pages,
                          layout.n_pages, device, codebook=w.codebook)
+    if stale_byte is not None:
+        for t in (cache.pages, cache.sink_k, cache.sink_v, cache.recent_k, cache.recent_v):
+            t.view(torch.uint8).fill_(stale_byte)
     cache.page_table.copy_(torch.from_numpy(layout.page_table))
     cache.seq_lens.copy_(torch.from_numpy(layout.lens.astype(np.int32)))
     stream = torch.cuda.current_stream().cuda_stream
