@@ -60,6 +60,11 @@ class OscarBf16Cache(ctypes.Structure):
                 ("seq_lens", ctypes.c_void_p), ("batch", ctypes.c_int32)]
 
 
+class OscarDecodeOptions(ctypes.Structure):
+    _fields_ = [("history_kernel", ctypes.c_int32), ("history_target", ctypes.c_int32),
+                ("history_start_event", ctypes.c_void_p), ("history_stop_event", ctypes.c_void_p)]
+
+
 # (name, restype, argtypes) of every exported function
 _P = ctypes.POINTER
 _SIGS = [
@@ -73,17 +78,30 @@ _SIGS = [
     ("oscar_kv_read_history", ctypes.c_int, [_P(OscarDims), _P(OscarCache), ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("oscar_history_splits", ctypes.c_int32, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
+    ("oscar_history_splits_ex", ctypes.c_int32, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32,
+                                                 _P(OscarDecodeOptions)]),
     ("oscar_decode_workspace_bytes", ctypes.c_size_t, [_P(OscarDims), ctypes.c_int32, ctypes.c_int32]),
     ("oscar_decode_attn", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    ("oscar_decode_attn_ex", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_size_t, _P(OscarDecodeOptions), ctypes.c_void_p]),
     ("oscar_decode", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_decode_ex", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p, ctypes.c_void_p, _P(OscarDecodeOptions),
+                                       ctypes.c_void_p]),
     ("oscar_decode_step", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]),
+    ("oscar_decode_step_ex", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                            _P(OscarDecodeOptions), ctypes.c_void_p]),
     ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -97,7 +115,6 @@ _SIGS = [
     ("oscar_read_history_schedule", ctypes.c_int, [_P(OscarDims), ctypes.c_int32, ctypes.c_void_p,
                                                    ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int32, ctypes.c_void_p]),
-    ("oscar_set_history_kernel", ctypes.c_int, [ctypes.c_int]),
     ("oscar_bf16_block_bytes", ctypes.c_size_t, []),
     ("oscar_bf16_fill", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -107,10 +124,13 @@ _SIGS = [
     ("oscar_bf16_decode", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]),
-    ("oscar_set_history_target", ctypes.c_int, [ctypes.c_int32]),
-    ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims)]),
-    ("oscar_set_history_events", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    ("oscar_bf16_decode_ex", ctypes.c_int, [_P(OscarDims), _P(OscarBf16Cache), ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                            _P(OscarDecodeOptions), ctypes.c_void_p]),
+    ("oscar_history_kernel_for", ctypes.c_int, [_P(OscarDims), _P(OscarDecodeOptions)]),
     ("oscar_last_error", ctypes.c_char_p, []),
+    ("oscar_probe_read", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
 
@@ -179,6 +199,30 @@ def oscar_codebook(codebook: int):
     return lev, thr
 
 
+def _event_handle(ev):
+    """hipEvent_t of a HipEvent-like object (``.ptr``), a torch event
+    (``.cuda_event``) or an int; None stays None."""
+    if ev is None:
+        return None
+    if hasattr(ev, "ptr"):
+        return ev.ptr
+    if hasattr(ev, "cuda_event"):
+        return ev.cuda_event
+    return ev
+
+
+def make_options(history_kernel: int = 0, history_target: int = 0, start_event=None,
+                 stop_event=None) -> OscarDecodeOptions:
+    """Per-call options of the decode entry points (oscar_decode_options)."""
+    o = OscarDecodeOptions(history_kernel, history_target, _event_handle(start_event), _event_handle(stop_event))
+    o._keep = (start_event, stop_event)
+    return o
+
+
+def _opt(options):
+    return None if options is None else ctypes.byref(options)
+
+
 def make_rotation(r_k, r_v, clip_k, clip_v) -> OscarRotation:
     rot = OscarRotation(_ptr(r_k), _ptr(r_v), _ptr(clip_k), _ptr(clip_v))
     rot._keep = (r_k, r_v, clip_k, clip_v)
@@ -224,8 +268,10 @@ def oscar_kv_read_history(dims, cache, request: int, hist_begin: int, n_tokens: 
                                        _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
-def oscar_history_splits(dims, batch: int, max_seq_len: int) -> int:
-    return lib().oscar_history_splits(ctypes.byref(dims), batch, max_seq_len)
+def oscar_history_splits(dims, batch: int, max_seq_len: int, options=None) -> int:
+    if options is None:
+        return lib().oscar_history_splits(ctypes.byref(dims), batch, max_seq_len)
+    return lib().oscar_history_splits_ex(ctypes.byref(dims), batch, max_seq_len, _opt(options))
 
 
 def oscar_decode_workspace_bytes(dims, batch: int, max_seq_len: int) -> int:
@@ -233,24 +279,36 @@ def oscar_decode_workspace_bytes(dims, batch: int, max_seq_len: int) -> int:
 
 
 def oscar_decode_attn(dims, rot, cache, q, max_seq_len: int, workspace, workspace_bytes: int,
-                      stream=None) -> None:
-    _check(lib().oscar_decode_attn(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
-                                   _ptr(q), max_seq_len, _ptr(workspace), workspace_bytes,
-                                   _stream(stream)))
+                      stream=None, options=None) -> None:
+    """oscar_decode_attn, or oscar_decode_attn_ex when options are given."""
+    args = (ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(q), max_seq_len, _ptr(workspace),
+            workspace_bytes)
+    if options is None:
+        _check(lib().oscar_decode_attn(*args, _stream(stream)))
+    else:
+        _check(lib().oscar_decode_attn_ex(*args, _opt(options), _stream(stream)))
 
 
 def oscar_decode(dims, rot, cache, q, max_seq_len: int, workspace, workspace_bytes: int, out,
-                 lse_out=None, stream=None) -> None:
-    _check(lib().oscar_decode(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(q),
-                              max_seq_len, _ptr(workspace), workspace_bytes, _ptr(out),
-                              _ptr(lse_out), _stream(stream)))
+                 lse_out=None, stream=None, options=None) -> None:
+    """oscar_decode, or oscar_decode_ex when options are given."""
+    args = (ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(q), max_seq_len, _ptr(workspace),
+            workspace_bytes, _ptr(out), _ptr(lse_out))
+    if options is None:
+        _check(lib().oscar_decode(*args, _stream(stream)))
+    else:
+        _check(lib().oscar_decode_ex(*args, _opt(options), _stream(stream)))
 
 
 def oscar_decode_step(dims, rot, cache, k_new, v_new, q, max_seq_len: int, workspace,
-                      workspace_bytes: int, out, lse_out=None, stream=None) -> None:
-    _check(lib().oscar_decode_step(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
-                                   _ptr(k_new), _ptr(v_new), _ptr(q), max_seq_len, _ptr(workspace),
-                                   workspace_bytes, _ptr(out), _ptr(lse_out), _stream(stream)))
+                      workspace_bytes: int, out, lse_out=None, stream=None, options=None) -> None:
+    """oscar_decode_step, or oscar_decode_step_ex when options are given."""
+    args = (ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(q),
+            max_seq_len, _ptr(workspace), workspace_bytes, _ptr(out), _ptr(lse_out))
+    if options is None:
+        _check(lib().oscar_decode_step(*args, _stream(stream)))
+    else:
+        _check(lib().oscar_decode_step_ex(*args, _opt(options), _stream(stream)))
 
 
 def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspace_bytes: int,
@@ -288,7 +346,9 @@ def oscar_read_history_schedule(dims, batch: int, workspace, workspace_bytes: in
     """(splits int32 [n][3] {request, first page, end page}, requests int32
     [batch][2] {first split, count}) of the last decode on this workspace."""
     import numpy as np
-    cap = lib().oscar_history_splits(ctypes.byref(dims), batch, 1)
+    # capacity of the workspace's split table: the largest target's bound
+    cap = lib().oscar_history_splits_ex(ctypes.byref(dims), batch, 1,
+                                        ctypes.byref(make_options(history_target=8192)))
     splits = np.zeros((max(cap, 1), 3), dtype=np.int32)
     reqs = np.zeros((batch, 2), dtype=np.int32)
     n = lib().oscar_read_history_schedule(ctypes.byref(dims), batch, _ptr(workspace), workspace_bytes,
@@ -319,34 +379,23 @@ def oscar_bf16_decode_workspace_bytes(dims, batch: int) -> int:
 
 
 def oscar_bf16_decode(dims, cache, q, max_seq_len: int, workspace, workspace_bytes: int, out,
-                      lse_out=None, stream=None) -> None:
-    _check(lib().oscar_bf16_decode(ctypes.byref(dims), ctypes.byref(cache), _ptr(q), max_seq_len,
-                                   _ptr(workspace), workspace_bytes, _ptr(out), _ptr(lse_out),
-                                   _stream(stream)))
+                      lse_out=None, stream=None, options=None) -> None:
+    """oscar_bf16_decode, or oscar_bf16_decode_ex when options are given."""
+    args = (ctypes.byref(dims), ctypes.byref(cache), _ptr(q), max_seq_len, _ptr(workspace), workspace_bytes,
+            _ptr(out), _ptr(lse_out))
+    if options is None:
+        _check(lib().oscar_bf16_decode(*args, _stream(stream)))
+    else:
+        _check(lib().oscar_bf16_decode_ex(*args, _opt(options), _stream(stream)))
 
 
-def oscar_set_history_kernel(kind: int) -> int:
-    prev = lib().oscar_set_history_kernel(kind)
-    if prev < 0:
-        raise OscarError(OSCAR_EINVAL, f"invalid history kernel {kind}")
-    return prev
+def oscar_history_kernel_for(dims, options=None) -> int:
+    return lib().oscar_history_kernel_for(ctypes.byref(dims), _opt(options))
 
 
-def oscar_set_history_target(workgroups: int) -> int:
-    prev = lib().oscar_set_history_target(workgroups)
-    if prev < 0:
-        raise OscarError(OSCAR_EINVAL, f"invalid history target {workgroups}")
-    return prev
-
-
-def oscar_history_kernel_for(dims) -> int:
-    return lib().oscar_history_kernel_for(ctypes.byref(dims))
-
-
-def oscar_set_history_events(before, after) -> None:
-    b = None if before is None else before.cuda_event if hasattr(before, "cuda_event") else before
-    a = None if after is None else after.cuda_event if hasattr(after, "cuda_event") else after
-    _check(lib().oscar_set_history_events(b, a))
+def oscar_probe_read(buf, nbytes: int, nontemporal: bool, sink, stream=None) -> None:
+    """One pass of the HBM read probe over nbytes of buf (include/oscar_probe.h)."""
+    _check(lib().oscar_probe_read(_ptr(buf), nbytes, 1 if nontemporal else 0, _ptr(sink), _stream(stream)))
 
 
 def oscar_last_error() -> str:

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 #include <string>
 
@@ -14,10 +15,10 @@ namespace oscar {
 namespace {
 
 thread_local std::string g_error;
-thread_local void* g_ev_before = nullptr;
-thread_local void* g_ev_after = nullptr;
-std::atomic<int> g_hist_kernel{0};
-std::atomic<int> g_hist_target{0};
+// Compute units of each device, read once from the device and kept (an
+// immutable hardware attribute, not a setting; 0 = not read yet).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -86,6 +87,75 @@ int check_bf16_cache(const oscar_bf16_cache* c) {
   return OSCAR_OK;
 }
 
+// SIMDs (4 per compute unit) of the current device.
+int current_device_simds(int* simds) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no current HIP device to size the default history target");
+  int cus = dev >= 0 && dev < kMaxDevices ? g_device_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(OSCAR_EHIP, "compute unit count of device %d: %s", dev, hipGetErrorString(e));
+    if (cus <= 0) return fail(OSCAR_EHIP, "device %d reports %d compute units", dev, cus);
+    if (dev >= 0 && dev < kMaxDevices) g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  *simds = 4 * cus;
+  return OSCAR_OK;
+}
+
+// Per-call options, validated, with the default target resolved for dims
+// when `need_target` (the split schedule is built in this call).
+struct CallOpts {
+  int kernel = 0;
+  int target_wg = 0;
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_stop = nullptr;
+};
+
+// The default target when none was given: the resident workgroups of the
+// history kernel on the current device (the bf16 baseline keeps a fixed
+// default).
+int resolve_target(const oscar_dims& d, bool bf16_baseline, CallOpts* c) {
+  if (c->target_wg != 0) return OSCAR_OK;
+  if (bf16_baseline) {
+    c->target_wg = d.num_q_heads / d.num_kv_heads > 4 ? kDefaultTargetWg / 2 : kDefaultTargetWg;
+    return OSCAR_OK;
+  }
+  int simds = 0;
+  const int rc = current_device_simds(&simds);
+  if (rc) return rc;
+  c->target_wg = std::min(hist_default_target(d, simds), kMaxTargetWg);
+  return OSCAR_OK;
+}
+
+int resolve_opts(const oscar_dims& d, const oscar_decode_options* o, bool need_target, bool bf16_baseline,
+                 CallOpts* out) {
+  CallOpts c;
+  if (o != nullptr) {
+    if (o->history_kernel < 0 || o->history_kernel > 2)
+      return fail(OSCAR_EINVAL, "history_kernel %d invalid (0 default, 1 vector-ALU, 2 matrix-core)",
+                  o->history_kernel);
+    if (bf16_baseline && o->history_kernel != 0)
+      return fail(OSCAR_EINVAL, "the bf16 baseline has one history kernel (history_kernel must be 0)");
+    if (o->history_target < 0 || o->history_target > kMaxTargetWg)
+      return fail(OSCAR_EINVAL, "history_target %d outside 0..%d", o->history_target, kMaxTargetWg);
+    c.kernel = o->history_kernel;
+    c.target_wg = o->history_target;
+    if (o->history_start_event != nullptr && o->history_stop_event != nullptr) {
+      c.ev_start = static_cast<hipEvent_t>(o->history_start_event);
+      c.ev_stop = static_cast<hipEvent_t>(o->history_stop_event);
+    }
+  }
+  if (c.kernel == 2 && !hist_mfma_supported(d))
+    return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
+  *out = c;
+  return need_target ? resolve_target(d, bf16_baseline, out) : OSCAR_OK;
+}
+
+bool use_mfma(const oscar_dims& d, const CallOpts& c) {
+  return c.kernel == 2 || (c.kernel == 0 && hist_mfma_supported(d));
+}
+
 int pages_for(int32_t max_seq_len) {
   const int n_hist = max_seq_len > kBf16Tokens ? max_seq_len - kBf16Tokens : 0;
   return (n_hist + kPage - 1) / kPage;
@@ -95,14 +165,15 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len) {
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+
+WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len, int target_wg) {
   (void)max_seq_len;
   WsLayout w;
-  // About as many history workgroups as the matrix-core history kernel keeps
-  // resident, unless set with oscar_set_history_target.
-  int target_wg = g_hist_target.load();
-  if (target_wg == 0) target_wg = hist_default_target(d);
-  const int t = (target_wg + d.num_kv_heads - 1) / d.num_kv_heads;
+  // the schedule of one call: about target_wg history workgroups (by
+  // default as many as the history kernel keeps resident)
+  const int t = (std::max(target_wg, 1) + d.num_kv_heads - 1) / d.num_kv_heads;
   w.target = t;
   w.slots = t + batch;
   // storage is sized for the largest target, so the layout (and the
@@ -175,29 +246,11 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
   return OSCAR_OK;
 }
 
-int oscar_set_history_kernel(int kind) {
-  if (kind < 0 || kind > 2) return -1;
-  return g_hist_kernel.exchange(kind);
-}
-
-int oscar_set_history_target(int32_t workgroups) {
-  if (workgroups < 0 || workgroups > kMaxTargetWg) return -1;
-  return g_hist_target.exchange(workgroups);
-}
-
-int oscar_history_kernel_for(const oscar_dims* dims) {
-  if (check_dims(dims)) return -1;
-  const int kind = g_hist_kernel.load();
-  const bool mfma_ok = hist_mfma_supported(*dims);
-  if (kind == 2) return mfma_ok ? 2 : -1;
-  if (kind == 1) return 1;
-  return mfma_ok ? 2 : 1;
-}
-
-int oscar_set_history_events(void* before, void* after) {
-  g_ev_before = before;
-  g_ev_after = after;
-  return OSCAR_OK;
+int oscar_history_kernel_for(const oscar_dims* dims, const oscar_decode_options* options) {
+  g_error.clear();
+  CallOpts c;
+  if (check_dims(dims) || resolve_opts(*dims, options, false, false, &c)) return -1;
+  return use_mfma(*dims, c) ? 2 : 1;
 }
 
 int oscar_kv_demote(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
@@ -257,14 +310,23 @@ int oscar_kv_read_history(const oscar_dims* dims, const oscar_cache* cache, int3
   return OSCAR_OK;
 }
 
+int32_t oscar_history_splits_ex(const oscar_dims* dims, int32_t batch, int32_t max_seq_len,
+                                const oscar_decode_options* options) {
+  g_error.clear();
+  CallOpts c;
+  if (check_dims(dims) || resolve_opts(*dims, options, true, false, &c)) return -1;
+  if (batch < 0 || max_seq_len < 0) return -1;
+  return workspace_layout(*dims, batch, max_seq_len, c.target_wg).slots;
+}
+
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
-  if (check_dims(dims) || batch < 0 || max_seq_len < 0) return -1;
-  return workspace_layout(*dims, batch, max_seq_len).slots;
+  return oscar_history_splits_ex(dims, batch, max_seq_len, nullptr);
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32_t max_seq_len) {
   if (check_dims(dims) || batch < 0 || max_seq_len < 0) return 0;
-  return workspace_layout(*dims, batch, max_seq_len).total;
+  // the layout holds kMaxTargetWg / Hkv + B splits whatever the target
+  return workspace_layout(*dims, batch, max_seq_len, kMaxTargetWg).total;
 }
 
 namespace {
@@ -274,27 +336,29 @@ namespace {
 int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                 float* out, float* lse_out, bool demote, const uint16_t* k_new, const uint16_t* v_new,
-                void* stream) {
+                const oscar_decode_options* options, void* stream) {
   g_error.clear();
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_rot(rot)) || (rc = check_cache(cache, true))) return rc;
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(OSCAR_EINVAL, "k_new and v_new must both be set or both be NULL");
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  CallOpts opt;
+  if ((rc = resolve_opts(*dims, options, false, false, &opt))) return rc;
   if (cache->batch == 0) return OSCAR_OK;
   if (q == nullptr || workspace == nullptr) return fail(OSCAR_EINVAL, "q or workspace is NULL");
   if (pages_for(max_seq_len) > cache->max_pages_per_req)
     return fail(OSCAR_EINVAL, "max_seq_len %d needs %d pages > max_pages_per_req %d", max_seq_len,
                 pages_for(max_seq_len), cache->max_pages_per_req);
-  const WsLayout lay = workspace_layout(*dims, cache->batch, max_seq_len);
-  if (workspace_bytes < lay.total)
-    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  // sizes and offsets do not depend on the target
+  const size_t need = workspace_layout(*dims, cache->batch, max_seq_len, kMaxTargetWg).total;
+  if (workspace_bytes < need)
+    return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
+  if ((rc = resolve_target(*dims, false, &opt))) return rc;
+  const WsLayout lay = workspace_layout(*dims, cache->batch, max_seq_len, opt.target_wg);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int kind = g_hist_kernel.load();
-  const bool use_mfma = kind == 2 || (kind == 0 && hist_mfma_supported(*dims));
-  if (kind == 2 && !hist_mfma_supported(*dims))
-    return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
+  const bool mfma = use_mfma(*dims, opt);
   DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
   DemoteStep dm;
   if (demote) {
@@ -303,14 +367,12 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   }
   hipError_t e = launch_qrot(a, s);
   if (e != hipSuccess) return hip_fail(e, "query rotation launch");
-  if (g_ev_before != nullptr && g_ev_after != nullptr) {
-    a.ev_start = static_cast<hipEvent_t>(g_ev_before);
-    a.ev_stop = static_cast<hipEvent_t>(g_ev_after);
-  }
+  a.ev_start = opt.ev_start;
+  a.ev_stop = opt.ev_stop;
   // the matrix-core launch also runs the bf16 sink/recent chunks
-  e = use_mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
+  e = mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
   if (e != hipSuccess) return hip_fail(e, "history launch");
-  if (!use_mfma) {
+  if (!mfma) {
     e = launch_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "bf16 launch");
   }
@@ -323,34 +385,55 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
 
 }  // namespace
 
+int oscar_decode_attn_ex(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                         const uint16_t* q, int32_t max_seq_len, void* workspace,
+                         size_t workspace_bytes, const oscar_decode_options* options, void* stream) {
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, nullptr, false,
+                     nullptr, nullptr, options, stream);
+}
+
 int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                       const uint16_t* q, int32_t max_seq_len, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, nullptr, false,
-                     nullptr, nullptr, stream);
+  return oscar_decode_attn_ex(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, nullptr, stream);
 }
 
-int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
-                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
-                 float* out, float* lse_out, void* stream) {
+int oscar_decode_ex(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                    const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                    float* out, float* lse_out, const oscar_decode_options* options, void* stream) {
   if (out == nullptr && cache != nullptr && cache->batch > 0) {
     g_error.clear();
     return fail(OSCAR_EINVAL, "out is NULL");
   }
   return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, false,
-                     nullptr, nullptr, stream);
+                     nullptr, nullptr, options, stream);
+}
+
+int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                 const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                 float* out, float* lse_out, void* stream) {
+  return oscar_decode_ex(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, nullptr,
+                         stream);
+}
+
+int oscar_decode_step_ex(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                         const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                         int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                         float* lse_out, const oscar_decode_options* options, void* stream) {
+  if (out == nullptr && cache != nullptr && cache->batch > 0) {
+    g_error.clear();
+    return fail(OSCAR_EINVAL, "out is NULL");
+  }
+  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, true,
+                     k_new, v_new, options, stream);
 }
 
 int oscar_decode_step(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
                       int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
                       float* lse_out, void* stream) {
-  if (out == nullptr && cache != nullptr && cache->batch > 0) {
-    g_error.clear();
-    return fail(OSCAR_EINVAL, "out is NULL");
-  }
-  return decode_impl(dims, rot, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, true,
-                     k_new, v_new, stream);
+  return oscar_decode_step_ex(dims, rot, cache, k_new, v_new, q, max_seq_len, workspace, workspace_bytes, out,
+                              lse_out, nullptr, stream);
 }
 
 int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,
@@ -362,7 +445,9 @@ int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t b
   if (batch < 0 || max_seq_len < 1) return fail(OSCAR_EINVAL, "batch %d / max_seq_len %d invalid", batch, max_seq_len);
   if (batch == 0) return OSCAR_OK;
   if (workspace == nullptr || out == nullptr) return fail(OSCAR_EINVAL, "workspace or out is NULL");
-  const WsLayout lay = workspace_layout(*dims, batch, max_seq_len);
+  // the merge reads the schedule the decode call wrote; its offsets do not
+  // depend on the target
+  const WsLayout lay = workspace_layout(*dims, batch, max_seq_len, kMaxTargetWg);
   if (workspace_bytes < lay.total)
     return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   const hipError_t e = launch_merge(*dims, *rot, batch, static_cast<const uint8_t*>(workspace), lay,
@@ -380,7 +465,7 @@ int oscar_read_history_schedule(const oscar_dims* dims, int32_t batch, const voi
   if (batch < 1) return -fail(OSCAR_EINVAL, "batch %d < 1", batch);
   if (workspace == nullptr || splits == nullptr || requests == nullptr)
     return -fail(OSCAR_EINVAL, "workspace, splits or requests is NULL");
-  const WsLayout lay = workspace_layout(*dims, batch, 1);
+  const WsLayout lay = workspace_layout(*dims, batch, 1, kMaxTargetWg);
   if (workspace_bytes < lay.total)
     return -fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -437,34 +522,38 @@ int oscar_bf16_append(const oscar_dims* dims, const oscar_bf16_cache* cache, con
 
 size_t oscar_bf16_decode_workspace_bytes(const oscar_dims* dims, int32_t batch) {
   if (check_dims(dims) || batch < 0) return 0;
-  return base_layout(*dims, batch, g_hist_target.load()).total;
+  return base_layout(*dims, batch, kMaxTargetWg).total;
 }
 
-int oscar_bf16_decode(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
-                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
-                      float* lse_out, void* stream) {
+int oscar_bf16_decode_ex(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
+                         int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                         float* lse_out, const oscar_decode_options* options, void* stream) {
   g_error.clear();
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_bf16_cache(cache))) return rc;
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  CallOpts opt;
+  if ((rc = resolve_opts(*dims, options, true, true, &opt))) return rc;
   if (cache->batch == 0) return OSCAR_OK;
   if (q == nullptr || workspace == nullptr || out == nullptr) return fail(OSCAR_EINVAL, "q, workspace or out is NULL");
   if ((max_seq_len + kPage - 1) / kPage > cache->max_pages_per_req)
     return fail(OSCAR_EINVAL, "max_seq_len %d needs %d pages > max_pages_per_req %d", max_seq_len,
                 (max_seq_len + kPage - 1) / kPage, cache->max_pages_per_req);
-  const BaseLayout lay = base_layout(*dims, cache->batch, g_hist_target.load());
+  const BaseLayout lay = base_layout(*dims, cache->batch, opt.target_wg);
   if (workspace_bytes < lay.total)
     return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned");
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (g_ev_before != nullptr && g_ev_after != nullptr) {
-    ev0 = static_cast<hipEvent_t>(g_ev_before);
-    ev1 = static_cast<hipEvent_t>(g_ev_after);
-  }
   const hipError_t e = launch_base_decode(*dims, *cache, q, static_cast<uint8_t*>(workspace), lay, out, lse_out,
-                                          static_cast<hipStream_t>(stream), ev0, ev1);
+                                          static_cast<hipStream_t>(stream), opt.ev_start, opt.ev_stop);
   if (e != hipSuccess) return hip_fail(e, "bf16 decode launch");
   return OSCAR_OK;
+}
+
+int oscar_bf16_decode(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
+                      int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse_out, void* stream) {
+  return oscar_bf16_decode_ex(dims, cache, q, max_seq_len, workspace, workspace_bytes, out, lse_out, nullptr,
+                              stream);
 }
 
 }  // extern "C"

@@ -17,12 +17,12 @@ constexpr int kBf16Parts = 5;
 constexpr int kMaxSplits = 251;
 // Smallest history split, in pages.
 constexpr int kMinSplitPages = 8;
-// SIMDs of the chip (256 compute units x 4); the history split schedule aims
-// by default for the workgroups the matrix-core history kernel keeps
-// resident on them (hist_default_target), so the splits run in one round.
-constexpr int kSimds = 1024;
+// The history split schedule aims by default for the workgroups the
+// matrix-core history kernel keeps resident on the device's SIMDs (4 per
+// compute unit, read from the device; hist_default_target), so the splits
+// run in one round.
 // Default target of the all-bf16 baseline (two one-wave workgroups per
-// SIMD; halved for query groups wider than four heads).
+// SIMD of a 256-CU MI355X; halved for query groups wider than four heads).
 constexpr int kDefaultTargetWg = 2048;
 // Largest settable target (bounds the workspace).
 constexpr int kMaxTargetWg = 8192;
@@ -60,7 +60,13 @@ constexpr size_t kQPackOperandBytes = 2 * 4 * kQPackRows * 16;  // 4096
 constexpr size_t kQPackScaleOffset = 2 * kQPackOperandBytes;
 constexpr size_t kQPackBytes = kQPackScaleOffset + 256;
 
-WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len);
+// target_wg: history workgroups the call's split schedule aims for (> 0);
+// the offsets and total do not depend on it.
+// Record `msg` as the calling thread's last error (oscar_last_error) and
+// return `code`.
+int set_error(int code, const char* msg);
+
+WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len, int target_wg);
 
 // Float32 levels (ascending) and decision thresholds of a codebook
 // (OSCAR_CODEBOOK_*); nullptr for an unknown one.
@@ -119,7 +125,8 @@ hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_hist_valu(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_hist_mfma(const DecodeArgs& a, hipStream_t s);
 bool hist_mfma_supported(const oscar_dims& d);
-int hist_default_target(const oscar_dims& d);
+// Workgroups of the matrix-core history kernel for dims resident on `simds` SIMDs.
+int hist_default_target(const oscar_dims& d, int simds);
 hipError_t launch_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t batch,
                         const uint8_t* ws, const WsLayout& lay, float* out, float* lse_out,

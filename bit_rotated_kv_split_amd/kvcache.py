@@ -95,9 +95,11 @@ class Rotation:
 
 
 class DecodeWorkspace:
-    """Workspace of one (batch, max_seq_len) decode configuration."""
+    """Workspace of one (batch, max_seq_len) decode configuration.  `splits`
+    is the split bound of the default schedule on the current device (or of
+    the given options')."""
 
-    def __init__(self, dims, batch: int, max_seq_len: int, device: str = "cuda"):
+    def __init__(self, dims, batch: int, max_seq_len: int, device: str = "cuda", options=None):
         self.batch = batch
         self.max_seq_len = max_seq_len
         self.nbytes = _lib.oscar_decode_workspace_bytes(dims, batch, max_seq_len)
@@ -105,13 +107,13 @@ class DecodeWorkspace:
             raise _lib.OscarError(_lib.OSCAR_EINVAL, _lib.oscar_last_error())
         # torch's caching allocator returns 512-byte aligned blocks
         self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
-        self.splits = _lib.oscar_history_splits(dims, batch, max_seq_len)
+        self.splits = _lib.oscar_history_splits(dims, batch, max_seq_len, options)
 
 
 def decode_step(cache: PagedKVCache, rot: Rotation, ws: DecodeWorkspace, q, out, lse=None,
-                k_new=None, v_new=None, stream=None) -> None:
+                k_new=None, v_new=None, stream=None, options=None) -> None:
     """One decode step on the current stream (oscar_decode_step): demote (and
     append k_new/v_new if given), decode attention, merge.  seq_lens must
     already count the new token."""
     _lib.oscar_decode_step(cache.dims, rot.struct, cache.struct(), k_new, v_new, q, ws.max_seq_len,
-                           ws.buf, ws.nbytes, out, lse, stream)
+                           ws.buf, ws.nbytes, out, lse, stream, options)

@@ -181,17 +181,45 @@ int oscar_kv_fill_history(const oscar_dims* dims, const oscar_rotation* rot,
 int oscar_kv_read_history(const oscar_dims* dims, const oscar_cache* cache, int32_t request,
                           int32_t hist_begin, int32_t n_tokens, float* k_out, float* v_out, void* stream);
 
+/* Per-call choices of the decode calls (the *_ex entry points; a NULL
+ * pointer, and the entry points without _ex, take every default).  The
+ * library keeps no setting between calls: two threads passing different
+ * options each get their own kernel and schedule.
+ *   history_kernel  0 = default (the matrix-core kernel), 1 = vector-ALU
+ *                   kernel, 2 = matrix-core (MFMA) kernel; both cover every
+ *                   supported dims.
+ *   history_target  history workgroups the split schedule aims for
+ *                   (oscar_history_splits); 0 = default: the workgroups the
+ *                   history kernel for these dims keeps resident on the
+ *                   current device (4 SIMDs per compute unit x waves per
+ *                   SIMD / waves per workgroup), at most 8192.
+ *   history_start_event, history_stop_event
+ *                   hipEvent_t or NULL: when both are set, the history
+ *                   launch is made with hipExtLaunchKernelGGL with these as
+ *                   its start and stop events, so their elapsed time is that
+ *                   kernel's execution (a timing hook). */
+typedef struct oscar_decode_options {
+  int32_t history_kernel;
+  int32_t history_target;
+  void* history_start_event;
+  void* history_stop_event;
+} oscar_decode_options;
+
 /* Upper bound on the history splits per KV head that oscar_decode_attn
  * schedules for a batch of this size.  The splits themselves are chosen on
- * the device from the lengths: with T = ceil(W / Hkv) and W the
- * oscar_set_history_target value (default 2048; 1024 when Hq/Hkv > 4), the
- * pages per split q is the smallest q >= max(8, ceil(longest / 251)) for
- * which the batch needs at most T splits, request b taking
- * ceil(pages_b / q) splits of equal size (the last one shorter); if one
- * split per request already exceeds T, q is the longest request's page
- * count.  The bound returned is T + B; -1 for invalid arguments.
- * max_seq_len is not used. */
+ * the device from the lengths: with T = ceil(W / Hkv) and W the options'
+ * history_target (by default the history kernel's resident workgroups on
+ * the current device: 2048 on a 256-CU MI355X, 1536 for eight-head groups
+ * at G = 128 and 1024 for other eight-head groups), the pages per split q
+ * is the smallest q >= max(8, ceil(longest / 251)) for which the batch
+ * needs at most T splits, request b taking ceil(pages_b / q) splits of
+ * equal size (the last one shorter); if one split per request already
+ * exceeds T, q is the longest request's page count.  The bound returned is
+ * T + B; -1 for invalid arguments, or when the default target is asked for
+ * and no HIP device is present.  max_seq_len is not used. */
 int32_t oscar_history_splits(const oscar_dims* dims, int32_t batch, int32_t max_seq_len);
+int32_t oscar_history_splits_ex(const oscar_dims* dims, int32_t batch, int32_t max_seq_len,
+                                const oscar_decode_options* options);
 
 /* Workspace bytes oscar_decode_attn / oscar_merge_lse need (device memory,
  * 256-byte aligned, owned by the caller; no initialisation required). */
@@ -212,6 +240,10 @@ size_t oscar_decode_workspace_bytes(const oscar_dims* dims, int32_t batch, int32
 int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot,
                       const oscar_cache* cache, const uint16_t* q, int32_t max_seq_len,
                       void* workspace, size_t workspace_bytes, void* stream);
+int oscar_decode_attn_ex(const oscar_dims* dims, const oscar_rotation* rot,
+                         const oscar_cache* cache, const uint16_t* q, int32_t max_seq_len,
+                         void* workspace, size_t workspace_bytes,
+                         const oscar_decode_options* options, void* stream);
 
 /* Decode attention with the merge in one call: oscar_decode_attn followed
  * by oscar_merge_lse on the same stream (out float32 [B][Hq][128], lse_out
@@ -219,6 +251,9 @@ int oscar_decode_attn(const oscar_dims* dims, const oscar_rotation* rot,
 int oscar_decode(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
                  const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                  float* out, float* lse_out, void* stream);
+int oscar_decode_ex(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                    const uint16_t* q, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                    float* out, float* lse_out, const oscar_decode_options* options, void* stream);
 
 /* One whole decode step: oscar_kv_demote(k_new, v_new) then
  * oscar_decode, in three launches instead of four (the demotion runs in the
@@ -229,12 +264,24 @@ int oscar_decode_step(const oscar_dims* dims, const oscar_rotation* rot, const o
                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
                       int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
                       float* lse_out, void* stream);
+int oscar_decode_step_ex(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                         const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                         int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                         float* lse_out, const oscar_decode_options* options, void* stream);
 
-/* Log-sum-exp merge: combine the history partials, rotate the history
- * output back by R_V^T, merge it with the sink/recent partial and write
- * out: float32 [B][Hq][128].  lse_out (may be NULL): float32 [B][Hq], the
- * natural-log log-sum-exp of all scores.  batch and max_seq_len must equal
- * those given to oscar_decode_attn for this workspace. */
+/* Log-sum-exp merge (second page, section "OSCAR的另一个关键点是": the
+ * INT2 history and the bf16 sink/recent results are combined by an
+ * online-softmax merge; first page, section "OSCAR 的不同之处": values are
+ * stored as v . R_V, so the history output is rotated back by R_V^T).
+ * With M the largest partial log-sum-exp, the merged output is
+ * sum_i e^(lse_i - M) O_i / sum_i e^(lse_i - M) and its log-sum-exp
+ * M + ln sum_i e^(lse_i - M); empty partials (lse = -inf) are skipped.  The
+ * history splits are merged first, in the rotated value domain, then
+ * multiplied by R_V^T and merged with the five sink/recent partials.
+ * Writes out: float32 [B][Hq][128].  lse_out (may be NULL): float32 [B][Hq],
+ * the natural-log log-sum-exp of all scores.  batch and max_seq_len must
+ * equal those given to oscar_decode_attn for this workspace; the workspace
+ * is only read. */
 int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,
                     int32_t max_seq_len, const void* workspace, size_t workspace_bytes,
                     float* out, float* lse_out, void* stream);
@@ -272,28 +319,9 @@ int oscar_calibrate(const oscar_dims* dims, int32_t n_tokens, const float* q, co
                     float* clip_v, double* r_k_host, double* r_v_host, void* workspace,
                     size_t workspace_bytes, void* stream);
 
-/* Which history kernel oscar_decode_attn launches: 0 = default (the
- * matrix-core kernel), 1 = vector-ALU kernel, 2 = matrix-core (MFMA) kernel.
- * Both cover every supported dims.
- * Process-wide setting.  Returns the previous value, or -1 for an invalid one. */
-int oscar_set_history_kernel(int kind);
-
-/* How many history workgroups the split schedule of oscar_decode_attn aims
- * for (see oscar_history_splits); 0 = default (2048; 1024 when Hq/Hkv > 4,
- * whose workgroups hold two waves), at most 8192.  Process-wide; the
- * workspace layout does not depend on it.  Returns the previous value, or
- * -1 for a value out of range. */
-int oscar_set_history_target(int32_t workgroups);
-
-/* History kernel the current selection launches for dims: 1 = vector-ALU,
- * 2 = matrix-core; -1 for invalid dims or an unsupported forced choice. */
-int oscar_history_kernel_for(const oscar_dims* dims);
-
-/* Optional timing hook: when both are non-NULL, oscar_decode_attn launches
- * the history kernel with hipEvent_t `before` and `after` as its start and
- * stop events (hipExtLaunchKernelGGL), so their elapsed time is that
- * kernel's execution.  Thread-local; NULL clears it. */
-int oscar_set_history_events(void* before, void* after);
+/* History kernel a decode call with these options launches for dims:
+ * 1 = vector-ALU, 2 = matrix-core; -1 for invalid dims or options. */
+int oscar_history_kernel_for(const oscar_dims* dims, const oscar_decode_options* options);
 
 /* Copy the history-split schedule that the last oscar_decode_attn on this
  * workspace wrote (device) to the host: splits (host int32 [capacity][3])
@@ -341,12 +369,16 @@ size_t oscar_bf16_decode_workspace_bytes(const oscar_dims* dims, int32_t batch);
 /* Decode attention over the bf16 cache: q bf16 [B][Hq][128] -> out float32
  * [B][Hq][128], lse_out float32 [B][Hq] (natural log) or NULL.  One softmax
  * over all L tokens with scale 1/sqrt(128).  Split-K over pages with the
- * same schedule rule as oscar_decode_attn (no tokens skipped), then a merge;
- * three launches.  The oscar_set_history_events hook times the split-K
- * launch. */
+ * same schedule rule as oscar_decode_attn (no tokens skipped; default
+ * target 2048 workgroups, 1024 for eight-head groups), then a merge; three
+ * launches.  With _ex, history_target sets the schedule's target and the
+ * two events time the split-K launch; history_kernel must be 0. */
 int oscar_bf16_decode(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
                       int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
                       float* lse_out, void* stream);
+int oscar_bf16_decode_ex(const oscar_dims* dims, const oscar_bf16_cache* cache, const uint16_t* q,
+                         int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                         float* lse_out, const oscar_decode_options* options, void* stream);
 
 /* Thread-local text of the last error ("" if none). */
 const char* oscar_last_error(void);

@@ -71,3 +71,31 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = "", atol: float =
     err = np.abs(got - ref).max()
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     assert err <= atol and rel <= rel_l2, f"{what}: max-abs {err:.3e} rel-L2 {rel:.3e}"
+
+
+def assert_demoted_slot(page_block: np.ndarray, slot: int, k_bits: np.ndarray, v_bits: np.ndarray,
+                        r_k32, r_v32, clip_k, clip_v, group: int, codebook: str, what: str = "") -> None:
+    """One demoted history slot of a (page, KV head) block read back from the
+    GPU against the oracle's demotion of the same bf16 token (k_bits,
+    v_bits [128]).  Scale and zero are bit-exact; codes are equal except
+    where (y - zero) / scale lies within 1e-5 (relative) of a level boundary,
+    the tolerance of the acceptance bar for the rotation's last-bit
+    rounding."""
+    got = O.unpack_block(page_block, group)
+    for which, bits, r, c, (gc, gs, gz) in (("k", k_bits, r_k32, clip_k, got[0:3]),
+                                            ("v", v_bits, r_v32, clip_v, got[3:6])):
+        y = O.clip(O.rotate(O.bf16_value(bits[None, :]), r), c)
+        codes, s, z = O.quantize(y, group, codebook)
+        assert np.array_equal(gs[slot], s[0]) and np.array_equal(gz[slot], z[0]), f"{what} {which} scale/zero"
+        diff = gc[slot] != codes[0]
+        if diff.any():
+            sr = np.repeat(s[0], group).astype(np.float64)
+            zr = np.repeat(z[0], group).astype(np.float64)
+            t = (y[0].astype(np.float64) - zr) / np.where(sr == 0, 1, sr)
+            if codebook == "uniform":
+                near = np.abs(t - np.floor(t) - 0.5) <= 1e-5 * np.maximum(np.abs(t), 1)
+            else:
+                _, thr = O.lloyd_max_codebook()
+                near = np.min(np.abs(t[:, None] - thr[None, :].astype(np.float64)), axis=1) <= \
+                    1e-5 * np.maximum(np.abs(t), 1)
+            assert not (diff & ~near).any(), f"{what} {which} codes differ away from a level boundary"

@@ -22,17 +22,14 @@ def small(name, seed, hq, hkv, lens, paged=True):
 
 
 def run(cache, q, max_len, target=0):
-    prev = ok.oscar_set_history_target(target)
-    try:
-        nb = ok.oscar_bf16_decode_workspace_bytes(cache.dims, cache.batch)
-        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        out = torch.full((cache.batch, cache.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
-        lse = torch.full((cache.batch, cache.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
-        ok.oscar_bf16_decode(cache.dims, cache.struct(), q, max_len, ws, nb, out, lse)
-        torch.cuda.synchronize()
-        return out.cpu().numpy(), lse.cpu().numpy()
-    finally:
-        ok.oscar_set_history_target(prev)
+    opts = ok.make_options(history_target=target) if target else None
+    nb = ok.oscar_bf16_decode_workspace_bytes(cache.dims, cache.batch)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.full((cache.batch, cache.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((cache.batch, cache.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    ok.oscar_bf16_decode(cache.dims, cache.struct(), q, max_len, ws, nb, out, lse, options=opts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
 
 
 def check(w, layout, model, out, lse, requests=None):

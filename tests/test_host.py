@@ -14,9 +14,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "oscar.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
+    """Functions declared by every header under include/."""
+    names = set()
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -37,34 +42,55 @@ def test_block_bytes():
 
 def test_workspace_and_splits():
     d = ok.make_dims(32, 8, 128)
-    s = ok.oscar_history_splits(d, 32, 100_000)
-    # default target 2048 / 8 splits per KV head, plus the batch
+    tgt = lambda n: ok.make_options(history_target=n)   # noqa: E731
+    # target 2048 -> 2048 / 8 splits per KV head, plus the batch
+    s = ok.oscar_history_splits(d, 32, 100_000, tgt(2048))
     assert s == 256 + 32
-    assert ok.oscar_history_splits(d, 32, 1000) == s        # lengths decide on the device
+    assert ok.oscar_history_splits(d, 32, 1000, tgt(2048)) == s        # lengths decide on the device
     # partials for 8192 / 8 + B history splits and five bf16 chunks per head
     assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) >= (1056 * 32 + 32 * 32 * 5) * 129 * 4
-    # 8-wide groups take two-wave workgroups: three waves per SIMD at G = 128
-    # (1536 workgroups), two at G = 64 and with the Lloyd-Max codebook (1024)
-    gqa8 = ok.make_dims(64, 8, 128)
-    assert ok.oscar_history_splits(gqa8, 4, 1000) == 192 + 4
-    assert ok.oscar_history_splits(ok.make_dims(64, 8, 64), 4, 1000) == 128 + 4
-    assert ok.oscar_history_splits(ok.make_dims(64, 8, 128, codebook=ok.CODEBOOK_LLOYD_MAX), 4, 1000) == 128 + 4
-    prev = ok.oscar_set_history_target(64)
-    try:
-        assert ok.oscar_history_splits(d, 32, 100_000) == 8 + 32
-        # the layout does not follow the target
-        assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) == \
-            ok.oscar_decode_workspace_bytes(d, 32, 10)
-        ok.oscar_set_history_target(1)
-        assert ok.oscar_history_splits(d, 2, 100_000) == 1 + 2
-    finally:
-        ok.oscar_set_history_target(prev)
+    assert ok.oscar_history_splits(d, 32, 100_000, tgt(64)) == 8 + 32
+    assert ok.oscar_history_splits(d, 2, 100_000, tgt(1)) == 1 + 2
+    assert ok.oscar_history_splits(ok.make_dims(64, 8, 128), 4, 1000, tgt(1536)) == 192 + 4
+    # the layout does not follow the target
+    assert ok.oscar_decode_workspace_bytes(d, 32, 100_000) == ok.oscar_decode_workspace_bytes(d, 32, 10)
     for bad_target in (-1, 8193):
-        with pytest.raises(ok.OscarError):
-            ok.oscar_set_history_target(bad_target)
+        assert ok.oscar_history_splits(d, 2, 1000, tgt(bad_target)) == -1
+        assert "history_target" in ok.oscar_last_error()
     bad = ok.make_dims(32, 8, 128, head_dim=64)
     assert ok.oscar_decode_workspace_bytes(bad, 1, 1000) == 0
-    assert ok.oscar_history_splits(bad, 1, 1000) == -1
+    assert ok.oscar_history_splits(bad, 1, 1000, tgt(2048)) == -1
+
+
+def test_default_target_needs_a_device_here():
+    """The default target is read from the current device's compute units;
+    with no HIP device (this CPU-only host) the sizing call says so instead
+    of assuming a chip."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a HIP device is present (covered by the GPU tests)")
+    assert ok.oscar_history_splits(ok.make_dims(32, 8, 128), 32, 100_000) == -1
+    assert "device" in ok.oscar_last_error()
+
+
+def test_invalid_options_are_rejected_before_anything_runs():
+    d = ok.make_dims(4, 2, 64)
+    for o in (ok.make_options(history_kernel=7), ok.make_options(history_kernel=-1),
+              ok.make_options(history_target=-5), ok.make_options(history_target=9000)):
+        with pytest.raises(ok.OscarError) as e:
+            ok.oscar_decode_attn(d, _rot(), _cache(batch=0), None, 100, None, 0, 0, options=o)
+        assert e.value.code == ok.OSCAR_EINVAL
+        with pytest.raises(ok.OscarError):
+            ok.oscar_decode_step(d, _rot(), _cache(batch=0), None, None, None, 100, None, 0, None, None, 0,
+                                 options=o)
+        assert ok.oscar_history_kernel_for(d, o) == -1
+    # the bf16 baseline has a single history kernel
+    with pytest.raises(ok.OscarError):
+        ok.oscar_bf16_decode(d, ok.make_bf16_cache(0, 0, 0, 0, 0, 0), None, 100, None, 0, None, None, 0,
+                             options=ok.make_options(history_kernel=1))
+    # valid options on an empty batch: nothing to do, no device needed
+    ok.oscar_decode(d, _rot(), _cache(batch=0), None, 100, None, 0, None, None, 0,
+                    options=ok.make_options(history_kernel=1, history_target=64))
 
 
 def _cache(batch=1):
@@ -156,11 +182,20 @@ def test_empty_batch_and_zero_tokens_are_no_ops():
     ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 0, 0, None, None, 0)
 
 
+def test_probe_rejects_misaligned_buffers():
+    for buf, n in ((0x1001, 4096), (0x1000, 4095), (0, 4096)):
+        with pytest.raises(ok.OscarError) as e:
+            ok.oscar_probe_read(buf, n, True, 0x1000, 0)
+        assert e.value.code == ok.OSCAR_EINVAL
+    ok.oscar_probe_read(0x1000, 0, False, 0x1000, 0)    # nothing to read
+
+
 def test_history_kernel_selector():
-    prev = ok.oscar_set_history_kernel(1)
-    assert ok.oscar_set_history_kernel(prev) == 1
-    with pytest.raises(ok.OscarError):
-        ok.oscar_set_history_kernel(7)
+    d = ok.make_dims(32, 8, 128)
+    assert ok.oscar_history_kernel_for(d) == 2
+    assert ok.oscar_history_kernel_for(d, ok.make_options(history_kernel=1)) == 1
+    assert ok.oscar_history_kernel_for(d, ok.make_options(history_kernel=2)) == 2
+    assert ok.oscar_history_kernel_for(d, ok.make_options(history_kernel=7)) == -1
 
 
 def test_codebook_constants_equal_the_oracle():
@@ -185,11 +220,8 @@ def test_history_kernel_choice_by_codebook_and_group():
         for cb in (ok.CODEBOOK_UNIFORM, ok.CODEBOOK_LLOYD_MAX):
             for hq in (8, 32, 64):
                 assert ok.oscar_history_kernel_for(ok.make_dims(hq, 8, g, codebook=cb)) == 2
-    prev = ok.oscar_set_history_kernel(1)
-    try:
-        assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 32, codebook=ok.CODEBOOK_LLOYD_MAX)) == 1
-    finally:
-        ok.oscar_set_history_kernel(prev)
+    assert ok.oscar_history_kernel_for(ok.make_dims(32, 8, 32, codebook=ok.CODEBOOK_LLOYD_MAX),
+                                       ok.make_options(history_kernel=1)) == 1
 
 
 def test_last_error_is_thread_local():
