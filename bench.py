@@ -4,14 +4,29 @@
 A step is one pass of the whole hot path over the batch (oscar_decode_step):
 append + demotion, query rotation and the split schedule in one launch; INT2
 history split-K + bf16 sink/recent in a second; LSE merge + value
-un-rotation in a third.  Inputs
-(cache, queries, new tokens, lengths) are resident in HBM before timing
-starts; every step appends one token per request, so lengths grow by one.
+un-rotation in a third.  Inputs (cache, queries, new tokens, lengths) are
+resident in HBM before timing starts; every step appends one token per
+request, so lengths grow by one.
 
 Default workload: 32 requests at 100K context, 32 query / 8 KV heads,
 head_dim 128, G = 128, paged cache (64-token pages, seeded random page
 permutation), synthetic seeded data; rotations and clips calibrated by the
 library from a synthetic calibration sequence before timing.
+
+Order of one run:
+  1. calibration, cache fill, per-step inputs (untimed);
+  2. bandwidth probes: a streaming HBM read (non-temporal and plain loads)
+     repeated for about 0.3 s, and a 2 GiB copy.  They give the read
+     ceiling the roofline is compared against, and they leave the GPU at
+     its steady clocks, so the timed steps do not measure the clock ramp
+     that follows the idle setup;
+  3. `warmup` untimed steps, then exactly `steps` timed steps: `value`,
+     `ms_per_step`, the history launch's `roofline` and per-quarter means;
+  4. `cold_start`: after 1 s with the GPU idle, 20 more timed steps with no
+     warm-up (diagnostic: the cost of starting from idle clocks);
+  5. the all-bf16 baseline's steps (the 32 x 100K workloads);
+  6. the oracle on the host cores (`cpu_baseline`), in worker processes
+     started before the GPU is touched.
 
 Prints ONE JSON line.
 """
@@ -32,6 +47,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PAGE = 64
 METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 100K ctx, batch 32"
+COLD_STEPS = 20
+COLD_IDLE_S = 1.0
 
 
 def workloads():
@@ -104,70 +121,158 @@ def _host_cpu():
     return model, os.cpu_count() or 1
 
 
-def cpu_baseline(model, layout, cal_host, lens, n_heads: int, budget_s: float = 10.0,
-                 single_budget_s: float = 4.0):
-    """Time the oracle (as it stands) on whole requests of the same workload
-    at their final length, request 0 first, until about budget_s seconds of
-    oracle work with numpy's default threads, then again single-threaded
-    (BLAS limited to one thread) for about single_budget_s; each scaled to
-    GB/s of the same algorithmic bytes.  The sample's tokens come from the GPU
-    twin of the seeded generator (bit-identical to synth.gen; not timed)."""
-    import torch
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle in worker processes (one BLAS thread each)
+
+def _oracle_worker(conn) -> None:
+    """Body of one oracle worker process.  Receives ("task", args) messages
+    (the arguments of oracle.request_attention for one (request, KV head)
+    pair, plus its algorithmic bytes), holds them until ("go",), then runs
+    them back to back and replies (start, end, bytes, count) on the
+    system-wide monotonic clock; ("stop",) ends the process."""
+    from threadpoolctl import threadpool_limits
     from oracle import oscar as O
+    tasks = []
+    with threadpool_limits(limits=1):
+        while True:
+            msg = conn.recv()
+            if msg[0] == "task":
+                tasks.append(msg[1])
+            elif msg[0] == "go":
+                t0 = time.monotonic()
+                nbytes = 0
+                for args, nb in tasks:
+                    O.request_attention(*args)
+                    nbytes += nb
+                t1 = time.monotonic()
+                conn.send((t0, t1, nbytes, len(tasks)))
+                tasks = []
+            else:
+                break
+
+
+class OracleWorkers:
+    """Worker processes for the oracle's CPU baseline.  They are started
+    (spawned, with one-thread BLAS in their environment) before this process
+    touches the GPU, and only ever run numpy."""
+
+    def __init__(self, n: int):
+        import multiprocessing as mp
+        ctx = mp.get_context("spawn")
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in saved:
+            os.environ[k] = "1"
+        self.conns, self.procs = [], []
+        try:
+            for _ in range(n):
+                a, b = ctx.Pipe()
+                p = ctx.Process(target=_oracle_worker, args=(b,), daemon=True)
+                p.start()
+                self.conns.append(a)
+                self.procs.append(p)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+
+    def run(self, assignments):
+        """assignments[w] = list of (args, bytes) for worker w; all workers
+        start together.  Returns (bytes, wall seconds, per-worker busy seconds)."""
+        used = [w for w, tasks in enumerate(assignments) if tasks]
+        for w in used:
+            for t in assignments[w]:
+                self.conns[w].send(("task", t))
+        for w in used:
+            self.conns[w].send(("go",))
+        res = [self.conns[w].recv() for w in used]
+        wall = max(r[1] for r in res) - min(r[0] for r in res)
+        return sum(r[2] for r in res), wall, [r[1] - r[0] for r in res]
+
+    def close(self):
+        for c in self.conns:
+            try:
+                c.send(("stop",))
+            except (OSError, BrokenPipeError):
+                pass
+        for p in self.procs:
+            p.join(timeout=10)
+
+
+def cpu_baseline(workers: OracleWorkers, model, layout, cal_host, lens, parallel_requests: int = 6,
+                 single_pairs: int = 12):
+    """The oracle (as it stands) on the host cores, at the workload's final
+    lengths, one (request, KV head) pair per task: demote the pair's history
+    and attend in float64 (oracle.request_attention).  The parallel leg gives
+    the pairs of requests 0 .. parallel_requests-1 (every KV head) to all
+    workers at once; the single-thread leg runs `single_pairs` pairs (KV
+    head 0 of successive requests) on one worker.  Both are scaled to GB/s
+    of the same algorithmic bytes.  The pairs' tokens come from the GPU twin
+    of the seeded generator (bit-identical to synth.gen; not timed)."""
+    import torch
     from synth import gpu as synth_gpu
     w = model.w
-    g = w.gqa
+    g, hkv = w.gqa, w.num_kv_heads
     stream = torch.cuda.current_stream().cuda_stream
     codebook = ("uniform", "lloyd-max")[w.codebook]
+    q_all = model.queries(0, w.batch)
 
-    def request_inputs(b):
+    def pair_tasks(b, heads):
         L = int(lens[b])
         host = {}
         for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
-            buf = torch.empty((L, n_heads, 128), dtype=torch.int16, device="cuda")
-            sc = torch.from_numpy(np.ascontiguousarray(scale[:n_heads])).cuda()
+            buf = torch.empty((L, hkv, 128), dtype=torch.int16, device="cuda")
+            sc = torch.from_numpy(np.ascontiguousarray(scale)).cuda()
             for src, p0, n in layout.src_ranges(b, 0, L):
-                synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * n_heads * 128, n, n_heads, n_heads * 128, 128,
+                synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * hkv * 128, n, hkv, hkv * 128, 128,
                                   w.seed, which, src, p0, sc, stream)
             torch.cuda.synchronize()
             host[which] = buf.cpu().numpy().view(np.uint16)
             del buf
-        return L, host
+        nb = step_bytes(np.array([L]), 1, g, w.group_size)[1]
+        out = []
+        for j in heads:
+            args = (q_all[b][j * g:(j + 1) * g], np.ascontiguousarray(host["k"][:, j:j + 1]),
+                    np.ascontiguousarray(host["v"][:, j:j + 1]), cal_host["r_k32"][j:j + 1],
+                    cal_host["r_v32"][j:j + 1], cal_host["clip_k"][j:j + 1], cal_host["clip_v"][j:j + 1],
+                    w.group_size, codebook)
+            out.append((args, nb))
+        return out
 
-    def run(budget, heads):
-        spent, done_bytes, reqs = 0.0, 0, 0
-        for b in range(w.batch):
-            L, host = request_inputs(b)
-            q = model.queries(0, w.batch)[b][: heads * g]
-            t0 = time.perf_counter()
-            O.request_attention(q, host["k"][:, :heads], host["v"][:, :heads], cal_host["r_k32"][:heads],
-                                cal_host["r_v32"][:heads], cal_host["clip_k"][:heads], cal_host["clip_v"][:heads],
-                                w.group_size, codebook)
-            spent += time.perf_counter() - t0
-            done_bytes += step_bytes(np.array([L]), heads, heads * g, w.group_size)[1]
-            reqs += 1
-            if spent >= budget:
-                break
-        return spent, done_bytes, reqs
-
-    spent, done_bytes, reqs = run(budget_s, n_heads)
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        cores = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
-        with threadpool_limits(limits=1):
-            s1, b1, r1 = run(single_budget_s, 1)
-        single = {"value": round(b1 / s1 / 1e9, 4), "seconds": round(s1, 3),
-                  "sample": f"requests 0..{r1 - 1}, KV head 0 only, one thread"}
-    except Exception:
-        cores, single = 1, None
+    n = len(workers.conns)
+    reqs = list(range(min(parallel_requests, w.batch)))
+    tasks = [t for b in reqs for t in pair_tasks(b, range(hkv))]
+    assign = [tasks[i::n] for i in range(n)]
+    par_bytes, par_wall, busy = workers.run(assign)
+    single = [t for b in range(min(single_pairs, w.batch)) for t in pair_tasks(b, [0])]
+    one_bytes, one_wall, _ = workers.run([single] + [[] for _ in range(n - 1)])
     cpu_model, nproc = _host_cpu()
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(spent, 3),
-            "sample": f"requests 0..{reqs - 1} of {w.batch}, {n_heads} of {w.num_kv_heads} KV heads each, "
-                      f"at their final lengths: the oracle demotes each history and attends in float64 "
-                      f"(numpy); {done_bytes / 1e9:.3f} GB of the step's algorithmic bytes",
-            "single_thread": single, "host_cpu": cpu_model, "host_logical_cores": nproc}
+    return {"value": round(par_bytes / par_wall / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "seconds": round(par_wall, 3),
+            "sample": f"{len(tasks)} (request, KV head) pairs: requests 0..{reqs[-1]} of {w.batch}, all "
+                      f"{hkv} KV heads, at their final lengths; each pair's history demoted and attended in "
+                      f"float64 by the oracle (numpy), {n} worker processes with one BLAS thread each, "
+                      f"{par_bytes / 1e9:.3f} GB of the step's algorithmic bytes",
+            "worker_busy_s": [round(x, 3) for x in busy],
+            "single_thread": {"value": round(one_bytes / one_wall / 1e9, 4), "seconds": round(one_wall, 3),
+                              "sample": f"{len(single)} pairs (KV head 0 of requests 0..{len(single) - 1}), "
+                                        f"one worker, one thread"},
+            "parallel_speedup": round((par_bytes / par_wall) / (one_bytes / one_wall), 2),
+            "host_cpu": cpu_model, "host_logical_cores": nproc}
 
+
+def cpu_worker_count() -> int:
+    """Worker processes for the oracle baseline: this process's CPU share,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ----------------------------------------------------------------------------
 
 def default_layers(workload: str) -> int:
     """Independent layer caches a run cycles through: the single-request
@@ -180,31 +285,82 @@ def pct(xs, q):
     return round(float(np.percentile(np.asarray(xs), q)), 2)
 
 
+def quarters(xs):
+    """Means of the first and the last quarter of a sequence of timings."""
+    xs = np.asarray(xs, dtype=np.float64)
+    k = max(1, len(xs) // 4)
+    return [round(float(xs[:k].mean()), 2), round(float(xs[-k:].mean()), 2)]
+
+
+def bandwidth_probes(ok, torch, HipEvent, stream, settle_s: float = 0.3, nbytes: int = 4 << 30):
+    """HBM read ceiling (the library's read probe over nbytes, non-temporal
+    and plain 16-byte loads, alternated for about settle_s seconds; median
+    GB/s of the second half of each kind's passes) and a device copy of
+    nbytes / 2 (read + write bytes / time, median of 5; the 2 GiB copy the
+    traffic counters are scaled by)."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    times = {True: [], False: []}
+    t_end = time.perf_counter() + settle_s
+    e0, e1 = HipEvent(), HipEvent()
+    while time.perf_counter() < t_end or min(len(v) for v in times.values()) < 6:
+        for nt in (True, False):
+            e0.record(stream)
+            ok.oscar_probe_read(buf, nbytes, nt, sink, stream)
+            e1.record(stream)
+            e1.synchronize()
+            times[nt].append(e0.elapsed_ms(e1))
+    rates = {}
+    for nt, ts in times.items():
+        ts = ts[len(ts) // 2:]
+        rates[nt] = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    copies = []
+    for _ in range(5):
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        copies.append(e0.elapsed_ms(e1))
+    copy_gbs = 2 * half / (float(np.median(copies)) * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"read_nontemporal_gbs": round(rates[True], 1), "read_plain_gbs": round(rates[False], 1),
+            "read_ceiling_gbs": round(max(rates.values()), 1), "copy_gbs": round(copy_gbs, 1),
+            "passes": len(times[True]) + len(times[False]), "buffer_bytes": nbytes}
+
+
 def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (0: the workload's own count, 100 for b1-100k and 200 for "
                          "b32-ragged-gqa8, else 100)")
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first (the GPU's clocks settle over the first tens of steps)")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the timed ones")
     ap.add_argument("--workload", default="b32-100k-g128", choices=sorted(workloads()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--layers", type=int, default=0,
                     help="independent layer caches cycled one per step (0: 10 for b1-100k, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads in the oracle sample")
+    ap.add_argument("--no-cold-start", action="store_true", help="skip the idle-start diagnostic leg")
     ap.add_argument("--bf16-baseline", choices=["auto", "on", "off"], default="auto",
                     help="also time the all-bf16 cache decode step (auto: on for the 32 x 100K workloads)")
     ap.add_argument("--history-target", type=int, default=0,
                     help="history workgroups the split schedule aims for (0: the library default)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="accepted for older command lines; the 2 GiB copy probe always runs")
+                    help="accepted for older command lines; the probes always run")
+    ap.add_argument("--trace-file", default="",
+                    help="also write every timed step's step and history-launch times (µs) to this JSON file")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path runs within one MI355X and "
               "launches no collectives; --gpus must be 1", file=sys.stderr)
         return 2
+
+    # the oracle's worker processes start before anything touches the GPU
+    workers = None if args.no_cpu_baseline else OracleWorkers(cpu_worker_count())
 
     import torch
     import bit_rotated_kv_split_amd as ok
@@ -216,7 +372,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     w = workloads()[args.workload]()
     steps, warmup = args.steps or (w.steps if w.steps > 1 else 100), args.warmup
-    total = steps + warmup
+    n_cold = 0 if args.no_cold_start else COLD_STEPS
+    total = steps + warmup + n_cold
     n_layers = args.layers or default_layers(args.workload)
     appends = -(-total // n_layers)          # tokens each layer cache receives
     layout = W.Layout(w, None, extra_tokens=appends)
@@ -262,93 +419,101 @@ def main() -> int:
     kn_all = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).cuda()
     vn_all = torch.from_numpy(vn.view(np.int16)).view(torch.bfloat16).cuda()
     max_len = int(lens_t.max())
-    ok.oscar_set_history_target(args.history_target)
-    ws = DecodeWorkspace(dims, B, max_len)
+    kind = {"auto": 0, "valu": 1, "mfma": 2}[args.kernel]
+    base_opts = ok.make_options(history_kernel=kind, history_target=args.history_target)
+    ws = DecodeWorkspace(dims, B, max_len, options=base_opts)
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     structs = [[ok.make_cache(c.pages, c.n_pages, c.sink_k, c.sink_v, c.recent_k, c.recent_v, c.page_table,
                               c.max_pages_per_req, seq_dev[t].data_ptr(), B) for t in range(appends)]
                for c in caches]
-    kind = {"auto": 0, "valu": 1, "mfma": 2}[args.kernel]
-    ok.oscar_set_history_kernel(kind)
 
-    def timed_run(one_step):
-        """Warm up, then time `steps` steps: per-step and history-launch events."""
-        ev_b = [HipEvent() for _ in range(steps)]
-        ev_a = [HipEvent() for _ in range(steps)]
-        marks = [HipEvent() for _ in range(steps + 1)]
-        for s in range(warmup):
-            ok.oscar_set_history_events(None, None)
-            one_step(s)
+    def timed_run(one_step, first: int, n_warm: int, n_timed: int):
+        """Steps first .. first+n_warm-1 untimed, then n_timed steps timed:
+        events around each step and around each history launch."""
+        ev_b = [HipEvent() for _ in range(n_timed)]
+        ev_a = [HipEvent() for _ in range(n_timed)]
+        marks = [HipEvent() for _ in range(n_timed + 1)]
+        opts = [ok.make_options(kind, args.history_target, ev_b[i], ev_a[i]) for i in range(n_timed)]
+        for s in range(n_warm):
+            one_step(first + s, base_opts)
         torch.cuda.synchronize()
-        for i in range(steps):
+        for i in range(n_timed):
             marks[i].record(stream)
-            ok.oscar_set_history_events(ev_b[i].ptr, ev_a[i].ptr)
-            one_step(warmup + i)
-        marks[steps].record(stream)
-        marks[steps].synchronize()
+            one_step(first + n_warm + i, opts[i])
+        marks[n_timed].record(stream)
+        marks[n_timed].synchronize()
         torch.cuda.synchronize()
-        ok.oscar_set_history_events(None, None)
-        step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]
-        hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(steps)]
+        step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(n_timed)]
+        hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(n_timed)]
         return step_us, hist_us
 
-    def int2_step(s: int):
+    def int2_step(s: int, opts):
         t = s // n_layers
         ok.oscar_decode_step(dims, rot.struct, structs[s % n_layers][t], kn_all[t], vn_all[t], q_all[s], max_len,
-                             ws.buf, ws.nbytes, out, None, stream)
+                             ws.buf, ws.nbytes, out, None, stream, options=opts)
 
     print(f"[bench] {w.name}: B={B} Hq={hq} Hkv={hkv} G={w.group_size} L0={int(layout.lens.min())}.."
           f"{int(layout.lens.max())} layers={n_layers} slots={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
           file=sys.stderr, flush=True)
-    step_us, k3_us = timed_run(int2_step)
+    probes = bandwidth_probes(ok, torch, HipEvent, stream)
+    step_us, k3_us = timed_run(int2_step, 0, warmup, steps)
     step_ms = sum(step_us) / steps / 1e3
 
-    kname = "mfma" if ok.oscar_history_kernel_for(dims) == 2 else "valu"
-    # the timed launch: history splits, plus the bf16 sink/recent chunks when
-    # the matrix-core kernel runs them in the same launch
-    launch_tot = 0
-    step_tot = 0
-    unique_tot = 0
-    for i in range(steps):
-        lens_i = lens_step[warmup + i]
-        hb, sb = step_bytes(lens_i, hkv, hq, w.group_size)
-        launch_tot += hb + (bf16_bytes(lens_i, hkv) if kname == "mfma" else 0)
-        step_tot += sb
-        shared_tok = PAGE * (sum(layout.shared_pages) - layout.chain_len) if layout.chain_len else 0
-        unique_tot += sb - shared_tok * hkv * hist_unit_bytes(w.group_size)
+    kname = "mfma" if ok.oscar_history_kernel_for(dims, base_opts) == 2 else "valu"
+    shared_tok = PAGE * (sum(layout.shared_pages) - layout.chain_len) if layout.chain_len else 0
+
+    def byte_totals(first: int, n: int):
+        """(history launch bytes, step bytes, unique step bytes) summed over
+        steps first .. first+n-1: the launch holds the history splits, plus
+        the bf16 sink/recent chunks when the matrix-core kernel runs them."""
+        launch = stp = uniq = 0
+        for i in range(n):
+            lens_i = lens_step[first + i]
+            hb, sb = step_bytes(lens_i, hkv, hq, w.group_size)
+            launch += hb + (bf16_bytes(lens_i, hkv) if kname == "mfma" else 0)
+            stp += sb
+            uniq += sb - shared_tok * hkv * hist_unit_bytes(w.group_size)
+        return launch, stp, uniq
+
+    launch_tot, step_tot, unique_tot = byte_totals(warmup, steps)
     k3_gbs = launch_tot / (sum(k3_us) * 1e-6) / 1e9
     value = step_tot / (sum(step_us) * 1e-6) / 1e9
     traffic = load_traffic(args.workload, kname)
 
-    # bandwidth reference: one 2 GiB device copy
-    nb = 2 << 30
-    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = HipEvent(), HipEvent()
-    c0.record(stream)
-    dst.copy_(src)
-    c1.record(stream)
-    c1.synchronize()
-    copy_gbs = round(2 * nb / (c0.elapsed_ms(c1) * 1e-3) / 1e9, 1)
-    del src, dst
+    trace = {"step_us": step_us, "history_us": k3_us}
+    cold = None
+    if n_cold:
+        torch.cuda.synchronize()
+        time.sleep(COLD_IDLE_S)
+        c_step, c_k3 = timed_run(int2_step, warmup + steps, 0, n_cold)
+        trace.update(cold_step_us=c_step, cold_history_us=c_k3)
+        c_launch, c_stp, _ = byte_totals(warmup + steps, n_cold)
+        c_k3_gbs = c_launch / (sum(c_k3) * 1e-6) / 1e9
+        cold = {"idle_s": COLD_IDLE_S, "warmup": 0, "steps": n_cold,
+                "us_per_step": round(sum(c_step) / n_cold, 2), "history_us": round(sum(c_k3) / n_cold, 2),
+                "history_frac": round(c_k3_gbs / PEAK_HBM_GBS, 4),
+                "quarters_step_us": quarters(c_step), "quarters_history_us": quarters(c_k3),
+                "what": "the same steps right after the GPU sat idle, with no warm-up: first and last "
+                        "quarter means show the clocks ramping"}
 
     base = None
     if args.bf16_baseline == "on" or (args.bf16_baseline == "auto" and args.workload in ("b32-100k-g128",
                                                                                        "b32-100k-g64")):
         base = bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len,
-                             timed_run, n_layers, stream, dims, hkv, hq)
+                             n_layers, stream, dims, hkv, hq, warmup, steps, args.history_target)
         if base is not None:
             base["int2_step_speedup"] = round(base["us_per_step"] / (step_ms * 1e3), 3)
             base["int2_history_speedup"] = round(base["history_us"] / (sum(k3_us) / steps), 3)
             base["byte_ratio"] = round(base["bytes_per_step"] / (step_tot / steps), 3)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if workers is not None:
         hosted = {"r_k32": r_k.cpu().numpy(), "r_v32": r_v.cpu().numpy(),
                   "clip_k": c_k.cpu().numpy(), "clip_v": c_v.cpu().numpy()}
-        cpu = cpu_baseline(model, layout, hosted, lens_step[-1], min(args.cpu_heads, hkv))
+        try:
+            cpu = cpu_baseline(workers, model, layout, hosted, lens_step[warmup + steps - 1])
+        finally:
+            workers.close()
 
     res = {
         "metric": METRIC,
@@ -381,23 +546,31 @@ def main() -> int:
                      "kernel": f"history ({kname})" + (" + bf16 sink/recent" if kname == "mfma" else ""),
                      "avg_us": round(sum(k3_us) / steps, 2),
                      "bytes_per_launch": int(launch_tot / steps),
-                     "frac_of_copy": round(k3_gbs / copy_gbs, 4),
+                     "read_ceiling_gbs": probes["read_ceiling_gbs"],
+                     "frac_of_read_ceiling": round(k3_gbs / probes["read_ceiling_gbs"], 4),
                      "unit_bytes": {"history_token_head": hist_unit_bytes(w.group_size),
                                     "bf16_token_head": 512}},
-        "copy_gbs": copy_gbs,
+        "quarters": {"step_us": quarters(step_us), "history_us": quarters(k3_us)},
+        "step_vs_history": round((sum(step_us) / steps) / (sum(k3_us) / steps), 4),
+        "probes": probes,
+        "cold_start": cold,
         "cpu_baseline": cpu,
         "bf16_baseline": base,
         "calibration_s": round(calib_s, 2),
     }
     if layout.chain_len:
         res["unique_value"] = round(unique_tot / (sum(step_us) * 1e-6) / 1e9, 2)
+    if args.trace_file:
+        with open(args.trace_file, "w") as f:
+            json.dump(trace, f)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len, timed_run,
-                  n_layers, stream, dims, hkv, hq):
-    """The same steps on an all-bf16 cache (oscar_bf16_append + oscar_bf16_decode)."""
+def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_all, vn_all, max_len,
+                  n_layers, stream, dims, hkv, hq, warmup, steps, target):
+    """The same steps on an all-bf16 cache (oscar_bf16_append +
+    oscar_bf16_decode), after the same bandwidth settle as the INT2 steps."""
     if n_layers != 1:
         return None
     t0 = time.perf_counter()
@@ -409,15 +582,30 @@ def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_
     nb = ok.oscar_bf16_decode_workspace_bytes(dims, w.batch)
     wsb = torch.empty(nb, dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, hq, 128), dtype=torch.float32, device="cuda")
+    n = min(warmup + steps, appends)
+    steps = min(steps, n)
+    warmup = n - steps
+    ev_b = [HipEvent() for _ in range(steps)]
+    ev_a = [HipEvent() for _ in range(steps)]
+    marks = [HipEvent() for _ in range(steps + 1)]
 
-    def one(s: int):
+    def one(s: int, opts):
         ok.oscar_bf16_append(dims, structs[s], kn_all[s], vn_all[s], stream)
-        ok.oscar_bf16_decode(dims, structs[s], q_all[s], max_len, wsb, nb, out, None, stream)
+        ok.oscar_bf16_decode(dims, structs[s], q_all[s], max_len, wsb, nb, out, None, stream, options=opts)
 
-    step_us, hist_us = timed_run(one)
-    steps = len(step_us)
-    warm = len(lens_t) - steps
-    hist_b = [int(lens_t[warm + i].sum()) * hkv * 512 for i in range(steps)]
+    bandwidth_probes(ok, torch, HipEvent, stream, settle_s=0.2)
+    plain = ok.make_options(history_target=target)
+    for s in range(warmup):
+        one(s, plain)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        marks[i].record(stream)
+        one(warmup + i, ok.make_options(0, target, ev_b[i], ev_a[i]))
+    marks[steps].record(stream)
+    marks[steps].synchronize()
+    step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]
+    hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(steps)]
+    hist_b = [int(lens_t[warmup + i].sum()) * hkv * 512 for i in range(steps)]
     step_b = [hb + w.batch * hq * 128 * (2 + 4) + w.batch * hkv * 512 for hb in hist_b]
     del bcache, wsb
     torch.cuda.empty_cache()

@@ -67,3 +67,37 @@ def test_source_sha_ignores_comments_but_not_code(tmp_path):
     assert source_sha(str(tmp_path)) == base
     (d / "decode_x.hip").write_text("int f() {\n  return 2;\n}\n")
     assert source_sha(str(tmp_path)) != base
+
+
+def test_oracle_workers_run_the_oracle_in_parallel_processes():
+    """The CPU-baseline workers (spawned processes, one BLAS thread each) run
+    the oracle's request_attention on the tasks they are given and report
+    their busy time on a shared clock."""
+    from oracle import oscar as O
+    rng = np.random.default_rng(5)
+    L, g = 700, 2
+
+    def bits(shape):
+        x = (rng.standard_normal(shape)).astype(np.float32)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    r = O.composite_rotation(np.eye(128)).astype(np.float32)[None]
+    clip = np.full((1, 128), 3.0, np.float32)
+    task = ((bits((g, 128)), bits((L, 1, 128)), bits((L, 1, 128)), r, r, clip, clip, 128, "uniform"), 1000)
+    ref, _ = O.request_attention(*task[0])
+    workers = bench.OracleWorkers(2)
+    try:
+        nbytes, wall, busy = workers.run([[task, task], [task]])
+        assert nbytes == 3000 and wall > 0 and len(busy) == 2
+        assert max(busy) <= wall + 1e-6
+        nbytes, wall, busy = workers.run([[task], []])
+        assert nbytes == 1000 and len(busy) == 1
+    finally:
+        workers.close()
+    assert np.isfinite(ref).all()
+    assert bench.cpu_worker_count() >= 1
+
+
+def test_quarter_means():
+    assert bench.quarters([4, 4, 2, 2, 2, 2, 1, 1]) == [4.0, 1.0]
+    assert bench.quarters([3.0]) == [3.0, 3.0]
