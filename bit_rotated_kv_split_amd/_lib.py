@@ -102,6 +102,10 @@ _SIGS = [
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                             _P(OscarDecodeOptions), ctypes.c_void_p]),
+    ("oscar_decode_step_noalloc", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), _P(OscarCache),
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
     ("oscar_merge_lse", ctypes.c_int, [_P(OscarDims), _P(OscarRotation), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -309,6 +313,18 @@ def oscar_decode_step(dims, rot, cache, k_new, v_new, q, max_seq_len: int, works
         _check(lib().oscar_decode_step(*args, _stream(stream)))
     else:
         _check(lib().oscar_decode_step_ex(*args, _opt(options), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def oscar_decode_step_noalloc(dims, rot, cache, k_new, v_new, q, max_seq_len: int, out, lse_out=None,
+                              stream=None) -> None:
+    """oscar_decode_step with the library's own per-device scratch as its
+    workspace (no allocation anywhere in the call)."""
+    _check(lib().oscar_decode_step_noalloc(ctypes.byref(dims), ctypes.byref(rot), ctypes.byref(cache),
+                                           _ptr(k_new), _ptr(v_new), _ptr(q), max_seq_len, _ptr(out),
+                                           _ptr(lse_out), _stream(stream)))
 
 
 def oscar_merge_lse(dims, rot, batch: int, max_seq_len: int, workspace, workspace_bytes: int,

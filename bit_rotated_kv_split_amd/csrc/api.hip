@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "oscar_device.h"
@@ -167,6 +168,39 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
 
+namespace {
+
+// Workspace of oscar_decode_step_noalloc: a device array of this library's
+// code object, so that call needs no allocation.  Each device the library
+// is loaded on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels
+// and copies get the address hipGetSymbolAddress returns for the current
+// device (scratch_address).
+static __device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no current HIP device for the no-allocation scratch");
+  if (dev < 0 || dev >= kMaxDevices) return fail(OSCAR_EUNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "device address of the no-allocation scratch");
+    if (p == nullptr) return fail(OSCAR_EHIP, "device address of the no-allocation scratch is NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OSCAR_OK;
+}
+
+}  // namespace
 
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len, int target_wg) {
   (void)max_seq_len;
@@ -434,6 +468,26 @@ int oscar_decode_step(const oscar_dims* dims, const oscar_rotation* rot, const o
                       float* lse_out, void* stream) {
   return oscar_decode_step_ex(dims, rot, cache, k_new, v_new, q, max_seq_len, workspace, workspace_bytes, out,
                               lse_out, nullptr, stream);
+}
+
+int oscar_decode_step_noalloc(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                              const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                              int32_t max_seq_len, float* out, float* lse_out, void* stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_cache(cache, true))) return rc;
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (cache->batch == 0) return OSCAR_OK;
+  const size_t need = workspace_layout(*dims, cache->batch, max_seq_len, kMaxTargetWg).total;
+  if (need > static_cast<size_t>(OSCAR_NOALLOC_SCRATCH_BYTES))
+    return fail(OSCAR_EINVAL,
+                "batch %d with %d query heads needs %zu bytes of workspace, more than the %zu-byte "
+                "no-allocation scratch; use oscar_decode_step with a caller workspace",
+                cache->batch, dims->num_q_heads, need, static_cast<size_t>(OSCAR_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return oscar_decode_step(dims, rot, cache, k_new, v_new, q, max_seq_len, ws, OSCAR_NOALLOC_SCRATCH_BYTES, out,
+                           lse_out, stream);
 }
 
 int oscar_merge_lse(const oscar_dims* dims, const oscar_rotation* rot, int32_t batch,

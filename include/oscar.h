@@ -269,6 +269,27 @@ int oscar_decode_step_ex(const oscar_dims* dims, const oscar_rotation* rot, cons
                          int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
                          float* lse_out, const oscar_decode_options* options, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same step
+ * as oscar_decode_step, with its workspace taken from a device array inside
+ * the library instead of a caller buffer.  The array holds
+ * OSCAR_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU; each GPU the library runs
+ * on keeps its copy until the process ends, and its address is looked up
+ * once per device, on the first call with that device current (`stream`
+ * must belong to the current device).  A batch whose workspace
+ * (oscar_decode_workspace_bytes) exceeds the array is rejected with
+ * OSCAR_EINVAL before anything is enqueued; with 8 KV heads that allows up
+ * to 111 requests of 64 query heads or 273 of 32.  Nothing is allocated or freed: no hipMalloc, hipFree or
+ * allocating library call.  The caller still owns the inputs and outputs.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams or threads with the same device) race and must be
+ * ordered by the caller.  The array keeps the last call's contents; nothing
+ * in it needs to start at zero.  Default options (oscar_decode_options). */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int oscar_decode_step_noalloc(const oscar_dims* dims, const oscar_rotation* rot, const oscar_cache* cache,
+                              const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                              int32_t max_seq_len, float* out, float* lse_out, void* stream);
+
 /* Log-sum-exp merge (second page, section "OSCAR的另一个关键点是": the
  * INT2 history and the bf16 sink/recent results are combined by an
  * online-softmax merge; first page, section "OSCAR 的不同之处": values are

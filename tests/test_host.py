@@ -182,6 +182,21 @@ def test_empty_batch_and_zero_tokens_are_no_ops():
     ok.oscar_kv_fill_history(d, _rot(), _cache(), 0, 0, 0, None, None, 0)
 
 
+def test_noalloc_step_rejects_a_batch_beyond_its_scratch():
+    """The no-allocation step refuses, on the host, a batch whose workspace
+    would not fit the library's 64 MiB scratch (64 q heads over 8 KV
+    heads: more than 111 requests), and an empty batch is a no-op."""
+    d = ok.make_dims(64, 8, 128)
+    assert ok.oscar_decode_workspace_bytes(d, 111, 131_072) <= ok.NOALLOC_SCRATCH_BYTES
+    assert ok.oscar_decode_workspace_bytes(d, 112, 131_072) > ok.NOALLOC_SCRATCH_BYTES
+    fake = 0x1000
+    big = ok.make_cache(fake, 4, fake, fake, fake, fake, fake, 4, fake, 112)
+    with pytest.raises(ok.OscarError) as e:
+        ok.oscar_decode_step_noalloc(d, _rot(), big, fake, fake, fake, 100, fake, None, 0)
+    assert e.value.code == ok.OSCAR_EINVAL and "scratch" in ok.oscar_last_error()
+    ok.oscar_decode_step_noalloc(d, _rot(), _cache(batch=0), None, None, None, 100, None, None, 0)
+
+
 def test_probe_rejects_misaligned_buffers():
     for buf, n in ((0x1001, 4096), (0x1000, 4095), (0, 4096)):
         with pytest.raises(ok.OscarError) as e:
