@@ -427,13 +427,18 @@ def main() -> int:
                               c.max_pages_per_req, seq_dev[t].data_ptr(), B) for t in range(appends)]
                for c in caches]
 
+    wall_khz = ok.wall_clock_khz()
+
     def timed_run(one_step, first: int, n_warm: int, n_timed: int):
         """Steps first .. first+n_warm-1 untimed, then n_timed steps timed:
-        events around each step and around each history launch."""
+        events around each step and around each history launch, and the
+        shader clock over the history launch's first workgroup (MHz)."""
         ev_b = [HipEvent() for _ in range(n_timed)]
         ev_a = [HipEvent() for _ in range(n_timed)]
         marks = [HipEvent() for _ in range(n_timed + 1)]
-        opts = [ok.make_options(kind, args.history_target, ev_b[i], ev_a[i]) for i in range(n_timed)]
+        clk = torch.zeros((n_timed, 4), dtype=torch.int64, device="cuda")
+        opts = [ok.make_options(kind, args.history_target, ev_b[i], ev_a[i], clk.data_ptr() + 32 * i)
+                for i in range(n_timed)]
         for s in range(n_warm):
             one_step(first + s, base_opts)
         torch.cuda.synchronize()
@@ -445,7 +450,9 @@ def main() -> int:
         torch.cuda.synchronize()
         step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(n_timed)]
         hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(n_timed)]
-        return step_us, hist_us
+        c = clk.cpu().numpy().astype(np.float64)
+        mhz = ((c[:, 2] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 1], 1) * wall_khz / 1e3).tolist()
+        return step_us, hist_us, mhz
 
     def int2_step(s: int, opts):
         t = s // n_layers
@@ -456,7 +463,7 @@ def main() -> int:
           f"{int(layout.lens.max())} layers={n_layers} slots={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
           file=sys.stderr, flush=True)
     probes = bandwidth_probes(ok, torch, HipEvent, stream)
-    step_us, k3_us = timed_run(int2_step, 0, warmup, steps)
+    step_us, k3_us, k3_mhz = timed_run(int2_step, 0, warmup, steps)
     step_ms = sum(step_us) / steps / 1e3
 
     kname = "mfma" if ok.oscar_history_kernel_for(dims, base_opts) == 2 else "valu"
@@ -480,21 +487,22 @@ def main() -> int:
     value = step_tot / (sum(step_us) * 1e-6) / 1e9
     traffic = load_traffic(args.workload, kname)
 
-    trace = {"step_us": step_us, "history_us": k3_us}
+    trace = {"step_us": step_us, "history_us": k3_us, "history_mhz": k3_mhz}
     cold = None
     if n_cold:
         torch.cuda.synchronize()
         time.sleep(COLD_IDLE_S)
-        c_step, c_k3 = timed_run(int2_step, warmup + steps, 0, n_cold)
-        trace.update(cold_step_us=c_step, cold_history_us=c_k3)
+        c_step, c_k3, c_mhz = timed_run(int2_step, warmup + steps, 0, n_cold)
+        trace.update(cold_step_us=c_step, cold_history_us=c_k3, cold_history_mhz=c_mhz)
         c_launch, c_stp, _ = byte_totals(warmup + steps, n_cold)
         c_k3_gbs = c_launch / (sum(c_k3) * 1e-6) / 1e9
         cold = {"idle_s": COLD_IDLE_S, "warmup": 0, "steps": n_cold,
                 "us_per_step": round(sum(c_step) / n_cold, 2), "history_us": round(sum(c_k3) / n_cold, 2),
                 "history_frac": round(c_k3_gbs / PEAK_HBM_GBS, 4),
                 "quarters_step_us": quarters(c_step), "quarters_history_us": quarters(c_k3),
-                "what": "the same steps right after the GPU sat idle, with no warm-up: first and last "
-                        "quarter means show the clocks ramping"}
+                "quarters_history_mhz": quarters(c_mhz), "min_history_mhz": round(min(c_mhz), 1),
+                "what": "the same steps after 1 s of GPU idle, with no warm-up; history_mhz is the shader "
+                        "clock over the history launch"}
 
     base = None
     if args.bf16_baseline == "on" or (args.bf16_baseline == "auto" and args.workload in ("b32-100k-g128",
@@ -550,7 +558,8 @@ def main() -> int:
                      "frac_of_read_ceiling": round(k3_gbs / probes["read_ceiling_gbs"], 4),
                      "unit_bytes": {"history_token_head": hist_unit_bytes(w.group_size),
                                     "bf16_token_head": 512}},
-        "quarters": {"step_us": quarters(step_us), "history_us": quarters(k3_us)},
+        "quarters": {"step_us": quarters(step_us), "history_us": quarters(k3_us),
+                     "history_mhz": quarters(k3_mhz), "min_history_mhz": round(min(k3_mhz), 1)},
         "step_vs_history": round((sum(step_us) / steps) / (sum(k3_us) / steps), 4),
         "probes": probes,
         "cold_start": cold,

@@ -62,7 +62,8 @@ class OscarBf16Cache(ctypes.Structure):
 
 class OscarDecodeOptions(ctypes.Structure):
     _fields_ = [("history_kernel", ctypes.c_int32), ("history_target", ctypes.c_int32),
-                ("history_start_event", ctypes.c_void_p), ("history_stop_event", ctypes.c_void_p)]
+                ("history_start_event", ctypes.c_void_p), ("history_stop_event", ctypes.c_void_p),
+                ("history_clock_trace", ctypes.c_void_p)]
 
 
 # (name, restype, argtypes) of every exported function
@@ -216,11 +217,27 @@ def _event_handle(ev):
 
 
 def make_options(history_kernel: int = 0, history_target: int = 0, start_event=None,
-                 stop_event=None) -> OscarDecodeOptions:
-    """Per-call options of the decode entry points (oscar_decode_options)."""
-    o = OscarDecodeOptions(history_kernel, history_target, _event_handle(start_event), _event_handle(stop_event))
-    o._keep = (start_event, stop_event)
+                 stop_event=None, clock_trace=None) -> OscarDecodeOptions:
+    """Per-call options of the decode entry points (oscar_decode_options);
+    clock_trace: a device uint64 [4] tensor or address, or None."""
+    o = OscarDecodeOptions(history_kernel, history_target, _event_handle(start_event), _event_handle(stop_event),
+                           _ptr(clock_trace))
+    o._keep = (start_event, stop_event, clock_trace)
     return o
+
+
+def wall_clock_khz(device: int = 0) -> int:
+    """The device's constant-rate counter frequency in kHz
+    (hipDeviceAttributeWallClockRate, value 10017 of hipDeviceAttribute_t
+    in hip_runtime_api.h), for history_clock_trace readings."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    hip.hipDeviceGetAttribute.restype = ctypes.c_int
+    v = ctypes.c_int()
+    rc = hip.hipDeviceGetAttribute(ctypes.byref(v), 10017, device)
+    if rc != 0:
+        raise OscarError(OSCAR_EHIP, f"hipDeviceGetAttribute(wall clock rate) failed ({rc})")
+    return v.value
 
 
 def _opt(options):

@@ -111,6 +111,7 @@ struct CallOpts {
   int target_wg = 0;
   hipEvent_t ev_start = nullptr;
   hipEvent_t ev_stop = nullptr;
+  unsigned long long* clock_trace = nullptr;
 };
 
 // The default target when none was given: the resident workgroups of the
@@ -146,6 +147,7 @@ int resolve_opts(const oscar_dims& d, const oscar_decode_options* o, bool need_t
       c.ev_start = static_cast<hipEvent_t>(o->history_start_event);
       c.ev_stop = static_cast<hipEvent_t>(o->history_stop_event);
     }
+    c.clock_trace = reinterpret_cast<unsigned long long*>(o->history_clock_trace);
   }
   if (c.kernel == 2 && !hist_mfma_supported(d))
     return fail(OSCAR_EUNSUPPORTED, "matrix-core history kernel does not support these dims");
@@ -403,6 +405,7 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   if (e != hipSuccess) return hip_fail(e, "query rotation launch");
   a.ev_start = opt.ev_start;
   a.ev_stop = opt.ev_stop;
+  a.clock_trace = opt.clock_trace;
   // the matrix-core launch also runs the bf16 sink/recent chunks
   e = mfma ? launch_hist_mfma(a, s) : launch_hist_valu(a, s);
   if (e != hipSuccess) return hip_fail(e, "history launch");

@@ -162,6 +162,7 @@ struct HistParams {
   int32_t hq;
   const int32_t* sched;
   float lev_lo, lev_hi;   // Lloyd-Max codebook: levels -hi, -lo, lo, hi
+  unsigned long long* clk;   // timing hook or nullptr: workgroup (0, 0)'s clock counters
 };
 
 // Level of a 2-bit code: the code itself (uniform codebook) or the
@@ -185,6 +186,12 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
   constexpr int NG = kDim / G;
   const int split = blockIdx.x, kvh = blockIdx.y;
   if (split >= a.sched[0]) return;   // unused slot (uniform)
+  const bool clk = a.clk != nullptr && split == 0 && kvh == 0;   // timing hook (uniform)
+  unsigned long long clk0 = 0, wall0 = 0;
+  if (clk) {
+    clk0 = clock64();
+    wall0 = wall_clock64();
+  }
   const int b = a.sched[1 + 3 * split];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float q_s[GQ][kDim];
@@ -334,6 +341,13 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
     const size_t pidx = static_cast<size_t>(split) * a.hq + kvh * GQ + h;
     a.po[pidx * kDim + c] = lt > 0.f ? at / lt : 0.f;
     if (c == 0) a.plse[pidx] = lt > 0.f ? (mx + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  if (clk && tid == 0) {
+    const unsigned long long clk1 = clock64(), wall1 = wall_clock64();
+    a.clk[0] = clk0;
+    a.clk[1] = wall0;
+    a.clk[2] = clk1;
+    a.clk[3] = wall1;
   }
 }
 
@@ -682,6 +696,7 @@ struct HistValuRun {
     const Codebook* cb = codebook_of(d.codebook);
     p.lev_lo = cb->lev[2];
     p.lev_hi = cb->lev[3];
+    p.clk = a.clock_trace;
     const dim3 grid(a.lay.slots, d.num_kv_heads);
     const bool timed = a.ev_start != nullptr && a.ev_stop != nullptr;
     if (d.codebook == OSCAR_CODEBOOK_LLOYD_MAX) {

@@ -199,6 +199,7 @@ struct MfmaParams {
   float lm_ka;            // hi - lo: weight of the code plane
   float lm_kb;            // (3 lo - hi) / 2: weight of the 2 b1 plane
   Bf16Params bf;          // the bf16 sink/recent chunks, run as extra workgroups
+  unsigned long long* clk;   // timing hook or nullptr: workgroup 0's clock counters
 };
 
 template <int G>
@@ -555,6 +556,13 @@ hist_mfma_kernel(MfmaParams a) {
   }
   const int split = id / a.hkv, kvh = id % a.hkv;
   if (split >= a.sched[0]) return;
+  // timing hook: shader-clock and constant-rate counters over workgroup 0
+  const bool clk = a.clk != nullptr && id == 0;   // uniform
+  unsigned long long clk0 = 0, wall0 = 0;
+  if (clk) {
+    clk0 = clock64();
+    wall0 = wall_clock64();
+  }
   // the split's request and page range, and the request's length, are
   // uniform: held in scalar registers so every branch on them is uniform
   const int b = __builtin_amdgcn_readfirstlane(a.sched[1 + 3 * split]);
@@ -687,6 +695,13 @@ hist_mfma_kernel(MfmaParams a) {
     }
     if (n == 0) a.plse[pidx] = any ? (st.m_ref[hb] + log2f(l)) * kLn2 : -INFINITY;
   }
+  if (clk && threadIdx.x == 0) {
+    const unsigned long long clk1 = clock64(), wall1 = wall_clock64();
+    a.clk[0] = clk0;
+    a.clk[1] = wall0;
+    a.clk[2] = clk1;
+    a.clk[3] = wall1;
+  }
 }
 
 // Register page buffers and waves per SIMD of each instantiation.  The
@@ -727,6 +742,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.lm_ka = cbk->lev[3] - cbk->lev[2];
   p.lm_kb = (3.f * cbk->lev[2] - cbk->lev[3]) * 0.5f;
   p.bf = make_bf16_params(a);
+  p.clk = a.clock_trace;
   const dim3 grid((a.lay.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
   const dim3 block(64 * WAVES);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)

@@ -118,6 +118,8 @@ struct DecodeArgs {
   WsLayout lay;
   hipEvent_t ev_start = nullptr;   // when both set, the history kernel is launched
   hipEvent_t ev_stop = nullptr;    // with these as its start/stop timestamps
+  unsigned long long* clock_trace = nullptr;   // when set, the history kernel's first
+                                               // workgroup records its clock counters
   const DemoteStep* demote = nullptr;   // when set, the prologue launch also demotes
 };
 

@@ -197,12 +197,22 @@ int oscar_kv_read_history(const oscar_dims* dims, const oscar_cache* cache, int3
  *                   hipEvent_t or NULL: when both are set, the history
  *                   launch is made with hipExtLaunchKernelGGL with these as
  *                   its start and stop events, so their elapsed time is that
- *                   kernel's execution (a timing hook). */
+ *                   kernel's execution (a timing hook).
+ *   history_clock_trace
+ *                   device uint64 [4] or NULL: when set, the history
+ *                   kernel's first workgroup writes the shader-clock cycle
+ *                   counter and the constant-rate counter (the device's
+ *                   hipDeviceAttributeWallClockRate, in kHz) at its start
+ *                   ([0], [1]) and at its end ([2], [3]), so
+ *                   ([2] - [0]) / ([3] - [1]) * wall rate is the average
+ *                   shader clock over that workgroup's split (a timing
+ *                   hook; the split spans most of the launch). */
 typedef struct oscar_decode_options {
   int32_t history_kernel;
   int32_t history_target;
   void* history_start_event;
   void* history_stop_event;
+  uint64_t* history_clock_trace;
 } oscar_decode_options;
 
 /* Upper bound on the history splits per KV head that oscar_decode_attn

@@ -630,3 +630,28 @@ def test_two_threads_with_different_targets_get_their_own_schedules():
         assert len(splits) == sum(-(-p // q_ref) for p in pages)
         check_all(layout, model, cal, out[:, :, :], np.zeros((w.batch, w.num_q_heads)), q_bits,
                   requests=[0, int(np.argmax(lens))], what=f"target {target}", lse_check=False)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_clock_trace_hook(kernel):
+    """history_clock_trace: the history launch's first workgroup writes
+    increasing shader-clock and constant-rate counters whose ratio is a
+    plausible shader clock, and the output is unchanged by the hook."""
+    w = small("clk", 97, 8, 2, 128, [6000, 900])
+    layout, model, cal, rot, cache = setup(w)
+    q = W.queries_tensor(model, 0, w.batch)
+    clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+    ws = DecodeWorkspace(cache.dims, w.batch, 6000)
+    outs = []
+    for opts in (ok.make_options(history_kernel=KERNELS[kernel]),
+                 ok.make_options(history_kernel=KERNELS[kernel], clock_trace=clk)):
+        out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+        ok.oscar_decode(cache.dims, rot.struct, cache.struct(), q, 6000, ws.buf, ws.nbytes, out, None,
+                        options=opts)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    c = clk.cpu().numpy().astype(np.float64)
+    assert c[2] > c[0] > 0 and c[3] > c[1] > 0
+    mhz = (c[2] - c[0]) / (c[3] - c[1]) * ok.wall_clock_khz() / 1e3
+    assert 100 < mhz < 4000, mhz
