@@ -20,8 +20,11 @@ Order of one run:
      ceiling the roofline is compared against, and they leave the GPU at
      its steady clocks, so the timed steps do not measure the clock ramp
      that follows the idle setup;
-  3. `warmup` untimed steps, then exactly `steps` timed steps: `value`,
-     `ms_per_step`, the history launch's `roofline` and per-quarter means;
+  3. `warmup` untimed steps, then exactly `steps` timed steps between one
+     pair of events: `value` and `ms_per_step`; each history launch between
+     its own events (`roofline`, per-quarter means, shader clock); then
+     `steps` more steps with an event between consecutive steps for the
+     per-step latency (`step_us_p50`, `step_us_p99`);
   4. `cold_start`: after 1 s with the GPU idle, 20 more timed steps with no
      warm-up (diagnostic: the cost of starting from idle clocks);
   5. the all-bf16 baseline's steps (the 32 x 100K workloads);
@@ -373,7 +376,7 @@ def main() -> int:
     w = workloads()[args.workload]()
     steps, warmup = args.steps or (w.steps if w.steps > 1 else 100), args.warmup
     n_cold = 0 if args.no_cold_start else COLD_STEPS
-    total = steps + warmup + n_cold
+    total = warmup + 2 * steps + n_cold     # warm-up, timed, latency leg, cold start
     n_layers = args.layers or default_layers(args.workload)
     appends = -(-total // n_layers)          # tokens each layer cache receives
     layout = W.Layout(w, None, extra_tokens=appends)
@@ -429,10 +432,14 @@ def main() -> int:
 
     wall_khz = ok.wall_clock_khz()
 
-    def timed_run(one_step, first: int, n_warm: int, n_timed: int):
-        """Steps first .. first+n_warm-1 untimed, then n_timed steps timed:
-        events around each step and around each history launch, and the
-        shader clock over the history launch's first workgroup (MHz)."""
+    def timed_run(one_step, first: int, n_warm: int, n_timed: int, marks_per_step: bool = False):
+        """Steps first .. first+n_warm-1 untimed, then n_timed steps timed
+        between one pair of events on the stream, each history launch between
+        its own start/stop events (hipExtLaunchKernelGGL), with the shader
+        clock over the launch's first workgroup.  With marks_per_step an
+        event is also recorded between consecutive steps (per-step times,
+        at a few µs of extra cost per step).  Returns (total µs, per-step µs
+        or None, per-launch µs, per-launch MHz)."""
         ev_b = [HipEvent() for _ in range(n_timed)]
         ev_a = [HipEvent() for _ in range(n_timed)]
         marks = [HipEvent() for _ in range(n_timed + 1)]
@@ -442,17 +449,20 @@ def main() -> int:
         for s in range(n_warm):
             one_step(first + s, base_opts)
         torch.cuda.synchronize()
+        marks[0].record(stream)
         for i in range(n_timed):
-            marks[i].record(stream)
+            if marks_per_step and i > 0:
+                marks[i].record(stream)
             one_step(first + n_warm + i, opts[i])
         marks[n_timed].record(stream)
         marks[n_timed].synchronize()
         torch.cuda.synchronize()
-        step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(n_timed)]
+        total_us = 1e3 * marks[0].elapsed_ms(marks[n_timed])
+        step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(n_timed)] if marks_per_step else None
         hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(n_timed)]
         c = clk.cpu().numpy().astype(np.float64)
         mhz = ((c[:, 2] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 1], 1) * wall_khz / 1e3).tolist()
-        return step_us, hist_us, mhz
+        return total_us, step_us, hist_us, mhz
 
     def int2_step(s: int, opts):
         t = s // n_layers
@@ -463,8 +473,10 @@ def main() -> int:
           f"{int(layout.lens.max())} layers={n_layers} slots={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
           file=sys.stderr, flush=True)
     probes = bandwidth_probes(ok, torch, HipEvent, stream)
-    step_us, k3_us, k3_mhz = timed_run(int2_step, 0, warmup, steps)
-    step_ms = sum(step_us) / steps / 1e3
+    total_us, _, k3_us, k3_mhz = timed_run(int2_step, 0, warmup, steps)
+    step_ms = total_us / steps / 1e3
+    # per-step latency: the next `steps` steps with an event between steps
+    _, step_us, _, _ = timed_run(int2_step, warmup + steps, 0, steps, marks_per_step=True)
 
     kname = "mfma" if ok.oscar_history_kernel_for(dims, base_opts) == 2 else "valu"
     shared_tok = PAGE * (sum(layout.shared_pages) - layout.chain_len) if layout.chain_len else 0
@@ -484,17 +496,18 @@ def main() -> int:
 
     launch_tot, step_tot, unique_tot = byte_totals(warmup, steps)
     k3_gbs = launch_tot / (sum(k3_us) * 1e-6) / 1e9
-    value = step_tot / (sum(step_us) * 1e-6) / 1e9
+    value = step_tot / (total_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, kname)
 
-    trace = {"step_us": step_us, "history_us": k3_us, "history_mhz": k3_mhz}
+    trace = {"history_us": k3_us, "history_mhz": k3_mhz, "latency_step_us": step_us}
     cold = None
     if n_cold:
         torch.cuda.synchronize()
         time.sleep(COLD_IDLE_S)
-        c_step, c_k3, c_mhz = timed_run(int2_step, warmup + steps, 0, n_cold)
+        c_first = warmup + 2 * steps
+        _, c_step, c_k3, c_mhz = timed_run(int2_step, c_first, 0, n_cold, marks_per_step=True)
         trace.update(cold_step_us=c_step, cold_history_us=c_k3, cold_history_mhz=c_mhz)
-        c_launch, c_stp, _ = byte_totals(warmup + steps, n_cold)
+        c_launch, c_stp, _ = byte_totals(c_first, n_cold)
         c_k3_gbs = c_launch / (sum(c_k3) * 1e-6) / 1e9
         cold = {"idle_s": COLD_IDLE_S, "warmup": 0, "steps": n_cold,
                 "us_per_step": round(sum(c_step) / n_cold, 2), "history_us": round(sum(c_k3) / n_cold, 2),
@@ -532,6 +545,8 @@ def main() -> int:
         "warmup": warmup,
         "ms_per_step": round(step_ms, 4),
         "us_per_step": round(step_ms * 1e3, 2),
+        # per-step latency from the next `steps` steps, with an event between
+        # consecutive steps (the events cost a few µs per step)
         "step_us_p50": pct(step_us, 50),
         "step_us_p99": pct(step_us, 99),
         "pct_peak": round(100 * value / PEAK_HBM_GBS, 2),
@@ -558,9 +573,9 @@ def main() -> int:
                      "frac_of_read_ceiling": round(k3_gbs / probes["read_ceiling_gbs"], 4),
                      "unit_bytes": {"history_token_head": hist_unit_bytes(w.group_size),
                                     "bf16_token_head": 512}},
-        "quarters": {"step_us": quarters(step_us), "history_us": quarters(k3_us),
-                     "history_mhz": quarters(k3_mhz), "min_history_mhz": round(min(k3_mhz), 1)},
-        "step_vs_history": round((sum(step_us) / steps) / (sum(k3_us) / steps), 4),
+        "quarters": {"history_us": quarters(k3_us), "history_mhz": quarters(k3_mhz),
+                     "min_history_mhz": round(min(k3_mhz), 1)},
+        "step_vs_history": round((total_us / steps) / (sum(k3_us) / steps), 4),
         "probes": probes,
         "cold_start": cold,
         "cpu_baseline": cpu,
@@ -568,7 +583,7 @@ def main() -> int:
         "calibration_s": round(calib_s, 2),
     }
     if layout.chain_len:
-        res["unique_value"] = round(unique_tot / (sum(step_us) * 1e-6) / 1e9, 2)
+        res["unique_value"] = round(unique_tot / (total_us * 1e-6) / 1e9, 2)
     if args.trace_file:
         with open(args.trace_file, "w") as f:
             json.dump(trace, f)
@@ -596,7 +611,7 @@ def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_
     warmup = n - steps
     ev_b = [HipEvent() for _ in range(steps)]
     ev_a = [HipEvent() for _ in range(steps)]
-    marks = [HipEvent() for _ in range(steps + 1)]
+    m0, m1 = HipEvent(), HipEvent()
 
     def one(s: int, opts):
         ok.oscar_bf16_append(dims, structs[s], kn_all[s], vn_all[s], stream)
@@ -607,20 +622,21 @@ def bf16_baseline(ok, W, HipEvent, torch, w, layout, lens_t, appends, q_all, kn_
     for s in range(warmup):
         one(s, plain)
     torch.cuda.synchronize()
+    opts = [ok.make_options(0, target, ev_b[i], ev_a[i]) for i in range(steps)]
+    m0.record(stream)
     for i in range(steps):
-        marks[i].record(stream)
-        one(warmup + i, ok.make_options(0, target, ev_b[i], ev_a[i]))
-    marks[steps].record(stream)
-    marks[steps].synchronize()
-    step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]
+        one(warmup + i, opts[i])
+    m1.record(stream)
+    m1.synchronize()
+    total_us = 1e3 * m0.elapsed_ms(m1)
     hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(steps)]
     hist_b = [int(lens_t[warmup + i].sum()) * hkv * 512 for i in range(steps)]
     step_b = [hb + w.batch * hq * 128 * (2 + 4) + w.batch * hkv * 512 for hb in hist_b]
     del bcache, wsb
     torch.cuda.empty_cache()
     h_gbs = sum(hist_b) / (sum(hist_us) * 1e-6) / 1e9
-    return {"us_per_step": round(sum(step_us) / steps, 2), "step_us_p50": pct(step_us, 50),
-            "value": round(sum(step_b) / (sum(step_us) * 1e-6) / 1e9, 2), "unit": "GB/s",
+    return {"us_per_step": round(total_us / steps, 2),
+            "value": round(sum(step_b) / (total_us * 1e-6) / 1e9, 2), "unit": "GB/s",
             "history_us": round(sum(hist_us) / steps, 2), "history_gbs": round(h_gbs, 1),
             "history_frac": round(h_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": int(sum(step_b) / steps),
             "fill_s": round(fill_s, 1),
