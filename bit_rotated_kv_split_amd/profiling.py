@@ -68,6 +68,26 @@ def counters(path: str, kernel: str) -> dict:
     return {k: sum(v) / len(v) for k, v in res.items()}
 
 
+def derived(vals: dict, page_heads: float, simds: int = 1024, xcds: int = 8) -> dict:
+    """Per-page instruction counts and busy fractions from the SQ counters.
+    A wave64 vector instruction occupies its SIMD for 4 cycles (16 lanes a
+    cycle); GRBM_GUI_ACTIVE is summed over the XCDs, so the kernel's cycles
+    are GRBM_GUI_ACTIVE / xcds; SQ_VALU_MFMA_BUSY_CYCLES is summed over the
+    SIMDs."""
+    out = {}
+    cycles = vals.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+    if page_heads > 0:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA"):
+            if k in vals:
+                out[f"{k} per page-head"] = vals[k] / page_heads
+    if cycles > 0:
+        if "SQ_INSTS_VALU" in vals:
+            out["vector ALU busy (4 cycles per instruction)"] = vals["SQ_INSTS_VALU"] * 4 / simds / cycles
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            out["matrix core busy"] = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cycles
+    return out
+
+
 def _code_only(text: str) -> str:
     """C++ source without comments, blank lines or indentation, so
     that editing a comment does not retire the traffic records.  Text after
@@ -125,12 +145,19 @@ def main(argv=None) -> int:
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernel", required=True)
+    c.add_argument("--page-heads", type=float, default=0.0,
+                   help="64-token pages x KV heads one dispatch processes (adds per-page and busy figures)")
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("--xcds", type=int, default=8)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.csv, [m for m in args.match.split(",") if m]))
     elif args.cmd == "counters":
-        for k, v in sorted(counters(args.csv, args.kernel).items()):
+        vals = counters(args.csv, args.kernel)
+        for k, v in sorted(vals.items()):
             print(f"{k}: {v:.6g}")
+        for k, v in derived(vals, args.page_heads, args.simds, args.xcds).items():
+            print(f"{k}: {v:.4g}")
     else:
         rec = traffic(args.fetch_csv, args.write_csv, args.kernel)
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

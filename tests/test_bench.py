@@ -101,3 +101,18 @@ def test_oracle_workers_run_the_oracle_in_parallel_processes():
 def test_quarter_means():
     assert bench.quarters([4, 4, 2, 2, 2, 2, 1, 1]) == [4.0, 1.0]
     assert bench.quarters([3.0]) == [3.0, 3.0]
+
+
+def test_counter_derived_figures():
+    """Per-page counts and busy fractions from summed SQ counters: 1024
+    SIMDs each issuing 1000 wave64 instructions (4 cycles each) over 8000
+    kernel cycles are half busy."""
+    from bit_rotated_kv_split_amd.profiling import derived
+    vals = {"SQ_INSTS_VALU": 1024 * 1000.0, "SQ_INSTS_MFMA": 512.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 2000.0,
+            "GRBM_GUI_ACTIVE": 8 * 8000.0}
+    d = derived(vals, page_heads=256.0)
+    assert d["SQ_INSTS_VALU per page-head"] == 4000.0
+    assert d["SQ_INSTS_MFMA per page-head"] == 2.0
+    assert d["vector ALU busy (4 cycles per instruction)"] == 0.5
+    assert d["matrix core busy"] == 0.25
+    assert derived({"SQ_INSTS_VALU": 1.0}, page_heads=0.0) == {}
