@@ -87,14 +87,14 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   // per-group sums and the largest magnitude, one wave per head
   for (int h = wave; h < GQ; h += 4) {
     const float v0 = qr[h][lane], v1 = qr[h][lane + 64];
-    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float mx = wave_reduce_dpp(fmaxf(fabsf(v0), fabsf(v1)), WaveMax());
     if (lane == 0) qinv[h] = mx > 0.f ? kQFixMax / mx : 0.f;
     for (int gi = 0; gi < 4; ++gi) {
       const int lo = gi * G, hi = lo + G;
       float sgi = 0.f;
       if (lo < kDim) {   // uniform: groups past the head dimension hold 0
         sgi = (lane >= lo && lane < hi ? v0 : 0.f) + (lane + 64 >= lo && lane + 64 < hi ? v1 : 0.f);
-        sgi = wave_sum(sgi);
+        sgi = wave_reduce_dpp(sgi, WaveAdd());
       }
       if (lane == 0) qsum[(head0 + h) * 4 + gi] = sgi;
     }
@@ -512,37 +512,40 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 
 // merge_group_kernel (256 threads): the request's history splits are
 // merged per head in the rotated value domain, rotated back by R_V^T, and
-// merged with the five bf16 partials.  Loads are issued early: each
-// thread's half-row of R_V before anything else, then the partials.  A
-// workgroup takes GQ heads of one (request, KV head): heads
-// GQ * blockIdx.z .. of the group (eight-head groups run as two four-head
-// workgroups).
+// merged with the five bf16 partials.  A workgroup takes GQ heads of one
+// (request, KV head): heads GQ * blockIdx.z .. of the group (eight-head
+// groups run as two four-head workgroups).  Each thread owns (head,
+// channel) items and, for the un-rotation, half a row of R_V.
+//
+// Loads are issued in the order they are needed: the log-sum-exps and the
+// partials of the first 16 splits and of the bf16 chunks, then R_V, so the
+// weights do not wait for the rotation rows.  When a request has at most 16
+// splits (the usual case at large batch) every thread computes its heads'
+// weights itself from the log-sum-exps it loaded (the same few addresses
+// across a wave): no reductions across lanes and one workgroup barrier.
+// Longer requests take the cooperative path: weights per head by one wave
+// through LDS, partials past the 16th read 16 at a time.
 template <int GQ>
 __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int kMaxHist = kMaxSplits + 1;
-  __shared__ float wh[GQ][kMaxHist];   // history split weights
-  __shared__ float wb[GQ][kBf16Parts]; // bf16 partial weights
+  __shared__ float wh[GQ][kMaxHist];   // history split weights (cooperative path)
+  __shared__ float wb[GQ][kBf16Parts]; // bf16 partial weights (cooperative path)
   __shared__ float lse_s[GQ][2];       // history LSE, bf16 LSE
   __shared__ float orot[GQ][kDim];     // merged history output, rotated domain
   __shared__ float obf[GQ][kDim];      // merged bf16 output
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
   const int h0 = kvh * a.gq + GQ * static_cast<int>(blockIdx.z);   // first head of this workgroup's block
   const size_t bhead0 = static_cast<size_t>(b) * a.hq + h0;
-  // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
-  const int i = tid >> 1, kh = tid & 1;
-  float4 rr[16];
-  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
-#pragma unroll
-  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
-  // partials of the first 16 splits and the bf16 chunks, loaded together
-  // with the log-sum-exps (they do not depend on the weights), so the kernel
-  // waits on memory once for all three
   constexpr int kItems = (GQ * kDim + 255) / 256;   // (head, channel) items per thread
   constexpr int kEarly = 16;
+  // (kept for up to two items per thread: four or more per thread would hold
+  // twice the registers and spill)
+  const bool local = kItems <= 2 && count <= kEarly;   // uniform
   const size_t hstride = static_cast<size_t>(a.hq) * kDim;
-  float vh[kItems][kEarly], vb[kItems][kBf16Parts];
+  constexpr int kLocalItems = kItems <= 2 ? kItems : 1;
+  float vh[kItems][kEarly], vb[kItems][kBf16Parts], lh[kLocalItems][kEarly], lb[kLocalItems][kBf16Parts];
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
     const int x = tid + 256 * it;
@@ -554,59 +557,110 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
     const float* bb = a.bo + ((bhead0 + h) * kBf16Parts) * kDim + k;
 #pragma unroll
     for (int c = 0; c < kBf16Parts; ++c) vb[it][c] = live ? bb[c * kDim] : 0.f;
-  }
-  for (int x = tid; x < GQ * count; x += 256) {
-    const int h = x / count, sp = x % count;
-    wh[h][sp] = a.hlse[static_cast<size_t>(first + sp) * a.hq + h0 + h];
-  }
-  for (int x = tid; x < GQ * kBf16Parts; x += 256)
-    wb[x / kBf16Parts][x % kBf16Parts] = a.blse[(bhead0 + x / kBf16Parts) * kBf16Parts + x % kBf16Parts];
-  __syncthreads();
-  // per head and side: normalised weights of the partials
-  for (int h = wave; h < GQ; h += 4) {
+    if (local && it < kLocalItems) {
 #pragma unroll
-    for (int side = 0; side < 2; ++side) {
-      float* w = side ? wb[h] : wh[h];
-      const int n = side ? kBf16Parts : count;
-      float mx = -INFINITY;
-      for (int sp = lane; sp < n; sp += 64) mx = fmaxf(mx, w[sp]);
-      mx = wave_max(mx);
-      float den = 0.f;
-      for (int sp = lane; sp < n; sp += 64) den += mx == -INFINITY ? 0.f : expf(w[sp] - mx);
-      den = wave_sum(den);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int sp = lane; sp < n; sp += 64) w[sp] = den > 0.f ? expf(w[sp] - mx) / den : 0.f;
-      if (lane == 0) lse_s[h][side] = den > 0.f ? mx + logf(den) : -INFINITY;
+      for (int u = 0; u < kEarly; ++u)
+        lh[it][u] = live && u < count ? a.hlse[static_cast<size_t>(first + u) * a.hq + h0 + h] : -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kBf16Parts; ++c) lb[it][c] = live ? a.blse[(bhead0 + h) * kBf16Parts + c] : -INFINITY;
     }
   }
-  __syncthreads();
-  // weighted sums of the partials: the first 16 splits from registers, the
-  // rest (long single requests) 16 loads at a time
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int x = tid + 256 * it;
-    if (x >= GQ * kDim) break;
-    const int h = x / kDim, k = x % kDim;
-    float oh = 0.f;
-#pragma unroll
-    for (int u = 0; u < kEarly; ++u)
-      if (u < count) oh = __builtin_fmaf(wh[h][u], vh[it][u], oh);
-    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
-    for (int s0 = kEarly; s0 < count; s0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s0 + u < count ? hb[static_cast<size_t>(s0 + u) * hstride] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (s0 + u < count) oh = __builtin_fmaf(wh[h][s0 + u], v[u], oh);
+  if (!local) {
+    for (int x = tid; x < GQ * count; x += 256) {
+      const int h = x / count, sp = x % count;
+      wh[h][sp] = a.hlse[static_cast<size_t>(first + sp) * a.hq + h0 + h];
     }
-    float ob = 0.f;
+    for (int x = tid; x < GQ * kBf16Parts; x += 256)
+      wb[x / kBf16Parts][x % kBf16Parts] = a.blse[(bhead0 + x / kBf16Parts) * kBf16Parts + x % kBf16Parts];
+  }
+  // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
+  const int i = tid >> 1, kh = tid & 1;
+  float4 rr[16];
+  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
 #pragma unroll
-    for (int c = 0; c < kBf16Parts; ++c) ob = __builtin_fmaf(wb[h][c], vb[it][c], ob);
-    orot[h][k] = oh;
-    obf[h][k] = ob;
+  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  if (local) {
+    // each thread weighs its own items' partials
+#pragma unroll
+    for (int it = 0; it < kLocalItems; ++it) {
+      const int x = tid + 256 * it;
+      if (x >= GQ * kDim) break;
+      const int h = x / kDim, k = x % kDim;
+      float mh = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kEarly; ++u) mh = fmaxf(mh, lh[it][u]);
+      float dh = 0.f, oh = 0.f;
+#pragma unroll
+      for (int u = 0; u < kEarly; ++u) {
+        const float e = u < count && mh != -INFINITY ? expf(lh[it][u] - mh) : 0.f;
+        dh += e;
+        oh = __builtin_fmaf(e, vh[it][u], oh);
+      }
+      float mb = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kBf16Parts; ++c) mb = fmaxf(mb, lb[it][c]);
+      float db = 0.f, ob = 0.f;
+#pragma unroll
+      for (int c = 0; c < kBf16Parts; ++c) {
+        const float e = lb[it][c] == -INFINITY ? 0.f : expf(lb[it][c] - mb);
+        db += e;
+        ob = __builtin_fmaf(e, vb[it][c], ob);
+      }
+      orot[h][k] = dh > 0.f ? oh / dh : 0.f;
+      obf[h][k] = db > 0.f ? ob / db : 0.f;
+      if (k == 0) {
+        lse_s[h][0] = dh > 0.f ? mh + logf(dh) : -INFINITY;
+        lse_s[h][1] = db > 0.f ? mb + logf(db) : -INFINITY;
+      }
+    }
+  } else {
+    __syncthreads();
+    // per head and side: normalised weights of the partials
+    for (int h = wave; h < GQ; h += 4) {
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        float* w = side ? wb[h] : wh[h];
+        const int n = side ? kBf16Parts : count;
+        float mx = -INFINITY;
+        for (int sp = lane; sp < n; sp += 64) mx = fmaxf(mx, w[sp]);
+        mx = wave_max(mx);
+        float den = 0.f;
+        for (int sp = lane; sp < n; sp += 64) den += mx == -INFINITY ? 0.f : expf(w[sp] - mx);
+        den = wave_sum(den);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int sp = lane; sp < n; sp += 64) w[sp] = den > 0.f ? expf(w[sp] - mx) / den : 0.f;
+        if (lane == 0) lse_s[h][side] = den > 0.f ? mx + logf(den) : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // weighted sums of the partials: the first 16 splits from registers, the
+    // rest 16 loads at a time
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int x = tid + 256 * it;
+      if (x >= GQ * kDim) break;
+      const int h = x / kDim, k = x % kDim;
+      float oh = 0.f;
+#pragma unroll
+      for (int u = 0; u < kEarly; ++u)
+        if (u < count) oh = __builtin_fmaf(wh[h][u], vh[it][u], oh);
+      const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
+      for (int s0 = kEarly; s0 < count; s0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = s0 + u < count ? hb[static_cast<size_t>(s0 + u) * hstride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (s0 + u < count) oh = __builtin_fmaf(wh[h][s0 + u], v[u], oh);
+      }
+      float ob = 0.f;
+#pragma unroll
+      for (int c = 0; c < kBf16Parts; ++c) ob = __builtin_fmaf(wb[h][c], vb[it][c], ob);
+      orot[h][k] = oh;
+      obf[h][k] = ob;
+    }
   }
   __syncthreads();
   // history output back to the model domain: x_i = sum_k y_k R_V[i][k]
@@ -627,10 +681,10 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   if (kh == 0) {
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      const float lh = lse_s[h][0], lb = lse_s[h][1];
-      const float mx = fmaxf(lh, lb);
+      const float lh = lse_s[h][0], lbb = lse_s[h][1];
+      const float mx = fmaxf(lh, lbb);
       const float whh = lh == -INFINITY ? 0.f : expf(lh - mx);
-      const float wbb = lb == -INFINITY ? 0.f : expf(lb - mx);
+      const float wbb = lbb == -INFINITY ? 0.f : expf(lbb - mx);
       const float den = whh + wbb;
       a.out[(bhead0 + h) * kDim + i] = den > 0.f ? (whh * oh[h] + wbb * obf[h][i]) / den : 0.f;
       if (a.lse_out != nullptr && i == 0) a.lse_out[bhead0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;

@@ -52,6 +52,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+struct WaveMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct WaveAdd {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Reduction over the whole wave: DPP steps inside each 16-lane row (every
+// lane of a row ends with the row's result), then the four rows read back
+// with v_readlane.  The result is uniform.  Much shorter than a chain of
+// cross-lane permutes through LDS.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
+  int x = __float_as_int(v);
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
+  x = __float_as_int(op(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(x, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(x, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(x, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(x, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 // log2(e) / sqrt(128): scores are kept in base-2 units inside the kernels.
 constexpr float kScoreScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;
 constexpr float kLn2 = 0.6931471805599453f;
