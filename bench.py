@@ -296,28 +296,34 @@ def quarters(xs):
 
 
 def bandwidth_probes(ok, torch, HipEvent, stream, settle_s: float = 0.3, nbytes: int = 4 << 30):
-    """HBM read ceiling (the library's read probe over nbytes, non-temporal
-    and plain 16-byte loads, alternated for about settle_s seconds; median
-    GB/s of the second half of each kind's passes) and a device copy of
-    nbytes / 2 (read + write bytes / time, median of 5; the 2 GiB copy the
-    traffic counters are scaled by)."""
+    """HBM read ceiling: the library's read probes over nbytes (grid-stride
+    16-byte loads, non-temporal and plain, and the block-streaming probe,
+    2048 one-wave workgroups reading 4 KB blocks front to back with
+    non-temporal loads, the history kernel's access pattern), alternated for
+    about settle_s seconds; median GB/s of the second half of each kind's
+    passes; the ceiling is the fastest kind.  Also a device copy of nbytes /
+    2 (read + write bytes / time, median of 5; the 2 GiB copy the traffic
+    counters are scaled by)."""
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    times = {True: [], False: []}
+    kinds = {"read_nontemporal_gbs": lambda: ok.oscar_probe_read(buf, nbytes, True, sink, stream),
+             "read_plain_gbs": lambda: ok.oscar_probe_read(buf, nbytes, False, sink, stream),
+             "read_blocks_gbs": lambda: ok.oscar_probe_read_blocks(buf, nbytes, True, 2048, sink, stream)}
+    times = {k: [] for k in kinds}
     t_end = time.perf_counter() + settle_s
     e0, e1 = HipEvent(), HipEvent()
     while time.perf_counter() < t_end or min(len(v) for v in times.values()) < 6:
-        for nt in (True, False):
+        for k, run in kinds.items():
             e0.record(stream)
-            ok.oscar_probe_read(buf, nbytes, nt, sink, stream)
+            run()
             e1.record(stream)
             e1.synchronize()
-            times[nt].append(e0.elapsed_ms(e1))
+            times[k].append(e0.elapsed_ms(e1))
     rates = {}
-    for nt, ts in times.items():
+    for k, ts in times.items():
         ts = ts[len(ts) // 2:]
-        rates[nt] = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+        rates[k] = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
     half = nbytes // 2
     src, dst = buf[:half], buf[half:]
     copies = []
@@ -330,9 +336,10 @@ def bandwidth_probes(ok, torch, HipEvent, stream, settle_s: float = 0.3, nbytes:
     copy_gbs = 2 * half / (float(np.median(copies)) * 1e-3) / 1e9
     del buf, sink
     torch.cuda.empty_cache()
-    return {"read_nontemporal_gbs": round(rates[True], 1), "read_plain_gbs": round(rates[False], 1),
-            "read_ceiling_gbs": round(max(rates.values()), 1), "copy_gbs": round(copy_gbs, 1),
-            "passes": len(times[True]) + len(times[False]), "buffer_bytes": nbytes}
+    res = {k: round(v, 1) for k, v in rates.items()}
+    res.update(read_ceiling_gbs=round(max(rates.values()), 1), copy_gbs=round(copy_gbs, 1),
+               passes=sum(len(v) for v in times.values()), buffer_bytes=nbytes)
+    return res
 
 
 def main() -> int:

@@ -136,6 +136,8 @@ _SIGS = [
     ("oscar_last_error", ctypes.c_char_p, []),
     ("oscar_probe_read", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    ("oscar_probe_read_blocks", ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_void_p, ctypes.c_void_p]),
 ]
 EXPORTED = [s[0] for s in _SIGS]
 
@@ -429,6 +431,12 @@ def oscar_history_kernel_for(dims, options=None) -> int:
 def oscar_probe_read(buf, nbytes: int, nontemporal: bool, sink, stream=None) -> None:
     """One pass of the HBM read probe over nbytes of buf (include/oscar_probe.h)."""
     _check(lib().oscar_probe_read(_ptr(buf), nbytes, 1 if nontemporal else 0, _ptr(sink), _stream(stream)))
+
+
+def oscar_probe_read_blocks(buf, nbytes: int, nontemporal: bool, waves: int, sink, stream=None) -> None:
+    """One pass of the block-streaming read probe (include/oscar_probe.h)."""
+    _check(lib().oscar_probe_read_blocks(_ptr(buf), nbytes, 1 if nontemporal else 0, waves, _ptr(sink),
+                                         _stream(stream)))
 
 
 def oscar_last_error() -> str:

@@ -28,6 +28,15 @@ extern "C" {
  * OSCAR_EINVAL otherwise.  Time it with events around the call. */
 int oscar_probe_read(const void* buf, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
 
+/* The history kernel's access pattern without its arithmetic: `waves`
+ * one-wave workgroups, each reading its own contiguous bytes / waves share
+ * front to back in 4096-byte blocks (four 16-byte loads per lane, each 1 KB
+ * across the wave), four blocks in flight.  Loads are non-temporal when
+ * `nontemporal` is non-zero; `sink` as above.  buf must be 16-byte aligned,
+ * waves > 0 and bytes a multiple of waves x 4096; OSCAR_EINVAL otherwise. */
+int oscar_probe_read_blocks(const void* buf, size_t bytes, int32_t nontemporal, int32_t waves, uint32_t* sink,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

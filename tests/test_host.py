@@ -203,6 +203,12 @@ def test_probe_rejects_misaligned_buffers():
             ok.oscar_probe_read(buf, n, True, 0x1000, 0)
         assert e.value.code == ok.OSCAR_EINVAL
     ok.oscar_probe_read(0x1000, 0, False, 0x1000, 0)    # nothing to read
+    for buf, n, waves in ((0x1001, 8192, 2), (0x1000, 8192 + 16, 2), (0x1000, 4096, 2), (0x1000, 8192, 0),
+                          (0, 8192, 2)):
+        with pytest.raises(ok.OscarError) as e:
+            ok.oscar_probe_read_blocks(buf, n, True, waves, 0x1000, 0)
+        assert e.value.code == ok.OSCAR_EINVAL
+    ok.oscar_probe_read_blocks(0x1000, 0, True, 4, 0x1000, 0)   # nothing to read
 
 
 def test_history_kernel_selector():
