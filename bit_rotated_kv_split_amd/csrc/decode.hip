@@ -108,8 +108,9 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   // int8 digit operands: row = 4*h + digit, 32 rows; for channel half hf and
   // lane group kg, byte e = 4*j + b2 of the row holds channel
   // 16*(4*hf + kg) + 4*b2 + j.  The matrix-core kernel feeds that channel's
-  // 2-bit code masked in place, i.e. multiplied by 4^j for j < 3, so the
-  // operand holds q / 4^j for those slots (rounded on its own, coarser grid).
+  // 2-bit code masked in place, i.e. multiplied by 4^j (64 (code - 2) for
+  // j = 3, whose codes are stored XOR 2), so the operand holds q / 4^j for
+  // those slots (rounded on its own, coarser grid).
   uint8_t* qp = qpack + (static_cast<size_t>(b) * hkv + kvh) * kQPackBytes;
   // the second operand (Lloyd-Max codebook only) holds q * lm_ratio on the
   // same fixed-point grid, so both code planes accumulate into one result
@@ -125,7 +126,7 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
       const int h = row >> 2, digit = row & 3;
       uint32_t word = 0;
       if (h < GQ) {
-        const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : 1.f);
+        const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : (j == 3 ? 0.015625f : 1.f));
 #pragma unroll
         for (int b2 = 0; b2 < 4; ++b2) {
           const int ch = 16 * (4 * hf + kg) + 4 * b2 + j;
@@ -236,7 +237,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
       for (int gi = 0; gi < NG; ++gi) dot[h][gi] = 0.f;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const uint32_t w = words[d * 64 + qo];
+      const uint32_t w = words[d * 64 + qo] ^ kTopFieldFlip;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float code = code_level<LM>((w >> (2 * i)) & 3u, a.lev_lo, a.lev_hi);
@@ -295,7 +296,7 @@ __global__ void __launch_bounds__(256) hist_valu_kernel(HistParams a) {
       for (int h = 0; h < GQ; ++h) accv[h] = 0.f;
 #pragma unroll
       for (int wq = 0; wq < 4; ++wq) {
-        const uint32_t w = words[512 + v_word_index(c, wq)];
+        const uint32_t w = words[512 + v_word_index(c, wq)] ^ kTopFieldFlip;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float code = code_level<LM>((w >> (2 * i)) & 3u, a.lev_lo, a.lev_hi);

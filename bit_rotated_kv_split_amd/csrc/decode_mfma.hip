@@ -12,10 +12,16 @@
 //   P' . code  A = p * value-scale per token as 4 signed base-256 digits
 //              (rows = head x digit), B = value codes as int8.
 // A word of sixteen 2-bit codes gives the four int8 operand registers as
-// w & 0x03030303 << 2j (j = 0, 1, 2: the code times 4^j, masked in place)
-// and (w >> 6) & 0x03030303, five operations; the A operand of those slots
-// carries the matching 4^-j (query digits are rounded on that grid, P'
-// digits are computed from floats and lose nothing).
+// w & 0x03030303 << 2j, four operations: the code times 4^j masked in place
+// for j = 0, 1, 2, and for j = 3, whose codes are stored XOR 2, the signed
+// byte 64 (code - 2).  The A operand of those slots carries the matching
+// 4^-j (query digits are rounded on that grid, P' digits are computed from
+// floats and lose nothing).  The -2 of the j = 3 slots adds -128 times the
+// digit to every product: for q . code the accumulators start from +128
+// times the query's j = 3 digit sums (one set of products per wave, before
+// the pages); for P' . code the same sums of the P' digits are accumulated
+// per page by one more product against a constant operand, and added back
+// when the accumulators are read.
 //
 // Softmax bookkeeping is amortised over pages.  Each head keeps a reference
 // maximum m and a fixed-point unit u; tokens use p = 2^(score - m) and
@@ -95,28 +101,40 @@ constexpr float kDigitLimit = 2130706432.0f;
 constexpr float kDigitUnitMax = 2147483648.0f; // the unit puts a page's largest weight at 2^28
 constexpr uint32_t kDigitBias = 0x80808080u;
 // Pages a head's int32 accumulators may take between folds: a page adds at
-// most 64 * 128 * 48 to a digit row.
-constexpr int kFoldPages = 4096;
+// most 64 * 128 * 128 to a digit row (the j = 3 operand bytes reach -128).
+constexpr int kFoldPages = 2047;
 
-// Codes at positions 4b+j of a 16-code word -> byte b of result j, times
-// 4^j for j < 3.
+// Codes at positions 4b+j of a stored 16-code word -> byte b of result j:
+// the code times 4^j for j < 3, and 64 (code - 2) for j = 3 (stored XOR 2).
 __device__ __forceinline__ v4i unpack16(uint32_t w) {
   v4i r;
   r.x = static_cast<int>(w & 0x03030303u);
   r.y = static_cast<int>(w & 0x0C0C0C0Cu);
   r.z = static_cast<int>(w & 0x30303030u);
-  r.w = static_cast<int>((w >> 6) & 0x03030303u);
+  r.w = static_cast<int>(w & 0xC0C0C0C0u);
   return r;
 }
 
-// High bits of the masked codes of unpack16: 2 b1 4^j in place of c 4^j.
+// High bits of the masked codes of unpack16: 2 b1 4^j in place of c 4^j,
+// and for j = 3 (stored bit 7 = not b1) the signed byte 64 (2 b1 - 2).
 __device__ __forceinline__ v4i high_bits(const v4i& r) {
   v4i h;
   h.x = r.x & 0x02020202;
   h.y = r.y & 0x08080808;
   h.z = r.z & 0x20202020;
-  h.w = r.w & 0x02020202;
+  h.w = r.w & static_cast<int>(0x80808080u);
   return h;
+}
+
+// Operand with +64 in every j = 3 slot: a product against it sums the A
+// operand's j = 3 digits (times 64) along each row.
+__device__ __forceinline__ v4i j3_ones() {
+  v4i r;
+  r.x = 0;
+  r.y = 0;
+  r.z = 0;
+  r.w = 0x40404040;
+  return r;
 }
 
 // value of the signed base-256 digit rows of q . code: each row sums at most
@@ -258,6 +276,14 @@ struct WaveState {
   float m_ref[NHB];        // reference maximum (log2 units)
   float unit[NHB][NG];     // P' fixed-point unit
   float inv[NHB][NG];      // 4^-j / unit for this lane's token residue j
+  // the j = 3 P' sums are counted by an extra product per group for G >= 64;
+  // at G = 32 (four groups, the register budget is spent) the correction
+  // joins the zero-point sums instead (zc)
+  static constexpr bool kDcorr = NG <= 2;
+  v4i kc[NHB][NG];         // q . code start values: 128 x the query's j = 3 digit sums per product
+  v4i dcorr[NHB][kDcorr ? NG : 1];   // 64 x the j = 3 P' digit sums per group (added back x 2 when read)
+  float zc;                // this lane's value-zero coefficient of the scale: -hi (Lloyd-Max), plus
+                           // the j = 3 correction when !kDcorr
   v4i dacc[NHB][8];        // int32 digit accumulators of P' . code, channel block cb
   v4i dacc1[NHB][8];       // Lloyd-Max only: the same for the 2 b1 plane
   float accf[NHB][8];      // folded float accumulators
@@ -285,8 +311,12 @@ struct HistSmem {
 // level products of channel block cb.
 template <bool LM, int NHB, int G>
 __device__ __forceinline__ float acc_value(const WaveState<NHB, G>& st, int hb, int cb, float ka, float kb) {
-  if constexpr (LM) return ka * p_digits(st.dacc[hb][cb]) + kb * p_digits(st.dacc1[hb][cb]);
-  else return p_digits(st.dacc[hb][cb]);
+  // the j = 3 slots counted code - 2: add back 2 x their P' sums (both
+  // code planes of the Lloyd-Max codebook carry the same offset)
+  float corr = 0.f;
+  if constexpr (WaveState<NHB, G>::kDcorr) corr = 2.f * p_digits(st.dcorr[hb][(16 * cb) / G]);
+  if constexpr (LM) return ka * (p_digits(st.dacc[hb][cb]) + corr) + kb * (p_digits(st.dacc1[hb][cb]) + corr);
+  else return p_digits(st.dacc[hb][cb]) + corr;
 }
 
 template <bool LM, int NHB, int G>
@@ -295,9 +325,10 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
                                     HistSmem<NHB, kDim / G>& sm, int lane, float ka, float kb) {
   constexpr int NG = kDim / G;
   // P' of this lane's tokens (residue j = n % 4 in the K-slot order) meets
-  // codes masked in place, i.e. times 4^j for j < 3: carry 4^-j here
+  // codes masked in place, i.e. times 4^j (64 (code - 2) for j = 3): carry
+  // 4^-j here
   const int jr = threadIdx.x & 3;
-  const float slot = jr == 1 ? 0.25f : (jr == 2 ? 0.0625f : 1.f);
+  const float slot = jr == 1 ? 0.25f : (jr == 2 ? 0.0625f : (jr == 3 ? 0.015625f : 1.f));
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float pm = row_reduce(fmaxf(fmaxf(sc[hb][0], sc[hb][1]), fmaxf(sc[hb][2], sc[hb][3])), MaxOp());
@@ -311,6 +342,13 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
       const v4i z = {0, 0, 0, 0};
       st.dacc[hb][cb] = need[hb] ? z : st.dacc[hb][cb];
       if constexpr (LM) st.dacc1[hb][cb] = need[hb] ? z : st.dacc1[hb][cb];
+    }
+    if constexpr (WaveState<NHB, G>::kDcorr) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const v4i z = {0, 0, 0, 0};
+        st.dcorr[hb][gi] = need[hb] ? z : st.dcorr[hb][gi];
+      }
     }
     st.ls[hb] *= alpha;
 #pragma unroll
@@ -346,7 +384,6 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
     const v4i b1 = unpack16(static_cast<uint32_t>(cur.kw[1][m]));
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const v4i zero = {0, 0, 0, 0};
       float s;
       if constexpr (NG == 4) {
         // two groups per half: one product per group against the operand
@@ -358,7 +395,8 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
           const v4i& bc = hf ? b1 : b0;
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qam[hb][hf][sub], bc, zero, 0, 0, 0);
+            v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qam[hb][hf][sub], bc, st.kc[hb][2 * hf + sub], 0, 0,
+                                                          0);
             if constexpr (LM)
               d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qbm[hb][hf][sub], high_bits(bc), d, 0, 0, 0);
             const int gi = 2 * hf + sub;
@@ -375,7 +413,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
         // carries ka; zero - hi * scale takes the rest
         const v4i h0 = high_bits(b0), h1 = high_bits(b1);
         if constexpr (NG == 1) {
-          v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+          v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
           d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
           d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][0], h0, d, 0, 0, 0);
           d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][1], h1, d, 0, 0, 0);
@@ -384,8 +422,8 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
           const float kz = __builtin_fmaf(-lm_hi, ks, __uint_as_float(sz & 0xFFFF0000u));
           s = __builtin_fmaf(ks * st.qs[hb], q_digits(d), kz * st.qz[hb][0]);
         } else {
-          v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
-          v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
+          v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
+          v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, st.kc[hb][1], 0, 0, 0);
           d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][0], h0, d0, 0, 0, 0);
           d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][1], h1, d1, 0, 0, 0);
           const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
@@ -396,14 +434,14 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
               __builtin_fmaf(ks1 * st.qs[hb], q_digits(d1), kz1 * st.qz[hb][1]);
         }
       } else if constexpr (NG == 1) {
-        v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
+        v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
         const uint32_t sz = cur.ksz[m];
         s = __builtin_fmaf(__uint_as_float(sz << 16) * st.qs[hb], q_digits(d),
                            __uint_as_float(sz & 0xFFFF0000u) * st.qz[hb][0]);
       } else {
-        const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, zero, 0, 0, 0);
-        const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, zero, 0, 0, 0);
+        const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
+        const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, st.kc[hb][1], 0, 0, 0);
         const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
         s = __builtin_fmaf(__uint_as_float(s0 << 16) * st.qs[hb], q_digits(d0),
                            __uint_as_float(s0 & 0xFFFF0000u) * st.qz[hb][0]) +
@@ -480,7 +518,7 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       for (int m = 0; m < 4; ++m) {
         const uint32_t sz = vsz[m * NG + gi];
         float vz = __uint_as_float(sz & 0xFFFF0000u);
-        if constexpr (LM) vz = __builtin_fmaf(-lm_hi, __uint_as_float(sz << 16), vz);
+        if constexpr (LM || !WaveState<NHB, G>::kDcorr) vz = __builtin_fmaf(st.zc, __uint_as_float(sz << 16), vz);
         zpage = __builtin_fmaf(pr[hb][m], vz, zpage);
         // floor with the carried fraction: the lane's rounded weights add up
         // to its exact ones within one unit
@@ -518,6 +556,14 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       for (int hb = 0; hb < NHB; ++hb)
         st.dacc1[hb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], bh, st.dacc1[hb][cb], 0, 0, 0);
     }
+  }
+  // the j = 3 P' digit sums of this page (64 x, every column alike)
+  if constexpr (WaveState<NHB, G>::kDcorr) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+        st.dcorr[hb][gi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], j3_ones(), st.dcorr[hb][gi], 0, 0, 0);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -594,12 +640,49 @@ hist_mfma_kernel(MfmaParams a) {
         }
       }
     }
+    // q . code start values: 128 x the j = 3 digit sums of each product's
+    // operands (two products against the +64 operand)
+    {
+      const v4i ones = j3_ones();
+#pragma unroll
+      for (int c = 0; c < NG; ++c) {
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int rep = 0; rep < 2; ++rep) {
+          if constexpr (NG == 1) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][hf], ones, acc, 0, 0, 0);
+              if constexpr (LM) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][hf], ones, acc, 0, 0, 0);
+            }
+          } else if constexpr (NG == 2) {
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][c], ones, acc, 0, 0, 0);
+            if constexpr (LM) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qb[hb][c], ones, acc, 0, 0, 0);
+          } else {
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qam[hb][c >> 1][c & 1], ones, acc, 0, 0, 0);
+            if constexpr (LM)
+              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qbm[hb][c >> 1][c & 1], ones, acc, 0, 0, 0);
+          }
+        }
+        st.kc[hb][c] = acc;
+        if constexpr (WaveState<NHB, G>::kDcorr) st.dcorr[hb][c] = v4i{0, 0, 0, 0};
+      }
+    }
     const int h = 4 * (wave + hb) + lg;
     head_ok[hb] = h < a.gq;
     st.qs[hb] = LM ? qscale[h] * a.lm_ka : qscale[h];
     st.m_ref[hb] = -INFINITY;
     st.ls[hb] = 0.f;
     st.since_fold = 0;
+    // value zero of a token: zero - hi * scale (Lloyd-Max), and without the
+    // extra products, + 2 (ka + kb or 1) * scale for the j = 3 tokens, whose
+    // P' . code products counted code - 2
+    {
+      const bool j3 = (lane & 3) == 3;
+      float zc = LM ? -a.lm_hi : 0.f;
+      if constexpr (!WaveState<NHB, G>::kDcorr) zc += j3 ? 2.f * (LM ? a.lm_ka + a.lm_kb : 1.f) : 0.f;
+      st.zc = zc;
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       st.qz[hb][gi] = head_ok[hb] ? a.qsum[(head0 + h) * 4 + gi] : 0.f;

@@ -82,8 +82,8 @@ read_history_kernel(const uint8_t* __restrict__ pages, const int32_t* __restrict
     const uint32_t* words = reinterpret_cast<const uint32_t*>(blk);
     const int slot = j & 63;
     uint32_t code;
-    if (!is_v) code = (words[(c >> 4) * 64 + qk_order(slot)] >> (2 * (c & 15))) & 3u;
-    else code = (words[512 + v_word_index(c, slot >> 4)] >> (2 * (slot & 15))) & 3u;
+    if (!is_v) code = ((words[(c >> 4) * 64 + qk_order(slot)] ^ kTopFieldFlip) >> (2 * (c & 15))) & 3u;
+    else code = ((words[512 + v_word_index(c, slot >> 4)] ^ kTopFieldFlip) >> (2 * (slot & 15))) & 3u;
     const uint16_t* sz = reinterpret_cast<const uint16_t*>(blk + kCodesBytes + (is_v ? kPage * ng * 4 : 0)) +
                          (qk_order(slot) * ng + gi) * 2;
     const float s = bf16_to_f32(sz[0]), z = bf16_to_f32(sz[1]);

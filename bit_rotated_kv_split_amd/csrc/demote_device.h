@@ -198,7 +198,7 @@ __device__ void store_tokens(const QuantSmem<NT>& sm, int nt, uint8_t* __restric
       uint32_t w = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) w |= static_cast<uint32_t>(sm.code[t][16 * d + i]) << (2 * i);
-      words[d * 64 + qk_order(slot0 + t)] = w;
+      words[d * 64 + qk_order(slot0 + t)] = w ^ kTopFieldFlip;
     }
   } else {
     // channel k: one value word holds slots 16w..16w+15 of this channel
@@ -206,7 +206,7 @@ __device__ void store_tokens(const QuantSmem<NT>& sm, int nt, uint8_t* __restric
     uint32_t bits = 0, mask = 0;
     for (int t = 0; t < nt; ++t) {
       const int sh = 2 * ((slot0 + t) & 15);
-      bits |= static_cast<uint32_t>(sm.code[t][k]) << sh;
+      bits |= code_bits(sm.code[t][k], (slot0 + t) & 15);
       mask |= 3u << sh;
     }
     uint32_t* wp = words + 512 + v_word_index(k, w);
@@ -262,7 +262,7 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
         uint32_t w = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) w |= static_cast<uint32_t>(sm.code[0][16 * k + i]) << (2 * i);
-        words[k * 64 + qk_order(slot)] = w;
+        words[k * 64 + qk_order(slot)] = w ^ kTopFieldFlip;
       }
     } else {
       // channel k's value word holds slots 16w .. 16w+15: clear this slot's
@@ -270,7 +270,7 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
       uint32_t* wp = words + 512 + v_word_index(k, slot >> 4);
       const int sh = 2 * (slot & 15);
       atomicAnd(wp, ~(3u << sh));
-      atomicOr(wp, static_cast<uint32_t>(sm.code[0][k]) << sh);
+      atomicOr(wp, code_bits(sm.code[0][k], slot & 15));
     }
     if (k < NG) {
       uint16_t* e = reinterpret_cast<uint16_t*>(blk + kCodesBytes + (is_v ? kPage * NG * 4 : 0)) +

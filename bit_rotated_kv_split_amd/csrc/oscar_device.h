@@ -16,6 +16,19 @@ constexpr int kCodesBytes = 4096;    // key + value words of one block
 
 __host__ __device__ constexpr int block_bytes(int G) { return kCodesBytes + 512 * (kDim / G); }
 
+// Stored form of a word of sixteen 2-bit codes (code i at bits 2i, 2i+1):
+// the code in the top two bits of each byte (i % 4 == 3) is kept XOR 2, so
+// a stored word is the plain packing XOR 0x80808080.  Masked in place
+// (word & 0xC0C0C0C0), that field then reads as the signed byte
+// 64 (code - 2): linear in the code, which lets the matrix-core kernel take
+// it with one AND instead of a shift and an AND.
+constexpr uint32_t kTopFieldFlip = 0x80808080u;
+
+// Stored bits of code c at position i of a word.
+__host__ __device__ constexpr uint32_t code_bits(uint32_t c, int i) {
+  return (c ^ ((i & 3) == 3 ? 2u : 0u)) << (2 * i);
+}
+
 // Position of slot t in the key-word rows and in the scale/zero tables:
 // the order in which the matrix-core history kernel's lanes consume tokens.
 __host__ __device__ __forceinline__ int qk_order(int t) {

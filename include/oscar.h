@@ -113,7 +113,9 @@ typedef struct oscar_rotation {
  *                then key scale/zero, then value scale/zero: entry qk(t) is
  *                  128/G pairs {scale, zero} of bf16.
  *              Words are 32-bit little endian; element i of a word sits at
- *              bits 2i..2i+1.  qk(t) = 16*(t/16) + 4*(t%4) + (t/4)%4.
+ *              bits 2i..2i+1, and the element in the top two bits of each
+ *              byte (i % 4 == 3) is stored XOR 2 (a stored word is the plain
+ *              packing XOR 0x80808080).  qk(t) = 16*(t/16) + 4*(t%4) + (t/4)%4.
  *              The stored channel index is the rotated one (after . R).
  * sink_k/v:    bf16 [B][Hkv][64][128]; position p < 64 at slot p.
  * recent_k/v:  bf16 [B][Hkv][256][128]; position p >= 64 at slot (p-64) % 256.

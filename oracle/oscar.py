@@ -411,7 +411,14 @@ def demote(x_bits: np.ndarray, r32: np.ndarray, clip32: np.ndarray, group: int, 
 #   then K scale/zero, then V scale/zero: entry qk_order(t) is 128/G pairs
 #   (scale, zero) of bfloat16, 4*(128/G) bytes per slot.
 # qk_order(t) = 16*(t//16) + 4*(t%4) + (t//4)%4.
+# The code in the top two bits of every byte (element i with i % 4 == 3) is
+# stored XOR 2: a stored word is the plain packing XOR 0x80808080.  (A
+# storage choice with no effect on any value: that element, masked in
+# place, then reads as the signed byte 64 (code - 2).)
 # ---------------------------------------------------------------------------
+
+TOP_FIELD_FLIP = 0x80808080
+
 
 def qk_order(t: int) -> int:
     return 16 * (t // 16) + 4 * (t % 4) + (t // 4) % 4
@@ -435,13 +442,13 @@ def pack_block(codes_k, s_k, z_k, codes_v, s_v, z_v, group: int) -> np.ndarray:
             w = 0
             for i in range(16):
                 w |= int(codes_k[t][16 * d + i]) << (2 * i)
-            words[d * 64 + qk_order(t)] = w
+            words[d * 64 + qk_order(t)] = w ^ TOP_FIELD_FLIP
     for c in range(HEAD_DIM):
         for wi in range(4):
             w = 0
             for i in range(16):
                 w |= int(codes_v[16 * wi + i][c]) << (2 * i)
-            words[512 + (c // 64) * 256 + (wi * 16 + c % 16) * 4 + (c // 16) % 4] = w
+            words[512 + (c // 64) * 256 + (wi * 16 + c % 16) * 4 + (c // 16) % 4] = w ^ TOP_FIELD_FLIP
     sz = np.zeros((2, PAGE, ng, 2), dtype=np.uint16)
     for t in range(PAGE):
         o = qk_order(t)
@@ -463,12 +470,12 @@ def unpack_block(block: np.ndarray, group: int):
     codes_v = np.zeros((PAGE, HEAD_DIM), dtype=np.uint8)
     for t in range(PAGE):
         for d in range(8):
-            w = int(words[d * 64 + qk_order(t)])
+            w = int(words[d * 64 + qk_order(t)]) ^ TOP_FIELD_FLIP
             for i in range(16):
                 codes_k[t][16 * d + i] = (w >> (2 * i)) & 3
     for c in range(HEAD_DIM):
         for wi in range(4):
-            w = int(words[512 + (c // 64) * 256 + (wi * 16 + c % 16) * 4 + (c // 16) % 4])
+            w = int(words[512 + (c // 64) * 256 + (wi * 16 + c % 16) * 4 + (c // 16) % 4]) ^ TOP_FIELD_FLIP
             for i in range(16):
                 codes_v[16 * wi + i][c] = (w >> (2 * i)) & 3
     sz = block[4096:].view("<u2").reshape(2, PAGE, ng, 2)

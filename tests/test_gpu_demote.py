@@ -48,8 +48,19 @@ def make_rot(kind, hkv, rng):
 CODEBOOK_ID = {"uniform": ok.CODEBOOK_UNIFORM, "lloyd-max": ok.CODEBOOK_LLOYD_MAX}
 
 
+def slot_bits(slots, group):
+    """Mask of the code bits of the given slots in a block (codes 3 and 0
+    differ in exactly those bits)."""
+    ng = 128 // group
+    mine = np.zeros((64, 128), np.uint8)
+    mine[slots] = 3
+    z = np.zeros((64, ng), np.float32)
+    return O.pack_block(mine, z, z, mine, z, z, group) ^ O.pack_block(mine * 0, z, z, mine * 0, z, z, group)
+
+
 def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid, codebook="uniform"):
-    """Oracle bytes of one page block whose first n_valid slots hold tokens."""
+    """Oracle bytes of one page block, zero-filled before, whose first
+    n_valid slots hold tokens (the other slots' bits stay 0)."""
     ng = 128 // group
     codes_k = np.zeros((64, 128), dtype=np.uint8)
     codes_v = np.zeros((64, 128), dtype=np.uint8)
@@ -62,7 +73,9 @@ def expected_block(k_bits, v_bits, rk, rv, ck, cv, group, n_valid, codebook="uni
         codes_k[:n_valid], sk[:n_valid], zk[:n_valid] = c, s, z
         c, s, z = O.demote(v_bits[:n_valid], rv, cv, group, codebook)
         codes_v[:n_valid], sv[:n_valid], zv[:n_valid] = c, s, z
-    return O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
+    blk = O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
+    blk[:4096] &= slot_bits(slice(0, n_valid), group)[:4096]
+    return blk
 
 
 @pytest.mark.parametrize("codebook", ["uniform", "lloyd-max"])
@@ -349,11 +362,9 @@ def test_demote_keeps_other_slots_of_reused_pages(group, codebook):
         codes_k[j0:j1], sk[j0:j1], zk[j0:j1] = O.demote(k_all[sl, j], rk[j], ck[j], group, codebook)
         codes_v[j0:j1], sv[j0:j1], zv[j0:j1] = O.demote(v_all[sl, j], rv[j], cv[j], group, codebook)
         new = O.pack_block(codes_k, sk, zk, codes_v, sv, zv, group)
-        mine = np.zeros((64, 128), np.uint8)
-        mine[j0:j1] = 3
-        mask = O.pack_block(mine, sk * 0, zk * 0, mine, sv * 0, zv * 0, group)   # code bits of the slots
+        mask = slot_bits(slice(j0, j1), group)   # code bits of the slots
         exp = stale[pt[0, 0], j].copy()
-        exp[:4096] = (exp[:4096] & ~mask[:4096]) | new[:4096]
+        exp[:4096] = (exp[:4096] & ~mask[:4096]) | (new[:4096] & mask[:4096])
         for t in range(j0, j1):                  # scale/zero entries of the slots
             for half in range(2):
                 a = 4096 + half * 64 * ng * 4 + O.qk_order(t) * ng * 4

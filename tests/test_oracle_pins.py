@@ -311,7 +311,8 @@ def test_pack_unpack_roundtrip_and_byte_values():
 def test_pack_byte_is_four_codes_lsb_first_all_values():
     """Every byte value 0..255 occurs, and each byte equals sum c_i 4^i of the
     four codes it holds (four consecutive channels of one token for K, four
-    consecutive tokens of one channel for V)."""
+    consecutive tokens of one channel for V) with its top bit flipped (the
+    fourth code stored XOR 2)."""
     ck = np.zeros((64, 128), dtype=np.uint8)
     cv = np.zeros((64, 128), dtype=np.uint8)
     for t in range(64):
@@ -334,7 +335,7 @@ def test_pack_byte_is_four_codes_lsb_first_all_values():
             for j in range(4):
                 byte = int(blk[word_off + j])
                 m = 4 * d + j
-                assert byte == sum(int(ck[t, 4 * m + i]) << (2 * i) for i in range(4))
+                assert byte == sum(int(ck[t, 4 * m + i]) << (2 * i) for i in range(4)) ^ 0x80
                 seen.add(byte)
     assert seen == set(range(256))
     seen = set()
@@ -344,7 +345,7 @@ def test_pack_byte_is_four_codes_lsb_first_all_values():
             for j in range(4):
                 byte = int(blk[word_off + j])
                 tok0 = 16 * w + 4 * j
-                assert byte == sum(int(cv[tok0 + i, c]) << (2 * i) for i in range(4))
+                assert byte == sum(int(cv[tok0 + i, c]) << (2 * i) for i in range(4)) ^ 0x80
                 seen.add(byte)
     assert seen == set(range(256))
 
