@@ -15,11 +15,12 @@ library from a synthetic calibration sequence before timing.
 
 Order of one run:
   1. calibration, cache fill, per-step inputs (untimed);
-  2. bandwidth probes: a streaming HBM read (non-temporal and plain loads)
-     repeated for about 0.3 s, and a 2 GiB copy.  They give the read
-     ceiling the roofline is compared against, and they leave the GPU at
-     its steady clocks, so the timed steps do not measure the clock ramp
-     that follows the idle setup;
+  2. bandwidth probes: streaming HBM reads (grid-stride non-temporal and
+     plain loads, and 4 KB blocks read front to back by one-wave
+     workgroups, the history kernel's access pattern) repeated for about
+     0.3 s, and a 2 GiB copy.  They give the read ceiling the roofline is
+     compared against, and they leave the GPU at its steady clocks, so the
+     timed steps do not measure the clock ramp that follows the idle setup;
   3. `warmup` untimed steps, then exactly `steps` timed steps between one
      pair of events: `value` and `ms_per_step`; each history launch between
      its own events (`roofline`, per-quarter means, shader clock); then
