@@ -76,6 +76,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_HIST_BUFFERS
 #define OSCAR_HIST_BUFFERS 2
 #endif
+// software-pipelined page loop (value half of page p-1 before the score
+// half of page p) for G >= 64: 32 x 100K Lloyd-Max 325.5 -> 320.9 us,
+// 1 x 100K 20.9 -> 20.3 us, G = 128 and 64 about 0.3 % faster; at G = 32
+// it measured 1 % slower and is not used there
+#ifndef OSCAR_HIST_PIPE
+#define OSCAR_HIST_PIPE 1
+#endif
 #ifndef OSCAR_HIST_MIN_WAVES
 #define OSCAR_HIST_MIN_WAVES 2
 #endif
@@ -300,7 +307,7 @@ struct WaveState {
 // LDS (one read-modify-write per page) to keep it out of the register budget.
 template <int NHB, int NG>
 struct HistSmem {
-  int32_t pop[NHB * NG][16][16];   // P' operand rows: [head block x group][4 h + digit][16 dwords]
+  int32_t pop[2][NHB * NG][16][16];   // P' operand rows: [page parity][head block x group][4 h + digit][16 dwords]
   double zacc[NHB * NG][64];
   int32_t pt[64];                  // page-table entries pt_base .. pt_base + 63 of the split
 };
@@ -370,10 +377,12 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
   }
 }
 
+// Score half of a page: q . code, the online softmax and the P' digit rows
+// of the page, written into P' slot `slot`.
 template <bool LM, int NHB, int G>
-__device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
-                                             int n_hist, int lane, HistSmem<NHB, kDim / G>& sm,
-                                             float lm_hi, float ka, float kb) {
+__device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
+                                           int n_hist, int lane, HistSmem<NHB, kDim / G>& sm, int slot,
+                                           float lm_hi, float ka, float kb) {
   constexpr int NG = kDim / G;
   const int n = lane & 15, lg = lane >> 4;
   // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n
@@ -531,18 +540,24 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       sm.zacc[hb * NG + gi][lane] += static_cast<double>(zpage);
       // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
 #pragma unroll
-      for (int d = 0; d < 4; ++d) sm.pop[hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(dig[d] ^ kDigitBias);
+      for (int d = 0; d < 4; ++d) sm.pop[slot][hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(dig[d] ^ kDigitBias);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // ---- P' . code accumulated in int32: column n = channel 16 cb + n, rows = head x digit
+}
+
+// Value half of a page: P' . code of the page's value codes against the P'
+// rows in slot `slot`, into the int32 accumulators.
+template <bool LM, int NHB, int G>
+__device__ __forceinline__ void value_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int lane,
+                                           HistSmem<NHB, kDim / G>& sm, int slot) {
+  constexpr int NG = kDim / G;
+  const int n = lane & 15, lg = lane >> 4;
+  // column n = channel 16 cb + n, rows = head x digit
   v4i pa[NHB][NG];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&sm.pop[hb * NG + gi][n][lg * 4]);
+    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&sm.pop[slot][hb * NG + gi][n][lg * 4]);
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
     const int gi = (16 * cb) / G;
@@ -565,9 +580,25 @@ __device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRe
       for (int gi = 0; gi < NG; ++gi)
         st.dcorr[hb][gi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[hb][gi], j3_ones(), st.dcorr[hb][gi], 0, 0, 0);
   }
+}
+
+// Orders one page's P' row writes before the reads that follow (a wave
+// reads rows other lanes wrote).
+__device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One whole page, scores then values (slot 0).
+template <bool LM, int NHB, int G>
+__device__ __forceinline__ void process_page(WaveState<NHB, G>& st, const PageRegs<G>& cur, int tok_base,
+                                             int n_hist, int lane, HistSmem<NHB, kDim / G>& sm,
+                                             float lm_hi, float ka, float kb) {
+  score_page<LM, NHB, G>(st, cur, tok_base, n_hist, lane, sm, 0, lm_hi, ka, kb);
+  wave_lds_fence();
+  value_page<LM, NHB, G>(st, cur, lane, sm, 0);
+  wave_lds_fence();
 }
 
 template <int G, int WAVES, int BUF, int MINW, bool LM>
@@ -736,22 +767,63 @@ hist_mfma_kernel(MfmaParams a) {
       // in: the loop head's wait then covers only the page it needs first
       __builtin_amdgcn_sched_barrier(0);
     }
-    // whole groups of BUF pages: one exit, at the latch, so the loads in
-    // flight at the loop head are the same on every path into it
-    const int groups = (p1 - p0) / BUF;
-    int p = p0;
-    for (int it = 0; it < groups; ++it, p += BUF) {
+    if constexpr (OSCAR_HIST_PIPE && G != 32) {
+      // Software-pipelined: each step takes the value half of the previous
+      // page (its matrix-core products) and then the score half of the next
+      // one, so the products of one page can run while the vector work of the
+      // next is issued.  P' rows alternate between two LDS slots by page
+      // parity.  The first page has no value half before it; the last page's
+      // value half follows the loop.  Page p0 + i lives in buf[i % BUF]; a
+      // step's loads go into the buffer whose value half has just been taken.
+      load_page<G, WAVES == 1, kStreamSz>(buf[BUF - 1], page_ptr(min(p0 + BUF - 1, p_last)), lane);
+      score_page<LM, NHB, G>(st, buf[0], p0 * kPage, n_hist, lane, sm, 0, a.lm_hi, a.lm_ka, a.lm_kb);
+      wave_lds_fence();
+      // pages p0 + 1 .. in whole groups of BUF (one exit, at the latch)
+      const int groups = (p1 - p0 - 1) / BUF;
+      int p = p0 + 1;
+      for (int it = 0; it < groups; ++it, p += BUF) {
 #pragma unroll
-      for (int k = 0; k < BUF; ++k) {
-        load_page<G, WAVES == 1, kStreamSz>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
-        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+        for (int k = 0; k < BUF; ++k) {
+          value_page<LM, NHB, G>(st, buf[k % BUF], lane, sm, (p + k - 1 - p0) & 1);
+          load_page<G, WAVES == 1, kStreamSz>(buf[k % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
+          score_page<LM, NHB, G>(st, buf[(k + 1) % BUF], (p + k) * kPage, n_hist, lane, sm, (p + k - p0) & 1, a.lm_hi,
+                                 a.lm_ka, a.lm_kb);
+          wave_lds_fence();
+        }
       }
-    }
-    // the last (p1 - p0) % BUF pages are already in buf[0 ..]
+      // the remaining (p1 - p0 - 1) % BUF pages are already loaded
+      const int rem = (p1 - p0 - 1) % BUF;
 #pragma unroll
-    for (int k = 0; k < BUF - 1; ++k)
-      if (p + k < p1)
-        process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+      for (int k = 0; k < BUF - 1; ++k)
+        if (k < rem) {
+          value_page<LM, NHB, G>(st, buf[k % BUF], lane, sm, (p + k - 1 - p0) & 1);
+          score_page<LM, NHB, G>(st, buf[(k + 1) % BUF], (p + k) * kPage, n_hist, lane, sm, (p + k - p0) & 1, a.lm_hi,
+                                 a.lm_ka, a.lm_kb);
+          wave_lds_fence();
+        }
+      // the last page's value half: page p1 - 1 = p0 + groups * BUF + rem, in buf[rem]
+#pragma unroll
+      for (int k = 0; k < BUF; ++k)
+        if (k == rem) value_page<LM, NHB, G>(st, buf[k], lane, sm, (p1 - 1 - p0) & 1);
+      wave_lds_fence();
+    } else {
+      // whole groups of BUF pages: one exit, at the latch, so the loads in
+      // flight at the loop head are the same on every path into it
+      const int groups = (p1 - p0) / BUF;
+      int p = p0;
+      for (int it = 0; it < groups; ++it, p += BUF) {
+#pragma unroll
+        for (int k = 0; k < BUF; ++k) {
+          load_page<G, WAVES == 1, kStreamSz>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
+          process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+        }
+      }
+      // the last (p1 - p0) % BUF pages are already in buf[0 ..]
+#pragma unroll
+      for (int k = 0; k < BUF - 1; ++k)
+        if (p + k < p1)
+          process_page<LM, NHB, G>(st, buf[k], (p + k) * kPage, n_hist, lane, sm, a.lm_hi, a.lm_ka, a.lm_kb);
+    }
   }
 
   // ---- partial output of this split (rotated value domain)

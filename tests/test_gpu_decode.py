@@ -114,8 +114,8 @@ def test_lloyd_max_codebook_ragged_edges(group, hq, hkv, kernel):
 @pytest.mark.parametrize("group,codebook", [(128, 0), (64, 1), (32, 0), (32, 1)])
 def test_stale_slots_past_the_end_are_ignored(kernel, group, codebook):
     """Pages and sink/recent buffers hold 0xFF bytes before the fill, so
-    every slot past a request's end keeps code 3 with a NaN bf16 scale and
-    zero.  Those slots carry no weight: the output matches the oracle (which
+    every slot past a request's end keeps stale codes with a NaN bf16 scale
+    and zero.  Those slots carry no weight: the output matches the oracle (which
     never sees them) and is finite, for both codebooks and every group
     size, GQA 4 and 8."""
     for hq in (8, 16):
