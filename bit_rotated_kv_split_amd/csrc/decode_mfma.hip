@@ -144,9 +144,9 @@ __device__ __forceinline__ v4i j3_ones() {
   return r;
 }
 
-// value of the signed base-256 digit rows of q . code: each row sums at most
-// four products of 64 digits (|digit| <= 128) and bytes (<= 48), so both
-// two-row integer sums fit in int32
+// value of the signed base-256 digit rows of q . code: a row sums 128
+// products of a digit (|d| <= 128) and a byte (|b| <= 128) plus its start
+// value, so both two-row integer sums fit in int32
 __device__ __forceinline__ float q_digits(const v4i& d) {
   const int lo = d.x + (d.y << 8);
   const int hi = d.z + (d.w << 8);
@@ -296,6 +296,7 @@ struct WaveState {
   float accf[NHB][8];      // folded float accumulators
   float ls[NHB];           // per-lane partial sum of p
   float carry[NHB][NG];    // rounding carry of this lane's P' digits, in [0, 1) units
+  float zf[NHB][NG];       // float32 zero-point sum of the pages since the last flush into zacc
   int since_fold;          // pages since every head's accumulators were folded
 };
 
@@ -303,8 +304,9 @@ struct WaveState {
 // p * value zero in float64: the zero-point term is common to every channel
 // of a group and large next to the output (it cancels against the code
 // term), so the rounding of a long float32 chain would come back
-// concentrated on a few channels after the rotation by R_V^T.  It lives in
-// LDS (one read-modify-write per page) to keep it out of the register budget.
+// concentrated on a few channels after the rotation by R_V^T.  Pages add
+// into a float32 register sum, flushed into zacc every 8 pages (a short
+// chain); zacc lives in LDS to keep it out of the register budget.
 template <int NHB, int NG>
 struct HistSmem {
   int32_t pop[2][NHB * NG][16][16];   // P' operand rows: [page parity][head block x group][4 h + digit][16 dwords]
@@ -361,6 +363,7 @@ __device__ __forceinline__ void rebase(WaveState<NHB, G>& st, const float (&sc)[
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       sm.zacc[hb * NG + gi][lane] *= static_cast<double>(alpha);
+      st.zf[hb][gi] *= alpha;
       float wmax = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -537,11 +540,21 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
       }
       uint32_t dig[4];
       transpose4x4(b[0], b[1], b[2], b[3], dig);
-      sm.zacc[hb * NG + gi][lane] += static_cast<double>(zpage);
+      st.zf[hb][gi] += zpage;
       // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
 #pragma unroll
       for (int d = 0; d < 4; ++d) sm.pop[slot][hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(dig[d] ^ kDigitBias);
     }
+  }
+  // every 8 pages the float32 zero-point sums go into the float64 ones
+  if ((st.since_fold & 7) == 0) {   // uniform
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        sm.zacc[hb * NG + gi][lane] += static_cast<double>(st.zf[hb][gi]);
+        st.zf[hb][gi] = 0.f;
+      }
   }
 }
 
@@ -720,6 +733,7 @@ hist_mfma_kernel(MfmaParams a) {
       st.unit[hb][gi] = 0.f;
       st.inv[hb][gi] = 0.f;
       sm.zacc[hb * NG + gi][lane] = 0.0;
+      st.zf[hb][gi] = 0.f;
       st.carry[hb][gi] = 0.5f;
     }
 #pragma unroll
@@ -833,7 +847,7 @@ hist_mfma_kernel(MfmaParams a) {
     double zsum[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      zsum[gi] = row_sum_f64(sm.zacc[hb * NG + gi][lane]);
+      zsum[gi] = row_sum_f64(sm.zacc[hb * NG + gi][lane] + static_cast<double>(st.zf[hb][gi]));
     }
     if (!head_ok[hb]) continue;
     const int h = 4 * (wave + hb) + lg;
