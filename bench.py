@@ -29,8 +29,9 @@ Order of one run:
   4. `cold_start`: after 1 s with the GPU idle, 20 more timed steps with no
      warm-up (diagnostic: the cost of starting from idle clocks);
   5. the all-bf16 baseline's steps (the 32 x 100K workloads);
-  6. the oracle on the host cores (`cpu_baseline`), in worker processes
-     started before the GPU is touched.
+  6. the oracle on the host cores (`cpu_baseline`): the plain C++ oracle
+     on OpenMP threads, and the numpy oracle in worker processes started
+     before the GPU is touched.
 
 Prints ONE JSON line.
 """
@@ -204,71 +205,105 @@ class OracleWorkers:
             p.join(timeout=10)
 
 
-def cpu_baseline(workers: OracleWorkers, model, layout, cal_host, lens, parallel_requests: int = 6,
-                 single_pairs: int = 12):
+def cpu_baseline(workers: OracleWorkers, model, layout, cal_host, lens, cpp_requests: int = 4,
+                 cpp_single_pairs: int = 3, numpy_requests: int = 2):
     """The oracle (as it stands) on the host cores, at the workload's final
     lengths, one (request, KV head) pair per task: demote the pair's history
-    and attend in float64 (oracle.request_attention).  The parallel leg gives
-    the pairs of requests 0 .. parallel_requests-1 (every KV head) to all
-    workers at once; the single-thread leg runs `single_pairs` pairs (KV
-    head 0 of successive requests) on one worker.  Both are scaled to GB/s
-    of the same algorithmic bytes.  The pairs' tokens come from the GPU twin
-    of the seeded generator (bit-identical to synth.gen; not timed)."""
+    and attend in float64.  `value` is the plain C++ oracle
+    (oracle/oscar_ref.cpp) with OpenMP threads over the pairs of requests
+    0 .. cpp_requests-1 (every KV head), as many threads as this process's
+    CPU share (at most 16); `single_thread` runs `cpp_single_pairs` pairs (KV
+    head 0 of successive requests) on one thread.  `numpy_oracle` is the
+    numpy oracle (BLAS products) over the pairs of numpy_requests requests
+    in the worker processes, one BLAS thread each.  Every leg is scaled to
+    GB/s of the same algorithmic bytes.  The pairs' tokens come from the GPU
+    twin of the seeded generator (bit-identical to synth.gen; not timed)."""
     import torch
+    from oracle import cpp as C
     from synth import gpu as synth_gpu
     w = model.w
     g, hkv = w.gqa, w.num_kv_heads
     stream = torch.cuda.current_stream().cuda_stream
     codebook = ("uniform", "lloyd-max")[w.codebook]
     q_all = model.queries(0, w.batch)
+    fetched = {}
 
-    def pair_tasks(b, heads):
-        L = int(lens[b])
-        host = {}
-        for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
-            buf = torch.empty((L, hkv, 128), dtype=torch.int16, device="cuda")
-            sc = torch.from_numpy(np.ascontiguousarray(scale)).cuda()
-            for src, p0, n in layout.src_ranges(b, 0, L):
-                synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * hkv * 128, n, hkv, hkv * 128, 128,
-                                  w.seed, which, src, p0, sc, stream)
-            torch.cuda.synchronize()
-            host[which] = buf.cpu().numpy().view(np.uint16)
-            del buf
-        nb = step_bytes(np.array([L]), 1, g, w.group_size)[1]
-        out = []
-        for j in heads:
-            args = (q_all[b][j * g:(j + 1) * g], np.ascontiguousarray(host["k"][:, j:j + 1]),
-                    np.ascontiguousarray(host["v"][:, j:j + 1]), cal_host["r_k32"][j:j + 1],
-                    cal_host["r_v32"][j:j + 1], cal_host["clip_k"][j:j + 1], cal_host["clip_v"][j:j + 1],
-                    w.group_size, codebook)
-            out.append((args, nb))
-        return out
+    def tokens(b):
+        """Host bf16 bits [L][Hkv][128] of request b's K and V tokens."""
+        if b not in fetched:
+            L = int(lens[b])
+            host = {}
+            for which, scale in (("k", model.k_scale), ("v", model.v_scale)):
+                buf = torch.empty((L, hkv, 128), dtype=torch.int16, device="cuda")
+                sc = torch.from_numpy(np.ascontiguousarray(scale)).cuda()
+                for src, p0, n in layout.src_ranges(b, 0, L):
+                    synth_gpu.fill_kv(buf.data_ptr() + 2 * p0 * hkv * 128, n, hkv, hkv * 128, 128,
+                                      w.seed, which, src, p0, sc, stream)
+                torch.cuda.synchronize()
+                host[which] = buf.cpu().numpy().view(np.uint16)
+                del buf
+            fetched[b] = host
+        return fetched[b]
+
+    def pair_bytes(b):
+        return step_bytes(np.array([int(lens[b])]), 1, g, w.group_size)[1]
+
+    def cpp_pairs(b, heads):
+        h = tokens(b)
+        L = h["k"].shape[0]
+        k, v = h["k"].reshape(L, hkv * 128), h["v"].reshape(L, hkv * 128)
+        return [{"q": q_all[b][j * g:(j + 1) * g], "k": k, "v": v, "off": j * 128,
+                 "r_k": cal_host["r_k32"][j], "r_v": cal_host["r_v32"][j],
+                 "clip_k": cal_host["clip_k"][j], "clip_v": cal_host["clip_v"][j]} for j in heads]
+
+    def numpy_tasks(b):
+        h = tokens(b)
+        return [((q_all[b][j * g:(j + 1) * g], np.ascontiguousarray(h["k"][:, j:j + 1]),
+                  np.ascontiguousarray(h["v"][:, j:j + 1]), cal_host["r_k32"][j:j + 1],
+                  cal_host["r_v32"][j:j + 1], cal_host["clip_k"][j:j + 1], cal_host["clip_v"][j:j + 1],
+                  w.group_size, codebook), pair_bytes(b)) for j in range(hkv)]
+
+    threads = cpu_worker_count()
+    reqs = list(range(min(cpp_requests, w.batch)))
+    par = [p for b in reqs for p in cpp_pairs(b, range(hkv))]
+    par_bytes = sum(pair_bytes(b) * hkv for b in reqs)
+    C.lib()
+    t0 = time.perf_counter()
+    C.attend_pairs(par, g, w.group_size, codebook, threads)
+    par_wall = time.perf_counter() - t0
+    singles = list(range(min(cpp_single_pairs, w.batch)))
+    one = [p for b in singles for p in cpp_pairs(b, [0])]
+    one_bytes = sum(pair_bytes(b) for b in singles)
+    t0 = time.perf_counter()
+    C.attend_pairs(one, g, w.group_size, codebook, 1)
+    one_wall = time.perf_counter() - t0
 
     n = len(workers.conns)
-    reqs = list(range(min(parallel_requests, w.batch)))
-    tasks = [t for b in reqs for t in pair_tasks(b, range(hkv))]
-    assign = [tasks[i::n] for i in range(n)]
-    par_bytes, par_wall, busy = workers.run(assign)
-    single = [t for b in range(min(single_pairs, w.batch)) for t in pair_tasks(b, [0])]
-    one_bytes, one_wall, _ = workers.run([single] + [[] for _ in range(n - 1)])
+    np_reqs = list(range(min(numpy_requests, w.batch)))
+    tasks = [t for b in np_reqs for t in numpy_tasks(b)]
+    np_bytes, np_wall, busy = workers.run([tasks[i::n] for i in range(n)])
     cpu_model, nproc = _host_cpu()
-    return {"value": round(par_bytes / par_wall / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+    return {"value": round(par_bytes / par_wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(par_wall, 3),
-            "sample": f"{len(tasks)} (request, KV head) pairs: requests 0..{reqs[-1]} of {w.batch}, all "
-                      f"{hkv} KV heads, at their final lengths; each pair's history demoted and attended in "
-                      f"float64 by the oracle (numpy), {n} worker processes with one BLAS thread each, "
+            "sample": f"{len(par)} (request, KV head) pairs: requests 0..{reqs[-1]} of {w.batch}, all {hkv} KV "
+                      f"heads, at their final lengths; each pair's history demoted and attended in float64 by "
+                      f"the plain C++ oracle, {threads} OpenMP threads over the pairs, "
                       f"{par_bytes / 1e9:.3f} GB of the step's algorithmic bytes",
-            "worker_busy_s": [round(x, 3) for x in busy],
             "single_thread": {"value": round(one_bytes / one_wall / 1e9, 4), "seconds": round(one_wall, 3),
-                              "sample": f"{len(single)} pairs (KV head 0 of requests 0..{len(single) - 1}), "
-                                        f"one worker, one thread"},
+                              "sample": f"{len(one)} pairs (KV head 0 of requests 0..{singles[-1]}), "
+                                        f"C++ oracle, one thread"},
             "parallel_speedup": round((par_bytes / par_wall) / (one_bytes / one_wall), 2),
+            "numpy_oracle": {"value": round(np_bytes / np_wall / 1e9, 4), "cores": n,
+                             "seconds": round(np_wall, 3),
+                             "sample": f"{len(tasks)} pairs (requests 0..{np_reqs[-1]}, all KV heads), numpy "
+                                       f"oracle, {n} worker processes with one BLAS thread each",
+                             "worker_busy_s": [round(x, 3) for x in busy]},
             "host_cpu": cpu_model, "host_logical_cores": nproc}
 
 
 def cpu_worker_count() -> int:
-    """Worker processes for the oracle baseline: this process's CPU share,
-    at most 16."""
+    """OpenMP threads and worker processes of the oracle baseline: this
+    process's CPU share, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

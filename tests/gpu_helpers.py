@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import cpp as C
 from oracle import oscar as O
 from synth import gen
 
@@ -38,11 +39,13 @@ def request_tokens(model, layout, b: int, L: int):
     return k, v
 
 
-def oracle_request(model, layout, cal, q_bits_b, b: int, L: int, heads=None):
-    """Oracle output [Hq][128] and lse [Hq] of request b at length L."""
+def oracle_request(model, layout, cal, q_bits_b, b: int, L: int, impl: str = "numpy"):
+    """Oracle output [Hq][128] and lse [Hq] of request b at length L, from
+    the numpy oracle or (impl "cpp") the plain C++ oracle."""
     k, v = request_tokens(model, layout, b, L)
-    return O.request_attention(q_bits_b, k, v, cal["r_k32"], cal["r_v32"], cal["clip_k"],
-                               cal["clip_v"], model.w.group_size, CODEBOOK_NAMES[model.w.codebook])
+    fn = C.request_attention if impl == "cpp" else O.request_attention
+    return fn(q_bits_b, k, v, cal["r_k32"], cal["r_v32"], cal["clip_k"], cal["clip_v"], model.w.group_size,
+              CODEBOOK_NAMES[model.w.codebook])
 
 
 def oracle_request_heads(model, layout, cal, q_bits_b, b: int, L: int, kv_heads):

@@ -55,11 +55,11 @@ def setup(w, lens=None, extra=0, stale_byte=None):
     return layout, model, cal, rot, cache
 
 
-def check_all(layout, model, cal, out, lse, q_bits, requests=None, what="", lse_check=True):
+def check_all(layout, model, cal, out, lse, q_bits, requests=None, what="", lse_check=True, impl="numpy"):
     w = model.w
     for b in (range(w.batch) if requests is None else requests):
         L = int(layout.lens[b])
-        ref, ref_lse = oracle_request(model, layout, cal, q_bits[b], b, L)
+        ref, ref_lse = oracle_request(model, layout, cal, q_bits[b], b, L, impl=impl)
         assert_close(out[b], ref, f"{what} b={b} L={L}")
         if lse_check:
             assert np.abs(lse[b] - ref_lse).max() < 2e-3, f"{what} lse b={b}"
@@ -70,7 +70,7 @@ def small(name, seed, hq, hkv, group, lens, paged=True, shared=False, aniso=True
                             shared_prefix=shared, anisotropic_q=aniso, codebook=codebook)
 
 
-def _run_case(w, kind, lens=None, stale_byte=None, target=0):
+def _run_case(w, kind, lens=None, stale_byte=None, target=0, impl="numpy"):
     layout, model, cal, rot, cache = setup(w, lens, stale_byte=stale_byte)
     q_bits = model.queries(0, w.batch)
     q = W.queries_tensor(model, 0, w.batch)
@@ -81,8 +81,17 @@ def _run_case(w, kind, lens=None, stale_byte=None, target=0):
         if e.code == ok.OSCAR_EUNSUPPORTED:
             pytest.skip(f"history kernel {kind} unsupported: {e}")
         raise
-    check_all(layout, model, cal, out, lse, q_bits, what=w.name)
+    check_all(layout, model, cal, out, lse, q_bits, what=w.name, impl=impl)
     return out
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("codebook", [0, 1])
+def test_ragged_batch_against_cpp_oracle(kernel, codebook):
+    """A ragged GQA-4 batch (every region boundary, several pages and a
+    partial last page) against the plain C++ oracle."""
+    lens = [1, 64, 320, 321, 385, 700, 3333, 9001]
+    _run_case(small(f"cpp{codebook}", 95, 16, 4, 64, lens, codebook=codebook), KERNELS[kernel], impl="cpp")
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
