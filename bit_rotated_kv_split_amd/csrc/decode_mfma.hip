@@ -102,11 +102,15 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 before re-basing
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
-// P' digits: x < 2^31 - 2^24, written as four signed base-256 digits (the
-// bytes of x + 0x80808080, each with its top bit flipped)
+// P' digits: x < 2^31 - 2^24.  With y = x + 0x808080 (below 2^31), the
+// bytes of y are x's four signed base-256 digits, the three low ones plus
+// 128 (their top bits flipped once the rows are formed) and the top one as
+// it is.  (The offset is added to the converted integer: added to the float
+// weight it would round away the fraction that the carry keeps.)
 constexpr float kDigitLimit = 2130706432.0f;
+constexpr uint32_t kDigitOffset = 0x808080u;
+constexpr uint32_t kLowDigitFlip = 0x80808080u;
 constexpr float kDigitUnitMax = 2147483648.0f; // the unit puts a page's largest weight at 2^28
-constexpr uint32_t kDigitBias = 0x80808080u;
 // Pages a head's int32 accumulators may take between folds: a page adds at
 // most 64 * 128 * 128 to a digit row (the j = 3 operand bytes reach -128).
 constexpr int kFoldPages = 2047;
@@ -248,22 +252,35 @@ __device__ __forceinline__ v4i load16(const uint8_t* p) {
   else return *reinterpret_cast<const v4i*>(p);
 }
 
+// 16-byte load through a buffer resource: scalar base, per-lane 32-bit
+// offset, so a page costs no vector address arithmetic.  STREAM sets the
+// non-temporal policy bit (aux 2), as load16 does.
+template <bool STREAM>
+__device__ __forceinline__ v4i load16r(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, STREAM ? 2 : 0));
+}
+
+// Raw-buffer resource word 3 for gfx9-family (untyped 32-bit data)
+constexpr int kRsrcWord3 = 0x00020000;
+
 // STREAM_SZ: the scale/zero entries non-temporal too (the kernel decides
-// per instantiation)
+// per instantiation).  blk is wave-uniform; the resource covers exactly the
+// block (a read past it would return 0; none is made).
 template <int G, bool STREAM, bool STREAM_SZ>
 __device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ blk, int lane) {
   constexpr int NG = kDim / G;
-  const int n = lane & 15;
-  r.kw[0] = load16<STREAM>(blk + lane * 16);
-  r.kw[1] = load16<STREAM>(blk + 1024 + lane * 16);
-  r.vw[0] = load16<STREAM>(blk + 2048 + lane * 16);
-  r.vw[1] = load16<STREAM>(blk + 3072 + lane * 16);
-  const uint8_t* ks = blk + kCodesBytes + n * 16 * NG;
-  const uint8_t* vs = blk + kCodesBytes + kPage * NG * 4 + n * 16 * NG;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, block_bytes(G), kRsrcWord3);
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+  const uint32_t so = static_cast<uint32_t>(kCodesBytes) + static_cast<uint32_t>(lane & 15) * (16u * NG);
+  r.kw[0] = load16r<STREAM>(rs, lo, 0);
+  r.kw[1] = load16r<STREAM>(rs, lo, 1024);
+  r.vw[0] = load16r<STREAM>(rs, lo, 2048);
+  r.vw[1] = load16r<STREAM>(rs, lo, 3072);
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    const v4i a = load16<STREAM_SZ>(ks + 16 * i);
-    const v4i b = load16<STREAM_SZ>(vs + 16 * i);
+    const v4i a = load16r<STREAM_SZ>(rs, so, 16 * i);
+    const v4i b = load16r<STREAM_SZ>(rs, so, kPage * NG * 4 + 16 * i);
     r.ksz[4 * i + 0] = a.x; r.ksz[4 * i + 1] = a.y; r.ksz[4 * i + 2] = a.z; r.ksz[4 * i + 3] = a.w;
     r.vsz[4 * i + 0] = b.x; r.vsz[4 * i + 1] = b.y; r.vsz[4 * i + 2] = b.z; r.vsz[4 * i + 3] = b.w;
   }
@@ -482,10 +499,16 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
   }
   // ---- p against the reference max, P' in units of the head's fixed point
   float pr[NHB][4], xv[NHB][NG][4];
-  float dmax = -INFINITY, xmax = 0.f;   // largest score above m, largest P' (this lane)
+  float dmax = 0.f, xmax = 0.f;       // largest score above m, largest P' (this lane)
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    dmax = fmaxf(dmax, fmaxf(fmaxf(sc[hb][0], sc[hb][1]), fmaxf(sc[hb][2], sc[hb][3])) - st.m_ref[hb]);
+    // (IEEE maximum: a score here is a finite product sum or the -inf of a
+    // masked slot, so NaN handling does not matter, and unlike fmaxf it
+    // needs no quieting of its operands)
+    const float d = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[hb][0], sc[hb][1]),
+                                                  __builtin_elementwise_maximum(sc[hb][2], sc[hb][3])) -
+                    st.m_ref[hb];
+    dmax = hb == 0 ? d : fmaxf(dmax, d);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
@@ -496,10 +519,9 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
       }
     }
   }
-  const bool flag = (dmax > kSlack) | (xmax >= kDigitLimit);
   // ---- re-base the heads that need a new reference max or unit (rare),
   // and every head once its int32 accumulators have taken kFoldPages pages
-  const uint64_t mask = __ballot(flag);
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(dmax > kSlack) | __builtin_amdgcn_ballot_w64(xmax >= kDigitLimit);
   const bool force = ++st.since_fold >= kFoldPages;
   if (mask != 0 || force) {
     bool need[NHB];
@@ -535,7 +557,7 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
         // floor with the carried fraction: the lane's rounded weights add up
         // to its exact ones within one unit
         const float t = xv[hb][gi][m] + st.carry[hb][gi];
-        b[m] = static_cast<uint32_t>(t) + kDigitBias;
+        b[m] = static_cast<uint32_t>(t) + kDigitOffset;
         st.carry[hb][gi] = __builtin_amdgcn_fractf(t);
       }
       uint32_t dig[4];
@@ -543,7 +565,8 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
       st.zf[hb][gi] += zpage;
       // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
 #pragma unroll
-      for (int d = 0; d < 4; ++d) sm.pop[slot][hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(dig[d] ^ kDigitBias);
+      for (int d = 0; d < 4; ++d)
+        sm.pop[slot][hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(d < 3 ? dig[d] ^ kLowDigitFlip : dig[d]);
     }
   }
   // every 8 pages the float32 zero-point sums go into the float64 ones
