@@ -240,21 +240,13 @@ struct PageRegs {
   uint32_t vsz[4 * NG];
 };
 
-// 16-byte load; STREAM marks it non-temporal.  A one-wave kernel reads its
-// code words once, and with non-temporal loads HBM streams them faster
-// (32 x 100K, G = 128: 326 -> 283 us; 16 x 128K: 218 -> 190 us).  The
-// two-wave kernels read every page twice, the second wave mostly from
-// cache, and keep ordinary loads (non-temporal: 284 -> 323 us on the ragged
-// GQA-8 batch).
-template <bool STREAM>
-__device__ __forceinline__ v4i load16(const uint8_t* p) {
-  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
-  else return *reinterpret_cast<const v4i*>(p);
-}
-
 // 16-byte load through a buffer resource: scalar base, per-lane 32-bit
 // offset, so a page costs no vector address arithmetic.  STREAM sets the
-// non-temporal policy bit (aux 2), as load16 does.
+// non-temporal policy bit (aux 2).  A one-wave kernel reads its code words
+// once, and with non-temporal loads HBM streams them faster (32 x 100K,
+// G = 128: 326 -> 283 us; 16 x 128K: 218 -> 190 us).  The two-wave kernels
+// read every page twice, the second wave mostly from cache, and keep
+// ordinary loads (non-temporal: 284 -> 323 us on the ragged GQA-8 batch).
 template <bool STREAM>
 __device__ __forceinline__ v4i load16r(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, STREAM ? 2 : 0));
