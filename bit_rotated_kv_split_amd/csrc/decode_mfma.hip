@@ -287,8 +287,8 @@ struct WaveState {
   // (lane groups 2 sub, 2 sub + 1 hold the group's 32 channels)
   v4i qam[NHB][2][2];
   v4i qbm[NHB][2][2];
-  float qs[NHB];           // query fixed-point unit of this lane's head
-  float qz[NHB][NG];       // per-group query sums (zero-point term of the score)
+  float qs[NHB];           // query fixed-point unit of this lane's head (1 for an all-zero query)
+  float qz[NHB][NG];       // per-group query sums / qs (zero-point term of the score / qs)
   float m_ref[NHB];        // reference maximum (log2 units)
   float unit[NHB][NG];     // P' fixed-point unit
   float inv[NHB][NG];      // 4^-j / unit for this lane's token residue j
@@ -397,7 +397,8 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
                                            float lm_hi, float ka, float kb) {
   constexpr int NG = kDim / G;
   const int n = lane & 15, lg = lane >> 4;
-  // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n
+  // ---- q . code: token tau(m, n) = 16 (n/4) + 4 m + n%4 in output column n;
+  // sc holds scores / qs (the head's query unit is applied in the exponent)
   float sc[NHB][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -425,7 +426,7 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
             const float ks = __uint_as_float(sz << 16);
             float kz = __uint_as_float(sz & 0xFFFF0000u);
             if constexpr (LM) kz = __builtin_fmaf(-lm_hi, ks, kz);
-            s += __builtin_fmaf(ks * st.qs[hb], q_digits(d), kz * st.qz[hb][gi]);
+            s += __builtin_fmaf(ks, q_digits(d), kz * st.qz[hb][gi]);
           }
         }
       } else if constexpr (LM) {
@@ -441,7 +442,7 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
           const uint32_t sz = cur.ksz[m];
           const float ks = __uint_as_float(sz << 16);
           const float kz = __builtin_fmaf(-lm_hi, ks, __uint_as_float(sz & 0xFFFF0000u));
-          s = __builtin_fmaf(ks * st.qs[hb], q_digits(d), kz * st.qz[hb][0]);
+          s = __builtin_fmaf(ks, q_digits(d), kz * st.qz[hb][0]);
         } else {
           v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
           v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, st.kc[hb][1], 0, 0, 0);
@@ -451,22 +452,22 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
           const float ks0 = __uint_as_float(s0 << 16), ks1 = __uint_as_float(s1 << 16);
           const float kz0 = __builtin_fmaf(-lm_hi, ks0, __uint_as_float(s0 & 0xFFFF0000u));
           const float kz1 = __builtin_fmaf(-lm_hi, ks1, __uint_as_float(s1 & 0xFFFF0000u));
-          s = __builtin_fmaf(ks0 * st.qs[hb], q_digits(d0), kz0 * st.qz[hb][0]) +
-              __builtin_fmaf(ks1 * st.qs[hb], q_digits(d1), kz1 * st.qz[hb][1]);
+          s = __builtin_fmaf(ks0, q_digits(d0), kz0 * st.qz[hb][0]) +
+              __builtin_fmaf(ks1, q_digits(d1), kz1 * st.qz[hb][1]);
         }
       } else if constexpr (NG == 1) {
         v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, d, 0, 0, 0);
         const uint32_t sz = cur.ksz[m];
-        s = __builtin_fmaf(__uint_as_float(sz << 16) * st.qs[hb], q_digits(d),
+        s = __builtin_fmaf(__uint_as_float(sz << 16), q_digits(d),
                            __uint_as_float(sz & 0xFFFF0000u) * st.qz[hb][0]);
       } else {
         const v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][0], b0, st.kc[hb][0], 0, 0, 0);
         const v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.qa[hb][1], b1, st.kc[hb][1], 0, 0, 0);
         const uint32_t s0 = cur.ksz[m * NG + 0], s1 = cur.ksz[m * NG + 1];
-        s = __builtin_fmaf(__uint_as_float(s0 << 16) * st.qs[hb], q_digits(d0),
+        s = __builtin_fmaf(__uint_as_float(s0 << 16), q_digits(d0),
                            __uint_as_float(s0 & 0xFFFF0000u) * st.qz[hb][0]) +
-            __builtin_fmaf(__uint_as_float(s1 << 16) * st.qs[hb], q_digits(d1),
+            __builtin_fmaf(__uint_as_float(s1 << 16), q_digits(d1),
                            __uint_as_float(s1 & 0xFFFF0000u) * st.qz[hb][1]);
       }
       sc[hb][m] = s;
@@ -497,13 +498,14 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
     // (IEEE maximum: a score here is a finite product sum or the -inf of a
     // masked slot, so NaN handling does not matter, and unlike fmaxf it
     // needs no quieting of its operands)
-    const float d = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[hb][0], sc[hb][1]),
-                                                  __builtin_elementwise_maximum(sc[hb][2], sc[hb][3])) -
-                    st.m_ref[hb];
+    const float d = __builtin_fmaf(st.qs[hb],
+                                   __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[hb][0], sc[hb][1]),
+                                                                 __builtin_elementwise_maximum(sc[hb][2], sc[hb][3])),
+                                   -st.m_ref[hb]);
     dmax = hb == 0 ? d : fmaxf(dmax, d);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);   // 0 for invalid tokens
+      pr[hb][m] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.qs[hb], sc[hb][m], -st.m_ref[hb]));   // 0 past the end
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         xv[hb][gi][m] = pr[hb][m] * __uint_as_float(vsz[m * NG + gi] << 16) * st.inv[hb][gi];
@@ -520,12 +522,17 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) need[hb] = force || ((mask >> (16 * lg)) & 0xFFFFull) != 0;
     if (force) st.since_fold = 0;
-    rebase<LM, NHB, G>(st, sc, vsz, need, sm, lane, ka, kb);
+    float sct[NHB][4];   // the scores themselves
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sct[hb][m] = st.qs[hb] * sc[hb][m];
+    rebase<LM, NHB, G>(st, sct, vsz, need, sm, lane, ka, kb);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        pr[hb][m] = __builtin_amdgcn_exp2f(sc[hb][m] - st.m_ref[hb]);
+        pr[hb][m] = __builtin_amdgcn_exp2f(sct[hb][m] - st.m_ref[hb]);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
           xv[hb][gi][m] = pr[hb][m] * __uint_as_float(vsz[m * NG + gi] << 16) * st.inv[hb][gi];
@@ -729,7 +736,12 @@ hist_mfma_kernel(MfmaParams a) {
     }
     const int h = 4 * (wave + hb) + lg;
     head_ok[hb] = h < a.gq;
-    st.qs[hb] = LM ? qscale[h] * a.lm_ka : qscale[h];
+    {
+      // an all-zero query has unit 0 and zero sums: take 1, so scores / qs
+      // stay 0 and a masked slot's -inf stays -inf
+      const float u = LM ? qscale[h] * a.lm_ka : qscale[h];
+      st.qs[hb] = u > 0.f ? u : 1.f;
+    }
     st.m_ref[hb] = -INFINITY;
     st.ls[hb] = 0.f;
     st.since_fold = 0;
@@ -744,7 +756,7 @@ hist_mfma_kernel(MfmaParams a) {
     }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      st.qz[hb][gi] = head_ok[hb] ? a.qsum[(head0 + h) * 4 + gi] : 0.f;
+      st.qz[hb][gi] = head_ok[hb] ? a.qsum[(head0 + h) * 4 + gi] / st.qs[hb] : 0.f;
       st.unit[hb][gi] = 0.f;
       st.inv[hb][gi] = 0.f;
       sm.zacc[hb * NG + gi][lane] = 0.0;
