@@ -340,6 +340,47 @@ def test_valu_and_mfma_agree(codebook):
     assert_close(b, a, "valu vs mfma", atol=2e-4, rel_l2=2e-5)
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_pages_beyond_4gib(kernel):
+    """Every physical page of the cache sits more than 4.5 GiB into the page
+    pool: page addresses are formed in 64 bits everywhere (bulk fill,
+    demotion, both history kernels; the matrix-core kernel builds a buffer
+    resource at each page's own address).  One decode, then one full step
+    with append and demotion, each against the oracle."""
+    w = small("far", 97, 8, 2, 128, [5000, 2100, 330])
+    layout = W.Layout(w, None, extra_tokens=1)
+    blk = w.num_kv_heads * (4096 + 512 * (128 // w.group_size))
+    off = (9 << 29) // blk + 1
+    layout.page_table = layout.page_table + np.int32(off)
+    layout.n_pages += off
+    model = W.SyntheticModel(w)
+    cal = oracle_calibration(model)
+    rot = Rotation(cal["r_k32"], cal["r_v32"], cal["clip_k"], cal["clip_v"])
+    cache = W.build_cache(w, layout, model, rot)
+    assert cache.pages.numel() * cache.pages.element_size() > (9 << 29)
+    q = W.queries_tensor(model, 0, w.batch)
+    try:
+        out, lse = run_decode(cache, rot, q, int(layout.lens.max()), KERNELS[kernel])
+    except ok.OscarError as e:
+        if e.code == ok.OSCAR_EUNSUPPORTED:
+            pytest.skip(str(e))
+        raise
+    check_all(layout, model, cal, out, lse, model.queries(0, w.batch), what="far pages")
+    lens = layout.lens + 1
+    cache.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    ws = DecodeWorkspace(cache.dims, w.batch, int(lens.max()))
+    out_t = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+    kn = W.new_tokens_tensor(model, layout, lens, "k")
+    vn = W.new_tokens_tensor(model, layout, lens, "v")
+    opts = ok.make_options(history_kernel=KERNELS[kernel])
+    ok.oscar_decode_step(cache.dims, rot.struct, cache.struct(), kn, vn, W.queries_tensor(model, 1, w.batch),
+                         ws.max_seq_len, ws.buf, ws.nbytes, out_t, None, options=opts)
+    torch.cuda.synchronize()
+    layout.lens = lens
+    check_all(layout, model, cal, out_t.cpu().numpy(), None, model.queries(1, w.batch), what="far pages step",
+              lse_check=False)
+
+
 def test_full_step_sequence_matches_oracle():
     """Decode steps with append + demotion (the bench's step) from L = 2000,
     checked against the oracle after several steps."""
