@@ -22,8 +22,10 @@ Order of one run:
      compared against, and they leave the GPU at its steady clocks, so the
      timed steps do not measure the clock ramp that follows the idle setup;
   3. `warmup` untimed steps, then exactly `steps` timed steps between one
-     pair of events: `value` and `ms_per_step`; each history launch between
-     its own events (`roofline`, per-quarter means, shader clock); then
+     pair of events: `value` and `ms_per_step`; every 4th of their history
+     launches (`--launch-event-every`) between its own events (`roofline`,
+     per-quarter means; an event pair adds about 4 us to its step, so not
+     every step carries one), and the shader clock over every launch; then
      `steps` more steps with an event between consecutive steps for the
      per-step latency (`step_us_p50`, `step_us_p99`);
   4. `cold_start`: after 1 s with the GPU idle, 20 more timed steps with no
@@ -391,6 +393,9 @@ def main() -> int:
                     help="independent layer caches cycled one per step (0: 10 for b1-100k, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold-start", action="store_true", help="skip the idle-start diagnostic leg")
+    ap.add_argument("--launch-event-every", type=int, default=4,
+                    help="time every n-th history launch of the timed steps between its own HIP events "
+                         "(an event pair adds about 4 us to its step; 1 = every launch)")
     ap.add_argument("--bf16-baseline", choices=["auto", "on", "off"], default="auto",
                     help="also time the all-bf16 cache decode step (auto: on for the 32 x 100K workloads)")
     ap.add_argument("--history-target", type=int, default=0,
@@ -475,19 +480,25 @@ def main() -> int:
 
     wall_khz = ok.wall_clock_khz()
 
-    def timed_run(one_step, first: int, n_warm: int, n_timed: int, marks_per_step: bool = False):
+    def timed_run(one_step, first: int, n_warm: int, n_timed: int, marks_per_step: bool = False,
+                  event_every: int = 1):
         """Steps first .. first+n_warm-1 untimed, then n_timed steps timed
-        between one pair of events on the stream, each history launch between
-        its own start/stop events (hipExtLaunchKernelGGL), with the shader
-        clock over the launch's first workgroup.  With marks_per_step an
-        event is also recorded between consecutive steps (per-step times,
-        at a few µs of extra cost per step).  Returns (total µs, per-step µs
-        or None, per-launch µs, per-launch MHz)."""
+        between one pair of events on the stream.  Timed step i's history
+        launch runs between its own start/stop events (hipExtLaunchKernelGGL)
+        when event_every > 0 and i % event_every == 0 (an event pair adds
+        about 4 µs to its step, so the headline steps time only a sample of
+        launches), and every launch records the shader clock over its first
+        workgroup (free).  With marks_per_step an event is also recorded
+        between consecutive steps (per-step times, at a few µs of extra cost
+        per step).  Returns (total µs, per-step µs or None, the timed
+        launches' indices and µs, per-launch MHz of every timed launch)."""
         ev_b = [HipEvent() for _ in range(n_timed)]
         ev_a = [HipEvent() for _ in range(n_timed)]
         marks = [HipEvent() for _ in range(n_timed + 1)]
         clk = torch.zeros((n_timed, 4), dtype=torch.int64, device="cuda")
+        timed = [i for i in range(n_timed) if event_every > 0 and i % event_every == 0]
         opts = [ok.make_options(kind, args.history_target, ev_b[i], ev_a[i], clk.data_ptr() + 32 * i)
+                if i in timed else ok.make_options(kind, args.history_target, None, None, clk.data_ptr() + 32 * i)
                 for i in range(n_timed)]
         for s in range(n_warm):
             one_step(first + s, base_opts)
@@ -502,10 +513,10 @@ def main() -> int:
         torch.cuda.synchronize()
         total_us = 1e3 * marks[0].elapsed_ms(marks[n_timed])
         step_us = [1e3 * marks[i].elapsed_ms(marks[i + 1]) for i in range(n_timed)] if marks_per_step else None
-        hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in range(n_timed)]
+        hist_us = [1e3 * ev_b[i].elapsed_ms(ev_a[i]) for i in timed]
         c = clk.cpu().numpy().astype(np.float64)
         mhz = ((c[:, 2] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 1], 1) * wall_khz / 1e3).tolist()
-        return total_us, step_us, hist_us, mhz
+        return total_us, step_us, (timed, hist_us), mhz
 
     def int2_step(s: int, opts):
         t = s // n_layers
@@ -516,20 +527,23 @@ def main() -> int:
           f"{int(layout.lens.max())} layers={n_layers} slots={ws.splits} calib {calib_s:.1f}s fill {fill_s:.1f}s",
           file=sys.stderr, flush=True)
     probes = bandwidth_probes(ok, torch, HipEvent, stream)
-    total_us, _, k3_us, k3_mhz = timed_run(int2_step, 0, warmup, steps)
+    every = max(1, args.launch_event_every)
+    total_us, _, (k3_idx, k3_us), k3_mhz = timed_run(int2_step, 0, warmup, steps, event_every=every)
     step_ms = total_us / steps / 1e3
     # per-step latency: the next `steps` steps with an event between steps
-    _, step_us, _, _ = timed_run(int2_step, warmup + steps, 0, steps, marks_per_step=True)
+    # (and none around the history launches)
+    _, step_us, _, _ = timed_run(int2_step, warmup + steps, 0, steps, marks_per_step=True, event_every=0)
 
     kname = "mfma" if ok.oscar_history_kernel_for(dims, base_opts) == 2 else "valu"
     shared_tok = PAGE * (sum(layout.shared_pages) - layout.chain_len) if layout.chain_len else 0
 
-    def byte_totals(first: int, n: int):
+    def byte_totals(first: int, n: int, only=None):
         """(history launch bytes, step bytes, unique step bytes) summed over
-        steps first .. first+n-1: the launch holds the history splits, plus
-        the bf16 sink/recent chunks when the matrix-core kernel runs them."""
+        steps first .. first+n-1 (or first + i for i in `only`): the launch
+        holds the history splits, plus the bf16 sink/recent chunks when the
+        matrix-core kernel runs them."""
         launch = stp = uniq = 0
-        for i in range(n):
+        for i in (range(n) if only is None else only):
             lens_i = lens_step[first + i]
             hb, sb = step_bytes(lens_i, hkv, hq, w.group_size)
             launch += hb + (bf16_bytes(lens_i, hkv) if kname == "mfma" else 0)
@@ -537,8 +551,10 @@ def main() -> int:
             uniq += sb - shared_tok * hkv * hist_unit_bytes(w.group_size)
         return launch, stp, uniq
 
-    launch_tot, step_tot, unique_tot = byte_totals(warmup, steps)
+    _, step_tot, unique_tot = byte_totals(warmup, steps)
+    launch_tot, _, _ = byte_totals(warmup, steps, only=k3_idx)     # the launches timed by events
     k3_gbs = launch_tot / (sum(k3_us) * 1e-6) / 1e9
+    k3_avg = sum(k3_us) / len(k3_us)
     value = step_tot / (total_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload, kname)
 
@@ -548,7 +564,7 @@ def main() -> int:
         torch.cuda.synchronize()
         time.sleep(COLD_IDLE_S)
         c_first = warmup + 2 * steps
-        _, c_step, c_k3, c_mhz = timed_run(int2_step, c_first, 0, n_cold, marks_per_step=True)
+        _, c_step, (_, c_k3), c_mhz = timed_run(int2_step, c_first, 0, n_cold, marks_per_step=True)
         trace.update(cold_step_us=c_step, cold_history_us=c_k3, cold_history_mhz=c_mhz)
         c_launch, c_stp, _ = byte_totals(c_first, n_cold)
         c_k3_gbs = c_launch / (sum(c_k3) * 1e-6) / 1e9
@@ -567,7 +583,7 @@ def main() -> int:
                              n_layers, stream, dims, hkv, hq, warmup, steps, args.history_target)
         if base is not None:
             base["int2_step_speedup"] = round(base["us_per_step"] / (step_ms * 1e3), 3)
-            base["int2_history_speedup"] = round(base["history_us"] / (sum(k3_us) / steps), 3)
+            base["int2_history_speedup"] = round(base["history_us"] / k3_avg, 3)
             base["byte_ratio"] = round(base["bytes_per_step"] / (step_tot / steps), 3)
 
     cpu = None
@@ -610,15 +626,18 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(k3_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(k3_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": f"history ({kname})" + (" + bf16 sink/recent" if kname == "mfma" else ""),
-                     "avg_us": round(sum(k3_us) / steps, 2),
-                     "bytes_per_launch": int(launch_tot / steps),
+                     "avg_us": round(k3_avg, 2),
+                     "bytes_per_launch": int(launch_tot / len(k3_us)),
+                     "launches_timed": {"every": every, "count": len(k3_us),
+                                        "what": "history launches of the timed steps that ran between their "
+                                                "own HIP start/stop events on the launch stream"},
                      "read_ceiling_gbs": probes["read_ceiling_gbs"],
                      "frac_of_read_ceiling": round(k3_gbs / probes["read_ceiling_gbs"], 4),
                      "unit_bytes": {"history_token_head": hist_unit_bytes(w.group_size),
                                     "bf16_token_head": 512}},
         "quarters": {"history_us": quarters(k3_us), "history_mhz": quarters(k3_mhz),
                      "min_history_mhz": round(min(k3_mhz), 1)},
-        "step_vs_history": round((total_us / steps) / (sum(k3_us) / steps), 4),
+        "step_vs_history": round((total_us / steps) / k3_avg, 4),
         "probes": probes,
         "cold_start": cold,
         "cpu_baseline": cpu,
