@@ -396,6 +396,7 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool mfma = use_mfma(*dims, opt);
   DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
+  a.max_seq_len = max_seq_len;
   DemoteStep dm;
   if (demote) {
     dm = make_demote_step(*dims, *rot, *cache, k_new, v_new);

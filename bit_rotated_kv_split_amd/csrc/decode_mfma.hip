@@ -906,9 +906,27 @@ hist_mfma_kernel(MfmaParams a) {
 // uniform G = 64 / 128 kernels keep two buffers at two waves per SIMD (with
 // the loop's single exit, a third buffer or a third wave measured 1-2 %
 // slower); the Lloyd-Max kernels keep three.
+// The most history splits this call's schedule can produce: at most
+// max(target, batch) (the schedule's rule), and at most ceil(pages /
+// kMinSplitPages) per request, every request holding at most max_seq_len
+// tokens.  The launch has that many history workgroup slots per KV head:
+// workgroups past the scheduled count exit at once, but at 1 x 100K the
+// workspace's slots launched twice as many, which cost the launch 1.5 us
+// (22.0-22.3 against 20.3-20.4 us).
+int hist_max_splits(const DecodeArgs& a) {
+  const long long pages = (std::max(0, a.max_seq_len - kBf16Tokens) + kPage - 1) / kPage;
+  const long long per_req = (pages + kMinSplitPages - 1) / kMinSplitPages;
+  const long long batch = a.cache->batch;
+  const long long n = std::min(std::max<long long>(a.lay.target, batch), per_req * batch);
+  return static_cast<int>(std::max(1LL, std::min<long long>(n, a.lay.slots)));
+}
+
 template <int G, int WAVES, bool LM>
 struct HistShape {
-  static constexpr bool kThreeWaves = G == 128 && WAVES == 2 && !LM;
+  // G = 128 uniform kernels fit three waves per SIMD (168 VGPRs, no spills):
+  // GQA-8 about 7 % faster than at two; GQA <= 4 about 0.6 % (32 x 100K:
+  // 279.8-280.9 against 281.7-282.4 us, same box)
+  static constexpr bool kThreeWaves = G == 128 && !LM;
   static constexpr int BUF = G == 32 ? (LM ? 1 : OSCAR_HIST_BUFFERS_32) : kThreeWaves ? 2
                                      : (LM ? OSCAR_HIST_BUFFERS_LM : OSCAR_HIST_BUFFERS);
   static constexpr int MINW = kThreeWaves ? 3 : (LM ? OSCAR_HIST_MIN_WAVES_LM : OSCAR_HIST_MIN_WAVES);
@@ -932,14 +950,14 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.hkv = d.num_kv_heads;
   p.hq = d.num_q_heads;
   p.gq = d.num_q_heads / d.num_kv_heads;
-  p.slots = a.lay.slots;
+  p.slots = hist_max_splits(a);
   const Codebook* cbk = codebook_of(d.codebook);
   p.lm_hi = cbk->lev[3];
   p.lm_ka = cbk->lev[3] - cbk->lev[2];
   p.lm_kb = (3.f * cbk->lev[2] - cbk->lev[3]) * 0.5f;
   p.bf = make_bf16_params(a);
   p.clk = a.clock_trace;
-  const dim3 grid((a.lay.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
+  const dim3 grid((p.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
   const dim3 block(64 * WAVES);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
     hipExtLaunchKernelGGL(hist_mfma_kernel<G, WAVES, BUF, MINW, LM>, grid, block, 0, s, a.ev_start, a.ev_stop, 0,

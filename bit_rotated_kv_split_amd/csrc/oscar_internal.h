@@ -121,6 +121,7 @@ struct DecodeArgs {
   unsigned long long* clock_trace = nullptr;   // when set, the history kernel's first
                                                // workgroup records its clock counters
   const DemoteStep* demote = nullptr;   // when set, the prologue launch also demotes
+  int32_t max_seq_len = 0;              // >= every request's length (bounds the splits launched)
 };
 
 hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);

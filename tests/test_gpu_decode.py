@@ -631,8 +631,9 @@ def test_default_target_follows_the_device():
     kernel for the dims, over the waves per workgroup."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     simds = 4 * cus
-    cases = [(ok.make_dims(32, 8, 128), simds * 2), (ok.make_dims(64, 8, 128), simds * 3 // 2),
-             (ok.make_dims(64, 8, 64), simds * 2 // 2)]
+    cases = [(ok.make_dims(32, 8, 128), simds * 3), (ok.make_dims(64, 8, 128), simds * 3 // 2),
+             (ok.make_dims(64, 8, 64), simds * 2 // 2), (ok.make_dims(32, 8, 64), simds * 2),
+             (ok.make_dims(32, 8, 128, codebook=ok.CODEBOOK_LLOYD_MAX), simds * 2)]
     for d, wgs in cases:
         assert ok.oscar_history_splits(d, 32, 100_000) == -(-min(wgs, 8192) // 8) + 32, (d.num_q_heads, wgs)
 
