@@ -900,12 +900,6 @@ hist_mfma_kernel(MfmaParams a) {
   }
 }
 
-// Register page buffers and waves per SIMD of each instantiation.  The
-// two-wave (GQA-8) G = 128 uniform kernel fits three waves per SIMD with two
-// buffers (168 VGPRs, no spills) and runs about 7 % faster that way; the
-// uniform G = 64 / 128 kernels keep two buffers at two waves per SIMD (with
-// the loop's single exit, a third buffer or a third wave measured 1-2 %
-// slower); the Lloyd-Max kernels keep three.
 // The most history splits this call's schedule can produce: at most
 // max(target, batch) (the schedule's rule), and at most ceil(pages /
 // kMinSplitPages) per request, every request holding at most max_seq_len
@@ -921,6 +915,12 @@ int hist_max_splits(const DecodeArgs& a) {
   return static_cast<int>(std::max(1LL, std::min<long long>(n, a.lay.slots)));
 }
 
+// Register page buffers and waves per SIMD of each instantiation: the
+// G = 128 uniform kernels run three waves per SIMD with two buffers; the
+// other uniform kernels keep two buffers at two waves per SIMD (a third
+// buffer measured 1-2 % slower, and G = 64 fits a third wave only with one
+// buffer, 3 % slower); the Lloyd-Max kernels keep two buffers (one at
+// G = 32, where two spill) at two waves.
 template <int G, int WAVES, bool LM>
 struct HistShape {
   // G = 128 uniform kernels fit three waves per SIMD (168 VGPRs, no spills):
