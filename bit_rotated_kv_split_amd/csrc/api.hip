@@ -204,6 +204,17 @@ int scratch_address(void** out) {
 
 }  // namespace
 
+void history_launch_slots(const WsLayout& lay, int32_t batch, int32_t max_seq_len, int32_t* slots,
+                          int32_t* sched_target) {
+  const long long pages = pages_for(max_seq_len);
+  const long long per_req = (pages + kMinSplitPages - 1) / kMinSplitPages;
+  const long long b = batch;
+  const long long t = lay.target;
+  const long long n = std::max(b, std::min(std::max(t, b), per_req * b));
+  *slots = static_cast<int32_t>(std::min<long long>(n, lay.slots));
+  *sched_target = static_cast<int32_t>(std::min(t, n));
+}
+
 WsLayout workspace_layout(const oscar_dims& d, int32_t batch, int32_t max_seq_len, int target_wg) {
   (void)max_seq_len;
   WsLayout w;
@@ -396,7 +407,7 @@ int decode_impl(const oscar_dims* dims, const oscar_rotation* rot, const oscar_c
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool mfma = use_mfma(*dims, opt);
   DecodeArgs a{dims, rot, cache, q, static_cast<uint8_t*>(workspace), lay};
-  a.max_seq_len = max_seq_len;
+  history_launch_slots(lay, cache->batch, max_seq_len, &a.hist_slots, &a.sched_target);
   DemoteStep dm;
   if (demote) {
     dm = make_demote_step(*dims, *rot, *cache, k_new, v_new);

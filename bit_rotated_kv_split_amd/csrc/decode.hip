@@ -727,7 +727,7 @@ struct QrotRun {
     qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),
-        a.ws + a.lay.off_qpack, a.cache->seq_lens, batch, a.lay.target,
+        a.ws + a.lay.off_qpack, a.cache->seq_lens, batch, a.sched_target > 0 ? a.sched_target : a.lay.target,
         reinterpret_cast<int32_t*>(a.ws + a.lay.off_sched), reinterpret_cast<int32_t*>(a.ws + a.lay.off_req),
         lm_ratio(d), a.demote != nullptr ? *a.demote : DemoteStep{});
     return hipGetLastError();

@@ -900,21 +900,6 @@ hist_mfma_kernel(MfmaParams a) {
   }
 }
 
-// The most history splits this call's schedule can produce: at most
-// max(target, batch) (the schedule's rule), and at most ceil(pages /
-// kMinSplitPages) per request, every request holding at most max_seq_len
-// tokens.  The launch has that many history workgroup slots per KV head:
-// workgroups past the scheduled count exit at once, but at 1 x 100K the
-// workspace's slots launched twice as many, which cost the launch 1.5 us
-// (22.0-22.3 against 20.3-20.4 us).
-int hist_max_splits(const DecodeArgs& a) {
-  const long long pages = (std::max(0, a.max_seq_len - kBf16Tokens) + kPage - 1) / kPage;
-  const long long per_req = (pages + kMinSplitPages - 1) / kMinSplitPages;
-  const long long batch = a.cache->batch;
-  const long long n = std::min(std::max<long long>(a.lay.target, batch), per_req * batch);
-  return static_cast<int>(std::max(1LL, std::min<long long>(n, a.lay.slots)));
-}
-
 // Register page buffers and waves per SIMD of each instantiation: the
 // G = 128 uniform kernels run three waves per SIMD with two buffers; the
 // other uniform kernels keep two buffers at two waves per SIMD (a third
@@ -950,7 +935,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.hkv = d.num_kv_heads;
   p.hq = d.num_q_heads;
   p.gq = d.num_q_heads / d.num_kv_heads;
-  p.slots = hist_max_splits(a);
+  p.slots = a.hist_slots > 0 ? a.hist_slots : a.lay.slots;
   const Codebook* cbk = codebook_of(d.codebook);
   p.lm_hi = cbk->lev[3];
   p.lm_ka = cbk->lev[3] - cbk->lev[2];

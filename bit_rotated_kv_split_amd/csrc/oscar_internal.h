@@ -121,8 +121,25 @@ struct DecodeArgs {
   unsigned long long* clock_trace = nullptr;   // when set, the history kernel's first
                                                // workgroup records its clock counters
   const DemoteStep* demote = nullptr;   // when set, the prologue launch also demotes
-  int32_t max_seq_len = 0;              // >= every request's length (bounds the splits launched)
+  // History split slots per KV head the matrix-core launch holds, and the
+  // target the call's split schedule aims for (history_launch_slots).
+  int32_t hist_slots = 0;
+  int32_t sched_target = 0;
 };
+
+// The history split slots (per KV head) a decode call launches, and the
+// schedule target that keeps the schedule inside them.  The schedule makes
+// at most max(target, batch) splits, and at most ceil(pages / kMinSplitPages)
+// per request, pages from max_seq_len (the API requires max_seq_len >= every
+// length).  The launch holds n = max(batch, min(max(t, batch),
+// batch * ceil(pages / kMinSplitPages))) slots, t the layout's target; the
+// schedule aims for min(t, n), which gives the same schedule as t whenever
+// the lengths respect max_seq_len, and at most n splits even when they do
+// not.  (The workspace's t + batch slots, launched whole, made a 1 x 100K
+// launch dispatch about twice the workgroups that had work, which cost it
+// 1.5 us.)
+void history_launch_slots(const WsLayout& lay, int32_t batch, int32_t max_seq_len, int32_t* slots,
+                          int32_t* sched_target);
 
 hipError_t launch_qrot(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_hist_valu(const DecodeArgs& a, hipStream_t s);
