@@ -617,6 +617,175 @@ __device__ __forceinline__ void value_page(WaveState<NHB, G>& st, const PageRegs
   }
 }
 
+// ---- bf16 sink/recent chunk on the matrix core ---------------------------
+//
+// One 64-slot chunk of the bf16 sink or recent tokens for query heads
+// h_lo .. h_lo + nh - 1 (nh <= 4) of KV head kvh, request b, by one wave
+// (page "超越TurboQuant：Together AI把2-bit KV Cache推向真实服务", section
+// "OSCAR的另一个关键点是": sink and recent stay bf16 and meet the unrotated
+// query).  The output is the chunk's normalised partial (natural-log LSE),
+// the same as the vector-ALU chunk writes.
+//   q . k on v_mfma_f32_16x16x32_bf16: rows = tokens (16 per block, four
+//          blocks), columns = heads (four of 16 used), the K dimension =
+//          channels; a lane's A operand is 16 contiguous bytes of one key
+//          row, read straight from memory, and its B operand 16 bytes of
+//          the query.  Products of bf16 values are exact in fp32.
+//   p . v on the vector ALU: lane = (8-channel group, token residue mod 4),
+//          16-byte loads along each value row, reduced over the residues.
+// Every key load is issued at once (64 VGPRs), and the value rows two
+// quarters ahead of their use, so the chunk waits on memory about twice
+// instead of once per quarter row.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct Bf16MfmaSmem {
+  float p[4][kPage];   // softmax numerators, [head][token]
+};
+
+__device__ __forceinline__ void bf16_chunk_mfma(const Bf16Params& a, int gq, int h_lo, int chunk, int kvh, int b,
+                                                Bf16MfmaSmem& sm) {
+  const int lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
+  const int nh = min(4, gq - h_lo);
+  const int L = a.seq_lens[b];
+  const int n_sink = min(L, kSink);
+  const int n_recent = min(max(L - kSink, 0), kRecent);
+  const int n_valid = chunk == 0 ? n_sink : min(max(n_recent - (chunk - 1) * kPage, 0), kPage);
+  const size_t head0 = static_cast<size_t>(b) * a.hq + static_cast<size_t>(kvh) * gq + h_lo;
+  if (n_valid == 0) {   // uniform across the wave
+    for (int i = lane; i < nh * kDim; i += 64)
+      a.po[((head0 + i / kDim) * kBf16Parts + chunk) * kDim + i % kDim] = 0.f;
+    if (lane < nh) a.plse[(head0 + lane) * kBf16Parts + chunk] = -INFINITY;
+    return;
+  }
+  const size_t kv0 = static_cast<size_t>(b) * a.hkv + kvh;
+  const uint16_t* kb = chunk == 0 ? a.sink_k + kv0 * kSink * kDim
+                                  : a.recent_k + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  const uint16_t* vb = chunk == 0 ? a.sink_v + kv0 * kSink * kDim
+                                  : a.recent_v + (kv0 * kRecent + (chunk - 1) * kPage) * kDim;
+  // Loads through buffer resources that cover only the valid rows: a read
+  // of a slot past n_valid (or of a head past nh) returns zeros, so those
+  // slots need no address clamping, and stale bytes there (NaN or Inf
+  // included) never reach the products.  Every offset goes in the
+  // per-lane operand (with any constant part the compiler folds into the
+  // instruction's offset field), which the range check covers; the scalar
+  // offset operand is not checked and stays 0.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kb), 0, n_valid * kDim * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vb), 0, n_valid * kDim * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.q + head0 * kDim), 0, nh * kDim * 2, kRsrcWord3);
+  // A operands: token 16 tb + n, channels 32 ks + 8 lg .. + 7; B operands:
+  // head n, the same channels
+  const uint32_t koff = static_cast<uint32_t>(n) * (kDim * 2) + static_cast<uint32_t>(lg) * 16u;
+  v4i kr[4][4], qb[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kr[tb][ks] = load16r<false>(krs, koff + tb * 16 * kDim * 2 + ks * 64, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qb[ks] = load16r<false>(qrs, koff + ks * 64, 0);
+  // d[tb][i] = q_n . k_t for token t = 16 tb + 4 lg + i
+  v4f d[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    d[tb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      d[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kr[tb][ks]),
+                                                      __builtin_bit_cast(v8bf, qb[ks]), d[tb], 0, 0, 0);
+  }
+  // value rows: quarter jq holds tokens res + 4 (4 jq + i), i = 0..3,
+  // channels 8 cg .. 8 cg + 7; the first two quarters are requested before
+  // the softmax, each later one while the quarter two before it is summed
+  const int cg = lane & 15, res = lane >> 4;
+  const uint32_t voff = static_cast<uint32_t>(res) * (kDim * 2) + static_cast<uint32_t>(cg) * 16u;
+  auto load_quarter = [&](v4i (&vq)[4], int jq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vq[i] = load16r<false>(vrs, voff + (4 * jq + i) * 4 * kDim * 2, 0);
+  };
+  v4i va[4], vb4[4];
+  load_quarter(va, 0);
+  load_quarter(vb4, 1);
+  // softmax per head over the 64 slots: head n's scores sit in lanes n,
+  // n + 16, n + 32, n + 48 (16 each)
+  float s[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * lg + i;
+      s[tb][i] = t < n_valid ? d[tb][i] * kScoreScaleLog2 : -INFINITY;
+      mx = fmaxf(mx, s[tb][i]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));   // finite: slot 0 holds a token
+  float ls = 0.f;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    float4 pv;
+    pv.x = exp2f(s[tb][0] - mx);   // 0 for masked slots
+    pv.y = exp2f(s[tb][1] - mx);
+    pv.z = exp2f(s[tb][2] - mx);
+    pv.w = exp2f(s[tb][3] - mx);
+    ls += (pv.x + pv.y) + (pv.z + pv.w);
+    if (n < 4) *reinterpret_cast<float4*>(&sm.p[n][16 * tb + 4 * lg]) = pv;
+  }
+  ls += __shfl_xor(ls, 16, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float acc[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  auto sum_quarter = [&](const v4i (&vq)[4], int jq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = res + 4 * (4 * jq + i);
+      const uint32_t ws[4] = {static_cast<uint32_t>(vq[i].x), static_cast<uint32_t>(vq[i].y),
+                              static_cast<uint32_t>(vq[i].z), static_cast<uint32_t>(vq[i].w)};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float pt = sm.p[h][t];   // 0 past n_valid
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[h][2 * e] = __builtin_fmaf(pt, __uint_as_float(ws[e] << 16), acc[h][2 * e]);
+          acc[h][2 * e + 1] = __builtin_fmaf(pt, __uint_as_float(ws[e] & 0xFFFF0000u), acc[h][2 * e + 1]);
+        }
+      }
+    }
+  };
+  // (a loop, not unrolled: fully unrolled, the scheduler holds every value
+  // word and numerator at once and exceeds the history kernel's budget)
+#pragma unroll 1
+  for (int jp = 0; jp < 2; ++jp) {   // uniform
+    sum_quarter(va, 2 * jp);
+    if (jp == 0) load_quarter(va, 2);
+    sum_quarter(vb4, 2 * jp + 1);
+    if (jp == 0) load_quarter(vb4, 3);
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    // head h's max and sum live in lane h
+    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h));
+    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), h));
+    const float inv = 1.f / lh;
+    const size_t pidx = (head0 + h) * kBf16Parts + chunk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (res == 0 && h < nh) a.po[pidx * kDim + cg * 8 + e] = v * inv;
+    }
+    if (lane == 0 && h < nh) a.plse[pidx] = (mh + log2f(lh)) * kLn2;
+  }
+}
+
 // Orders one page's P' row writes before the reads that follow (a wave
 // reads rows other lanes wrote).
 __device__ __forceinline__ void wave_lds_fence() {
@@ -657,13 +826,13 @@ hist_mfma_kernel(MfmaParams a) {
   const int lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
   union Smem {
     HistSmem<NHB, NG> hist[WAVES];
-    Bf16Smem<4> bf[WAVES];
+    Bf16MfmaSmem bf[WAVES];
   };
   __shared__ Smem smem;
   if (id >= n_hist_wg) {   // a bf16 sink/recent chunk, four heads per wave
     const int r = id - n_hist_wg;
-    bf16_chunk<4>(a.bf, a.gq, 4 * wave, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv),
-                  smem.bf[wave]);
+    bf16_chunk_mfma(a.bf, a.gq, 4 * wave, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv),
+                    smem.bf[wave]);
     return;
   }
   const int split = id / a.hkv, kvh = id % a.hkv;
