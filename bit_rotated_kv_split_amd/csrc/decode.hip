@@ -362,7 +362,9 @@ __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
   bf16_chunk<GQ>(a, GQ, 0, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
-// LSE merge, two launch shapes.  merge_head_kernel: workgroup = (query
+// LSE merge, two launch shapes.  The partial log-sum-exps are natural logs;
+// every weight e^(l - max) (argument <= 0) is taken as 2^((l - max) log2 e)
+// on the hardware exponential.  merge_head_kernel: workgroup = (query
 // head, request), for batches too small to fill the chip by KV head;
 // merge_group_kernel: workgroup = (KV head, request), sharing R_V across the
 // group's heads.
@@ -424,14 +426,19 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
   const size_t bh = static_cast<size_t>(b) * a.hq + head;
   // the log-sum-exps first: the weights need only these
-  const float l = tid < count ? a.hlse[static_cast<size_t>(first + tid) * a.hq + head] : -INFINITY;
+  // (loads unconditional with clamped indices, values selected afterwards:
+  // a conditional load becomes a branch whose wait serialises the loads)
+  const int last_sp = max(count - 1, 0);
+  const size_t slot0 = count > 0 ? static_cast<size_t>(first) : 0;
+  const float l_raw = a.hlse[(slot0 + min(tid, last_sp)) * a.hq + head];
+  const float l = tid < count ? l_raw : -INFINITY;
   float lb[kBf16Parts];
 #pragma unroll
   for (int c = 0; c < kBf16Parts; ++c) lb[c] = a.blse[bh * kBf16Parts + c];
   // threads 0..255: row i of R_V, columns 64 kh .. 64 kh + 63
   const int i = (tid >> 1) & (kDim - 1), kh = tid & 1;
   float4 rr[16];
-  if (tid < 2 * kDim) {
+  {
     const float4* rrow =
         reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
 #pragma unroll
@@ -441,21 +448,24 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   // to par modulo kPar) and its bf16 partials are requested now, before the
   // weights are known, so the kernel waits on memory once
   const int k = tid & (kDim - 1), par = tid / kDim;
-  const float* hp = a.ho + (static_cast<size_t>(first) * a.hq + head) * kDim + k;
+  const float* hp = a.ho + (slot0 * a.hq + head) * kDim + k;
   const size_t stride = static_cast<size_t>(a.hq) * kDim;
   float v[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int sp = par + kPar * u;
-    v[u] = sp < count ? hp[static_cast<size_t>(sp) * stride] : 0.f;
+    const float x = hp[static_cast<size_t>(min(sp, last_sp)) * stride];
+    v[u] = sp < count ? x : 0.f;
   }
   float vb[kBf16Parts];
 #pragma unroll
-  for (int c = 0; c < kBf16Parts; ++c)
-    vb[c] = tid < 2 * kDim && kh == 0 ? a.bo[(bh * kBf16Parts + c) * kDim + i] : 0.f;
+  for (int c = 0; c < kBf16Parts; ++c) {
+    const float x = a.bo[(bh * kBf16Parts + c) * kDim + i];
+    vb[c] = tid < 2 * kDim && kh == 0 ? x : 0.f;
+  }
   // history split weights e^{lse - M} / sum (count <= kMaxSplits < threads)
   const float mh = bmax(l);
-  const float e = mh == -INFINITY || tid >= count ? 0.f : expf(l - mh);
+  const float e = mh == -INFINITY || tid >= count ? 0.f : __builtin_amdgcn_exp2f((l - mh) * kLog2e);
   const float dh = bsum(e);
   if (tid < count) w[tid] = dh > 0.f ? e / dh : 0.f;
   const float lse_h = dh > 0.f ? mh + logf(dh) : -INFINITY;
@@ -465,7 +475,8 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   for (int c = 0; c < kBf16Parts; ++c) mb = fmaxf(mb, lb[c]);
   float db = 0.f;
 #pragma unroll
-  for (int c = 0; c < kBf16Parts; ++c) db += lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb);
+  for (int c = 0; c < kBf16Parts; ++c)
+    db += lb[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lb[c] - mb) * kLog2e);
   const float lse_b = mb + logf(db);   // the sink chunk always holds a token
   __syncthreads();
   // weighted sum over the splits, in ascending split order
@@ -502,11 +513,12 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
     float ob = 0.f;
 #pragma unroll
     for (int c = 0; c < kBf16Parts; ++c) {
-      const float wc = lb[c] == -INFINITY ? 0.f : expf(lb[c] - mb) / db;
+      const float wc = lb[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lb[c] - mb) * kLog2e) / db;
       ob = __builtin_fmaf(wc, vb[c], ob);
     }
     const float mx = fmaxf(lse_h, lse_b);
-    const float eh = lse_h == -INFINITY ? 0.f : expf(lse_h - mx), eb = expf(lse_b - mx);
+    const float eh = lse_h == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lse_h - mx) * kLog2e);
+    const float eb = __builtin_amdgcn_exp2f((lse_b - mx) * kLog2e);
     const float den = eh + eb;
     a.out[bh * kDim + i] = (eh * xh + eb * ob) / den;
     if (a.lse_out != nullptr && i == 0) a.lse_out[bh] = mx + logf(den);
@@ -549,23 +561,43 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const size_t hstride = static_cast<size_t>(a.hq) * kDim;
   constexpr int kLocalItems = kItems <= 2 ? kItems : 1;
   float vh[kItems][kEarly], vb[kItems][kBf16Parts], lh[kLocalItems][kEarly], lb[kLocalItems][kBf16Parts];
+  // Every load is issued unconditionally, its index clamped to one that
+  // exists, and its value selected afterwards: a load under a condition
+  // compiles to a branch around it, and the wait at each branch serialised
+  // the loads (a request's first split slot is `first` only when it has
+  // history)
+  const int last_u = max(count - 1, 0);
+  const size_t slot0 = count > 0 ? static_cast<size_t>(first) : 0;
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
     const int x = tid + 256 * it;
-    const int h = x / kDim, k = x % kDim;
     const bool live = x < GQ * kDim;
-    const float* hb = a.ho + (static_cast<size_t>(first) * a.hq + h0 + h) * kDim + k;
+    const int xc = live ? x : 0;
+    const int h = xc / kDim, k = xc % kDim;
+    const float* hb = a.ho + (slot0 * a.hq + h0 + h) * kDim + k;
+    // (masks applied arithmetically: the loaded values are finite, and a
+    // select on them let the compiler move each load under a branch)
 #pragma unroll
-    for (int u = 0; u < kEarly; ++u) vh[it][u] = live && u < count ? hb[static_cast<size_t>(u) * hstride] : 0.f;
+    for (int u = 0; u < kEarly; ++u) {
+      const float v = hb[static_cast<size_t>(min(u, last_u)) * hstride];
+      vh[it][u] = v * (live && u < count ? 1.f : 0.f);
+    }
     const float* bb = a.bo + ((bhead0 + h) * kBf16Parts) * kDim + k;
 #pragma unroll
-    for (int c = 0; c < kBf16Parts; ++c) vb[it][c] = live ? bb[c * kDim] : 0.f;
-    if (local && it < kLocalItems) {
+    for (int c = 0; c < kBf16Parts; ++c) vb[it][c] = bb[c * kDim] * (live ? 1.f : 0.f);
+    if constexpr (kItems <= 2) {   // loaded whether or not the request takes the local path
+      // a wave's items share one head (128 channels = two waves), so its
+      // log-sum-exps are wave-uniform: scalar loads, outside the vector
+      // load count
+      const int hu = __builtin_amdgcn_readfirstlane(h);
 #pragma unroll
-      for (int u = 0; u < kEarly; ++u)
-        lh[it][u] = live && u < count ? a.hlse[static_cast<size_t>(first + u) * a.hq + h0 + h] : -INFINITY;
+      for (int u = 0; u < kEarly; ++u) {
+        const float l = a.hlse[(slot0 + min(u, last_u)) * a.hq + h0 + hu];
+        lh[it][u] = l + (live && u < count ? 0.f : -INFINITY);
+      }
 #pragma unroll
-      for (int c = 0; c < kBf16Parts; ++c) lb[it][c] = live ? a.blse[(bhead0 + h) * kBf16Parts + c] : -INFINITY;
+      for (int c = 0; c < kBf16Parts; ++c)
+        lb[it][c] = a.blse[(bhead0 + hu) * kBf16Parts + c] + (live ? 0.f : -INFINITY);
     }
   }
   if (!local) {
@@ -594,8 +626,10 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
       for (int u = 0; u < kEarly; ++u) mh = fmaxf(mh, lh[it][u]);
       float dh = 0.f, oh = 0.f;
 #pragma unroll
+      // (e^x as 2^(x log2 e) on the hardware exponential: arguments <= 0,
+      // and -inf gives 0)
       for (int u = 0; u < kEarly; ++u) {
-        const float e = u < count && mh != -INFINITY ? expf(lh[it][u] - mh) : 0.f;
+        const float e = u < count && mh != -INFINITY ? __builtin_amdgcn_exp2f((lh[it][u] - mh) * kLog2e) : 0.f;
         dh += e;
         oh = __builtin_fmaf(e, vh[it][u], oh);
       }
@@ -605,7 +639,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
       float db = 0.f, ob = 0.f;
 #pragma unroll
       for (int c = 0; c < kBf16Parts; ++c) {
-        const float e = lb[it][c] == -INFINITY ? 0.f : expf(lb[it][c] - mb);
+        const float e = lb[it][c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lb[it][c] - mb) * kLog2e);
         db += e;
         ob = __builtin_fmaf(e, vb[it][c], ob);
       }
@@ -628,12 +662,14 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
         for (int sp = lane; sp < n; sp += 64) mx = fmaxf(mx, w[sp]);
         mx = wave_max(mx);
         float den = 0.f;
-        for (int sp = lane; sp < n; sp += 64) den += mx == -INFINITY ? 0.f : expf(w[sp] - mx);
+        for (int sp = lane; sp < n; sp += 64)
+          den += mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((w[sp] - mx) * kLog2e);
         den = wave_sum(den);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int sp = lane; sp < n; sp += 64) w[sp] = den > 0.f ? expf(w[sp] - mx) / den : 0.f;
+        for (int sp = lane; sp < n; sp += 64)
+          w[sp] = den > 0.f ? __builtin_amdgcn_exp2f((w[sp] - mx) * kLog2e) / den : 0.f;
         if (lane == 0) lse_s[h][side] = den > 0.f ? mx + logf(den) : -INFINITY;
       }
     }
@@ -686,8 +722,8 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
     for (int h = 0; h < GQ; ++h) {
       const float lh = lse_s[h][0], lbb = lse_s[h][1];
       const float mx = fmaxf(lh, lbb);
-      const float whh = lh == -INFINITY ? 0.f : expf(lh - mx);
-      const float wbb = lbb == -INFINITY ? 0.f : expf(lbb - mx);
+      const float whh = lh == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lh - mx) * kLog2e);
+      const float wbb = lbb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lbb - mx) * kLog2e);
       const float den = whh + wbb;
       a.out[(bhead0 + h) * kDim + i] = den > 0.f ? (whh * oh[h] + wbb * obf[h][i]) / den : 0.f;
       if (a.lse_out != nullptr && i == 0) a.lse_out[bhead0 + h] = den > 0.f ? mx + logf(den) : -INFINITY;

@@ -93,5 +93,6 @@ __device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
 // log2(e) / sqrt(128): scores are kept in base-2 units inside the kernels.
 constexpr float kScoreScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace oscar
