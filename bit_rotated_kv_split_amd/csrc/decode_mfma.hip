@@ -104,12 +104,12 @@ constexpr float kSlack = 2.0f;                 // log2 headroom of p above 1 bef
 constexpr float kHeadroom = 8.0f;              // 2^kSlack times 2x room for larger value scales
 // P' digits: x < 2^31 - 2^24.  With y = x + 0x808080 (below 2^31), the
 // bytes of y are x's four signed base-256 digits, the three low ones plus
-// 128 (their top bits flipped once the rows are formed) and the top one as
+// 128 (their top bits flipped before the word is stored) and the top one as
 // it is.  (The offset is added to the converted integer: added to the float
 // weight it would round away the fraction that the carry keeps.)
 constexpr float kDigitLimit = 2130706432.0f;
 constexpr uint32_t kDigitOffset = 0x808080u;
-constexpr uint32_t kLowDigitFlip = 0x80808080u;
+constexpr uint32_t kLowDigitFlip = 0x00808080u;   // bytes 0..2 of a token's digit word
 constexpr float kDigitUnitMax = 2147483648.0f; // the unit puts a page's largest weight at 2^28
 // Pages a head's int32 accumulators may take between folds: a page adds at
 // most 64 * 128 * 128 to a digit row (the j = 3 operand bytes reach -128).
@@ -163,18 +163,16 @@ __device__ __forceinline__ float p_digits(const v4i& d) {
          16777216.f * static_cast<float>(d.w);
 }
 
-// Byte transpose: row d of the result holds byte d of b0..b3 (byte m = b_m).
-__device__ __forceinline__ void transpose4x4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3,
-                                             uint32_t (&row)[4]) {
-  // v_perm_b32 selects bytes of {src0 (bytes 4..7), src1 (bytes 0..3)}
-  const uint32_t lo01 = __builtin_amdgcn_perm(b1, b0, 0x05010400u);   // b0.0 b1.0 b0.1 b1.1
-  const uint32_t hi01 = __builtin_amdgcn_perm(b1, b0, 0x07030602u);   // b0.2 b1.2 b0.3 b1.3
-  const uint32_t lo23 = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
-  const uint32_t hi23 = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
-  row[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-  row[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-  row[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-  row[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+// 8-byte read from LDS transposed across each 16-lane group
+// (ds_read_b64_tr_b8): lane 16 g + 8 h + b receives, as its byte i, byte b
+// of the 8 bytes that lane 16 g + 2 i + h addressed (checked lane by lane on
+// the device with permuted addresses).
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i lds_read_tr8(const int32_t* p) {
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  // a generic address of LDS data holds the LDS offset in its low 32 bits
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_v2i*)static_cast<size_t>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p))));
 }
 
 // Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
@@ -318,7 +316,7 @@ struct WaveState {
 // chain); zacc lives in LDS to keep it out of the register budget.
 template <int NHB, int NG>
 struct HistSmem {
-  int32_t pop[2][NHB * NG][16][16];   // P' operand rows: [page parity][head block x group][4 h + digit][16 dwords]
+  int32_t pop[2][NHB * NG][kPage][4];   // P' digits: [page parity][head block x group][token][head]
   double zacc[NHB * NG][64];
   int32_t pt[64];                  // page-table entries pt_base .. pt_base + 63 of the split
 };
@@ -559,13 +557,12 @@ __device__ __forceinline__ void score_page(WaveState<NHB, G>& st, const PageRegs
         b[m] = static_cast<uint32_t>(t) + kDigitOffset;
         st.carry[hb][gi] = __builtin_amdgcn_fractf(t);
       }
-      uint32_t dig[4];
-      transpose4x4(b[0], b[1], b[2], b[3], dig);
       st.zf[hb][gi] += zpage;
-      // row 4 lg + digit, dword n: tokens 16 (n/4) + 4 m + n%4 in K-slot order
+      // a word per (token, head): the four digits of token tau(m, n) for
+      // head lg; the value half reads them back transposed into rows
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        sm.pop[slot][hb * NG + gi][4 * lg + d][n] = static_cast<int32_t>(d < 3 ? dig[d] ^ kLowDigitFlip : dig[d]);
+      for (int m = 0; m < 4; ++m)
+        sm.pop[slot][hb * NG + gi][16 * (n >> 2) + 4 * m + (n & 3)][lg] = static_cast<int32_t>(b[m] ^ kLowDigitFlip);
     }
   }
   // every 8 pages the float32 zero-point sums go into the float64 ones
@@ -587,12 +584,23 @@ __device__ __forceinline__ void value_page(WaveState<NHB, G>& st, const PageRegs
                                            HistSmem<NHB, kDim / G>& sm, int slot) {
   constexpr int NG = kDim / G;
   const int n = lane & 15, lg = lane >> 4;
-  // column n = channel 16 cb + n, rows = head x digit
+  // column n = channel 16 cb + n, rows = head x digit.  Lane (n, lg) needs
+  // row n (head n/4, digit n%4) for the K slots of lane group lg: operand
+  // byte e holds token 16 lg + 4 (e % 4) + e / 4.  Two transposed reads build
+  // it from the [token][head] words: as a source, lane (n, lg) addresses the
+  // words of heads 2 (n % 2), +1 for token 16 lg + 4 (i % 4) + i / 4 (i = n / 2),
+  // then for that token + 2 (operand bytes 8..15).
+  const int ti = n >> 1;
+  const int t1 = 16 * lg + 4 * (ti & 3) + (ti >> 2), hp = 2 * (n & 1);
   v4i pa[NHB][NG];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) pa[hb][gi] = *reinterpret_cast<const v4i*>(&sm.pop[slot][hb * NG + gi][n][lg * 4]);
+    for (int gi = 0; gi < NG; ++gi) {
+      const v2i lo = lds_read_tr8(&sm.pop[slot][hb * NG + gi][t1][hp]);
+      const v2i hi = lds_read_tr8(&sm.pop[slot][hb * NG + gi][t1 + 2][hp]);
+      pa[hb][gi] = v4i{lo.x, lo.y, hi.x, hi.y};
+    }
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
     const int gi = (16 * cb) / G;
