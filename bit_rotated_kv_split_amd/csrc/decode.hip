@@ -525,7 +525,8 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   }
 }
 
-// merge_group_kernel (256 threads): the request's history splits are
+// merge_group_kernel (kMergeGroupThreads = 512 threads, one (head,
+// channel) item per thread for four-head blocks): the request's history splits are
 // merged per head in the rotated value domain, rotated back by R_V^T, and
 // merged with the five bf16 partials.  A workgroup takes GQ heads of one
 // (request, KV head): heads GQ * blockIdx.z .. of the group (eight-head
@@ -540,8 +541,8 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 // across a wave): no reductions across lanes and one workgroup barrier.
 // Longer requests take the cooperative path: weights per head by one wave
 // through LDS, partials past the 16th read 16 at a time.
-template <int GQ>
-__global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
+template <int GQ, int NT>
+__global__ void __launch_bounds__(NT) merge_group_kernel(MergeParams a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int kMaxHist = kMaxSplits + 1;
@@ -553,7 +554,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const int first = a.req[2 * b], count = a.req[2 * b + 1];
   const int h0 = kvh * a.gq + GQ * static_cast<int>(blockIdx.z);   // first head of this workgroup's block
   const size_t bhead0 = static_cast<size_t>(b) * a.hq + h0;
-  constexpr int kItems = (GQ * kDim + 255) / 256;   // (head, channel) items per thread
+  constexpr int kItems = (GQ * kDim + NT - 1) / NT;   // (head, channel) items per thread
   constexpr int kEarly = 16;
   // (kept for up to two items per thread: four or more per thread would hold
   // twice the registers and spill)
@@ -570,7 +571,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   const size_t slot0 = count > 0 ? static_cast<size_t>(first) : 0;
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
-    const int x = tid + 256 * it;
+    const int x = tid + NT * it;
     const bool live = x < GQ * kDim;
     const int xc = live ? x : 0;
     const int h = xc / kDim, k = xc % kDim;
@@ -601,24 +602,27 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
     }
   }
   if (!local) {
-    for (int x = tid; x < GQ * count; x += 256) {
+    for (int x = tid; x < GQ * count; x += NT) {
       const int h = x / count, sp = x % count;
       wh[h][sp] = a.hlse[static_cast<size_t>(first + sp) * a.hq + h0 + h];
     }
-    for (int x = tid; x < GQ * kBf16Parts; x += 256)
+    for (int x = tid; x < GQ * kBf16Parts; x += NT)
       wb[x / kBf16Parts][x % kBf16Parts] = a.blse[(bhead0 + x / kBf16Parts) * kBf16Parts + x % kBf16Parts];
   }
-  // thread (i, kh): row i of R_V, columns 64 kh .. 64 kh + 63
-  const int i = tid >> 1, kh = tid & 1;
-  float4 rr[16];
-  const float4* rrow = reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+  // thread (i, kh): row i of R_V, columns kCols kh .. kCols (kh + 1) - 1
+  constexpr int kParts = NT / kDim, kCols = kDim / kParts;
+  static_assert(kParts == 2 || kParts == 4, "two or four threads per R_V row");
+  const int i = tid / kParts, kh = tid % kParts;
+  float4 rr[kCols / 4];
+  const float4* rrow =
+      reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + kCols * kh);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+  for (int c = 0; c < kCols / 4; ++c) rr[c] = rrow[c];
   if (local) {
     // each thread weighs its own items' partials
 #pragma unroll
     for (int it = 0; it < kLocalItems; ++it) {
-      const int x = tid + 256 * it;
+      const int x = tid + NT * it;
       if (x >= GQ * kDim) break;
       const int h = x / kDim, k = x % kDim;
       float mh = -INFINITY;
@@ -653,7 +657,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   } else {
     __syncthreads();
     // per head and side: normalised weights of the partials
-    for (int h = wave; h < GQ; h += 4) {
+    for (int h = wave; h < GQ; h += NT / 64) {
 #pragma unroll
       for (int side = 0; side < 2; ++side) {
         float* w = side ? wb[h] : wh[h];
@@ -678,7 +682,7 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
     // rest 16 loads at a time
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
-      const int x = tid + 256 * it;
+      const int x = tid + NT * it;
       if (x >= GQ * kDim) break;
       const int h = x / kDim, k = x % kDim;
       float oh = 0.f;
@@ -708,14 +712,16 @@ __global__ void __launch_bounds__(256) merge_group_kernel(MergeParams a) {
   for (int h = 0; h < GQ; ++h) {
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int k = 64 * kh + 4 * c;
+    for (int c = 0; c < kCols / 4; ++c) {
+      const int k = kCols * kh + 4 * c;
       acc = __builtin_fmaf(orot[h][k + 0], rr[c].x, acc);
       acc = __builtin_fmaf(orot[h][k + 1], rr[c].y, acc);
       acc = __builtin_fmaf(orot[h][k + 2], rr[c].z, acc);
       acc = __builtin_fmaf(orot[h][k + 3], rr[c].w, acc);
     }
-    oh[h] = acc + __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 1, 64);
+    if constexpr (kParts == 4) acc += __shfl_xor(acc, 2, 64);
+    oh[h] = acc;
   }
   if (kh == 0) {
 #pragma unroll
@@ -827,10 +833,15 @@ struct Bf16Run {
   }
 };
 
+#ifndef OSCAR_MERGE_GROUP_THREADS
+#define OSCAR_MERGE_GROUP_THREADS 512
+#endif
+constexpr int kMergeGroupThreads = OSCAR_MERGE_GROUP_THREADS;
+
 template <int GQ>
 struct MergeGroupRun {
   static hipError_t run(const MergeParams& p, int hkv, int32_t batch, hipStream_t s) {
-    merge_group_kernel<GQ><<<dim3(hkv, batch), 256, 0, s>>>(p);
+    merge_group_kernel<GQ, kMergeGroupThreads><<<dim3(hkv, batch), kMergeGroupThreads, 0, s>>>(p);
     return hipGetLastError();
   }
 };
@@ -872,7 +883,8 @@ hipError_t launch_merge(const oscar_dims& d, const oscar_rotation& rot, int32_t 
     return hipGetLastError();
   }
   if (p.gq % 4 == 0 && p.gq > 4) {   // four heads per workgroup: more, shorter workgroups
-    merge_group_kernel<4><<<dim3(d.num_kv_heads, batch, p.gq / 4), 256, 0, s>>>(p);
+    merge_group_kernel<4, kMergeGroupThreads><<<dim3(d.num_kv_heads, batch, p.gq / 4), kMergeGroupThreads, 0, s>>>(
+        p);
     return hipGetLastError();
   }
   return dispatch_gq<MergeGroupRun>(p.gq, p, d.num_kv_heads, batch, s);
