@@ -369,13 +369,13 @@ __global__ void __launch_bounds__(64) bf16_kernel(Bf16Params a) {
 // merge_group_kernel: workgroup = (KV head, request), sharing R_V across the
 // group's heads.
 //
-// merge_head_kernel (512 threads): the request's history splits (from the
-// schedule) are merged in the rotated value domain, rotated back by R_V^T,
-// and merged with the five bf16 partials.  Thread t weighs split t; the
-// weighted sum over splits runs on four threads per channel (channel
-// t % 128, every fourth split), so a long request's up to 251 splits take
-// four rounds of loads; threads 0..255 hold half a row of R_V each, loaded
-// before anything else.
+// merge_head_kernel (kMergeHeadThreads = 1024 threads): the request's
+// history splits (from the schedule) are merged in the rotated value domain,
+// rotated back by R_V^T, and merged with the five bf16 partials.  Thread t
+// weighs split t; the weighted sum over splits runs on eight threads per
+// channel (channel t % 128, every eighth split: up to 32 loads per thread
+// for a long request's 251 splits); each thread holds an eighth of a row of
+// R_V, loaded before anything else.
 struct MergeParams {
   const float* ho;        // [slots][Hq][128]
   const float* hlse;      // [slots][Hq]
@@ -389,7 +389,10 @@ struct MergeParams {
   int32_t gq;
 };
 
-constexpr int kMergeHeadThreads = 512;
+#ifndef OSCAR_MERGE_HEAD_THREADS
+#define OSCAR_MERGE_HEAD_THREADS 1024
+#endif
+constexpr int kMergeHeadThreads = OSCAR_MERGE_HEAD_THREADS;
 static_assert(kMaxSplits < kMergeHeadThreads, "one thread weighs each split");
 
 __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergeParams a) {
@@ -435,14 +438,16 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
   float lb[kBf16Parts];
 #pragma unroll
   for (int c = 0; c < kBf16Parts; ++c) lb[c] = a.blse[bh * kBf16Parts + c];
-  // threads 0..255: row i of R_V, columns 64 kh .. 64 kh + 63
-  const int i = (tid >> 1) & (kDim - 1), kh = tid & 1;
-  float4 rr[16];
+  // thread (i, kh): row i of R_V, columns kCols kh .. kCols (kh + 1) - 1
+  constexpr int kParts = kMergeHeadThreads / kDim, kCols = kDim / kParts;
+  static_assert(kParts == 4 || kParts == 8, "four or eight threads per R_V row");
+  const int i = tid / kParts, kh = tid % kParts;
+  float4 rr[kCols / 4];
   {
     const float4* rrow =
-        reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + 64 * kh);
+        reinterpret_cast<const float4*>(a.r_v + (static_cast<size_t>(kvh) * kDim + i) * kDim + kCols * kh);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) rr[c] = rrow[c];
+    for (int c = 0; c < kCols / 4; ++c) rr[c] = rrow[c];
   }
   // every history partial this thread sums (channel k, the splits congruent
   // to par modulo kPar) and its bf16 partials are requested now, before the
@@ -461,7 +466,7 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
 #pragma unroll
   for (int c = 0; c < kBf16Parts; ++c) {
     const float x = a.bo[(bh * kBf16Parts + c) * kDim + i];
-    vb[c] = tid < 2 * kDim && kh == 0 ? x : 0.f;
+    vb[c] = kh == 0 ? x : 0.f;
   }
   // history split weights e^{lse - M} / sum (count <= kMaxSplits < threads)
   const float mh = bmax(l);
@@ -497,18 +502,19 @@ __global__ void __launch_bounds__(kMergeHeadThreads) merge_head_kernel(MergePara
     y[tid] = t;
   }
   __syncthreads();
-  if (tid >= 2 * kDim) return;   // whole waves
   // back to the model domain: x_i = sum_k y_k R_V[i][k]
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int kc = 64 * kh + 4 * c;
+  for (int c = 0; c < kCols / 4; ++c) {
+    const int kc = kCols * kh + 4 * c;
     acc = __builtin_fmaf(y[kc + 0], rr[c].x, acc);
     acc = __builtin_fmaf(y[kc + 1], rr[c].y, acc);
     acc = __builtin_fmaf(y[kc + 2], rr[c].z, acc);
     acc = __builtin_fmaf(y[kc + 3], rr[c].w, acc);
   }
-  const float xh = acc + __shfl_xor(acc, 1, 64);
+#pragma unroll
+  for (int o = 1; o < kParts; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  const float xh = acc;
   if (kh == 0) {
     float ob = 0.f;
 #pragma unroll
