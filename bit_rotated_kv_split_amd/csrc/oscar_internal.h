@@ -16,7 +16,7 @@ constexpr int kBf16Parts = 5;
 // Upper bound on the history splits of one request.
 constexpr int kMaxSplits = 251;
 // Smallest history split, in pages.
-constexpr int kMinSplitPages = 8;
+constexpr int kMinSplitPages = 4;
 // The history split schedule aims by default for the workgroups the
 // matrix-core history kernel keeps resident on the device's SIMDs (4 per
 // compute unit, read from the device; hist_default_target), so the splits

@@ -221,9 +221,10 @@ typedef struct oscar_decode_options {
  * schedules for a batch of this size.  The splits themselves are chosen on
  * the device from the lengths: with T = ceil(W / Hkv) and W the options'
  * history_target (by default the history kernel's resident workgroups on
- * the current device: 2048 on a 256-CU MI355X, 1536 for eight-head groups
- * at G = 128 and 1024 for other eight-head groups), the pages per split q
- * is the smallest q >= max(8, ceil(longest / 251)) for which the batch
+ * the current device; on a 256-CU MI355X 3072 at G = 128 with the uniform
+ * codebook and 2048 otherwise, halved for groups of more than four query
+ * heads, which take two-wave workgroups), the pages per split q
+ * is the smallest q >= max(4, ceil(longest / 251)) for which the batch
  * needs at most T splits, request b taking ceil(pages_b / q) splits of
  * equal size (the last one shorter); if one split per request already
  * exceeds T, q is the longest request's page count.  The bound returned is

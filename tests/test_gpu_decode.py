@@ -141,8 +141,8 @@ def test_split_targets_edges(kernel, target):
     _run_case(w, KERNELS[kernel], target=target)
 
 
-def _reference_split_pages(pages, target, max_per_request=251, min_pages=8):
-    """The documented split rule: the smallest q >= max(8, ceil(longest /
+def _reference_split_pages(pages, target, max_per_request=251, min_pages=4):
+    """The documented split rule: the smallest q >= max(4, ceil(longest /
     251)) whose split count sum(ceil(pages_b / q)) is at most target, else
     the longest request's page count."""
     pages = np.asarray(pages, dtype=np.int64)
