@@ -825,7 +825,10 @@ hist_mfma_kernel(MfmaParams a) {
   // 1-D grid: every history split slot first (workgroups are dispatched in
   // id order, so these are the resident ones), then the bf16 chunks, which
   // fill the slots freed as history splits finish.  Slots beyond the
-  // scheduled split count exit at once.  A query group wider than four
+  // scheduled split count exit at once.  The chunks take only even ids
+  // (the odd ones between them exit at once): workgroups go to the XCDs
+  // round robin by id, and the even XCDs finish their history splits
+  // 7-10 % sooner on these GPUs, so the chunks stay off the slower ones.  A query group wider than four
   // heads takes two waves, heads 4w .. 4w+3 each; both read the same pages,
   // the second mostly from the compute unit's cache.
   const int id = blockIdx.x;
@@ -838,7 +841,9 @@ hist_mfma_kernel(MfmaParams a) {
   };
   __shared__ Smem smem;
   if (id >= n_hist_wg) {   // a bf16 sink/recent chunk, four heads per wave
-    const int r = id - n_hist_wg;
+    const int c0 = (n_hist_wg + 1) & ~1;   // first even id of the chunk range
+    if (id < c0 || (id & 1)) return;
+    const int r = (id - c0) >> 1;
     bf16_chunk_mfma(a.bf, a.gq, 4 * wave, r % kBf16Parts, (r / kBf16Parts) % a.hkv, r / (kBf16Parts * a.hkv),
                     smem.bf[wave]);
     return;
@@ -1119,7 +1124,8 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   p.lm_kb = (3.f * cbk->lev[2] - cbk->lev[3]) * 0.5f;
   p.bf = make_bf16_params(a);
   p.clk = a.clock_trace;
-  const dim3 grid((p.slots + kBf16Parts * a.cache->batch) * d.num_kv_heads);
+  const int n_hist_wg = p.slots * d.num_kv_heads;
+  const dim3 grid(((n_hist_wg + 1) & ~1) + 2 * kBf16Parts * a.cache->batch * d.num_kv_heads);
   const dim3 block(64 * WAVES);
   if (a.ev_start != nullptr && a.ev_stop != nullptr)
     hipExtLaunchKernelGGL(hist_mfma_kernel<G, WAVES, BUF, MINW, LM>, grid, block, 0, s, a.ev_start, a.ev_stop, 0,
