@@ -54,34 +54,45 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
     demote_unit_g(G, dm, kvh, b - batch, half != 0, threadIdx.x & 127, dsm[half]);
     return;
   }
-  const int tid = threadIdx.x, k = tid & (kDim - 1), half = tid >> 7;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  constexpr int kRowGroups = 8, kGroupRows = kDim / kRowGroups;
   __shared__ float qs[GQ][kDim];
-  __shared__ float part[2][GQ][kDim];
+  __shared__ float part[kRowGroups][GQ][kDim];
   __shared__ float qr[GQ][kDim];
   __shared__ float qinv[GQ];
   const size_t head0 = static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * GQ;
-  // q . R_K: thread (k, half) sums rows i of its half; its rotation values
-  // are requested together with the queries, so the rows wait on memory once
-  const float* r = r_k + static_cast<size_t>(kvh) * kDim * kDim;
-  float rv[64];
+  // q . R_K: thread (cq, rg) sums rows 16 rg .. 16 rg + 15 for channels
+  // 4 cq .. 4 cq + 3 with 16-byte loads, requested together with the
+  // queries, so the rows wait on memory once; the eight row-group partials
+  // are added in LDS
+  const int cq = tid & (kDim / 4 - 1), rg = tid >> 5;
+  const float4* r4 = reinterpret_cast<const float4*>(r_k + static_cast<size_t>(kvh) * kDim * kDim);
+  float4 rv[kGroupRows];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) rv[i] = r[(64 * half + i) * kDim + k];
+  for (int i = 0; i < kGroupRows; ++i) rv[i] = r4[(kGroupRows * rg + i) * (kDim / 4) + cq];
   for (int i = tid; i < GQ * kDim; i += 256) qs[i / kDim][i % kDim] = bf16_to_f32(q[head0 * kDim + i]);
   __syncthreads();
-  float acc[GQ];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
+  for (int h = 0; h < GQ; ++h) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < 64; ++i)
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h] = __builtin_fmaf(qs[h][64 * half + i], rv[i], acc[h]);
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) part[half][h][k] = acc[h];
+    for (int i = 0; i < kGroupRows; ++i) {
+      const float x = qs[h][kGroupRows * rg + i];
+      acc.x = __builtin_fmaf(x, rv[i].x, acc.x);
+      acc.y = __builtin_fmaf(x, rv[i].y, acc.y);
+      acc.z = __builtin_fmaf(x, rv[i].z, acc.z);
+      acc.w = __builtin_fmaf(x, rv[i].w, acc.w);
+    }
+    *reinterpret_cast<float4*>(&part[rg][h][4 * cq]) = acc;
+  }
   __syncthreads();
   for (int i = tid; i < GQ * kDim; i += 256) {
     const int h = i / kDim, c = i % kDim;
-    const float v = (part[0][h][c] + part[1][h][c]) * kScoreScaleLog2;
+    float t = part[0][h][c];
+#pragma unroll
+    for (int g = 1; g < kRowGroups; ++g) t += part[g][h][c];
+    const float v = t * kScoreScaleLog2;
     qr[h][c] = v;
     qrot[(head0 + h) * kDim + c] = v;
   }

@@ -26,6 +26,7 @@ struct QuantSmem {
   float xw[2][NT][2];          // per-wave (min, max) when a group spans both waves
   double xd[2][2][NT];         // per-wave float64 (sum, sum of squares), same case
   uint8_t code[NT][kDim];
+  double rp[4][kDim];          // demotion of one token: float64 partial rotations per row quarter
 };
 
 // Sum over the G lanes of this thread's group, in float64: a butterfly
@@ -56,17 +57,6 @@ __device__ __forceinline__ void group_sum_f64(double (&v)[NT], double (&xd)[2][N
 //     float64; code = number of thresholds (-thr, 0, thr) below
 //     (y - zero) / scale.
 // A group whose scale is 0 gets code 0.
-// Channel k of x . R for one token held in sm.x[0], with the rotation
-// column already in registers (rv[i] = R[i][k]): float64 products and four
-// float64 partial sums, rounded once to float32.
-__device__ __forceinline__ float rotate_one(const QuantSmem<1>& sm, const float (&rv)[kDim]) {
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int i = 0; i < kDim; ++i)
-    acc[i & 3] = fma(static_cast<double>(sm.x[0][i]), static_cast<double>(rv[i]), acc[i & 3]);
-  return static_cast<float>((acc[0] + acc[1]) + (acc[2] + acc[3]));
-}
-
 template <int G, int NT>
 __device__ void quantize_rotated(QuantSmem<NT>& sm, int nt, float (&y)[NT], int k, int codebook, float thr);
 
@@ -243,16 +233,36 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
   if (L > kBf16Tokens) {   // uniform across the workgroup
     const int j = L - kBf16Tokens - 1;            // history index of position L-257
     const int ring = (L - 1 - kSink) & (kRecent - 1);
-    const float* r = a.r + static_cast<size_t>(kvh) * kDim * kDim;
+    // x . R: thread k sums rows 32 rg .. 32 rg + 31 (rg = k / 32) for
+    // channels 4 cq .. 4 cq + 3 (cq = k % 32), float64 products, 16-byte
+    // loads of R; the four row-quarter partials of channel k are added in a
+    // fixed order and rounded once to float32
+    const int cq = k & 31, rg = k >> 5;
+    const float4* r4 = reinterpret_cast<const float4*>(a.r + static_cast<size_t>(kvh) * kDim * kDim);
     const uint16_t xk = recent[ring * kDim + k];
-    float rv[kDim];
+    float4 rv[32];
 #pragma unroll
-    for (int i = 0; i < kDim; ++i) rv[i] = r[i * kDim + k];
+    for (int i = 0; i < 32; ++i) rv[i] = r4[(32 * rg + i) * (kDim / 4) + cq];
     const float c = a.clip[kvh * kDim + k];
     const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + (j >> 6)];
     sm.x[0][k] = bf16_to_f32(xk);
     __syncthreads();
-    float y[1] = {fminf(fmaxf(rotate_one(sm, rv), -c), c)};
+    {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double xi = static_cast<double>(sm.x[0][32 * rg + i]);
+        acc[0] = fma(xi, static_cast<double>(rv[i].x), acc[0]);
+        acc[1] = fma(xi, static_cast<double>(rv[i].y), acc[1]);
+        acc[2] = fma(xi, static_cast<double>(rv[i].z), acc[2]);
+        acc[3] = fma(xi, static_cast<double>(rv[i].w), acc[3]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.rp[rg][4 * cq + e] = acc[e];
+    }
+    __syncthreads();
+    const float yk = static_cast<float>((sm.rp[0][k] + sm.rp[1][k]) + (sm.rp[2][k] + sm.rp[3][k]));
+    float y[1] = {fminf(fmaxf(yk, -c), c)};
     quantize_rotated<G, 1>(sm, 1, y, k, a.codebook, a.thr);
     uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
     const int slot = j & 63;
