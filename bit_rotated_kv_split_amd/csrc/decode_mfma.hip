@@ -827,8 +827,9 @@ hist_mfma_kernel(MfmaParams a) {
   // fill the slots freed as history splits finish.  Slots beyond the
   // scheduled split count exit at once.  The chunks take only even ids
   // (the odd ones between them exit at once): workgroups go to the XCDs
-  // round robin by id, and the even XCDs finish their history splits
-  // 7-10 % sooner on these GPUs, so the chunks stay off the slower ones.  A query group wider than four
+  // round robin by id, and on the MI355X parts measured the even XCDs
+  // finished their history splits 7-10 % sooner, so the chunks stay off the
+  // slower ones.  A query group wider than four
   // heads takes two waves, heads 4w .. 4w+3 each; both read the same pages,
   // the second mostly from the compute unit's cache.
   const int id = blockIdx.x;
