@@ -131,13 +131,14 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   for (int op = 0; op < n_ops; ++op) {
     uint32_t* qpw = reinterpret_cast<uint32_t*>(qp + op * kQPackOperandBytes);
     const float mul = op == 0 ? 1.f : lm_ratio;
-    for (int widx = tid; widx < 2 * 4 * kQPackRows * 4; widx += 256) {
-      const int j = widx & 3;                     // dword j = bytes 4j .. 4j+3 of the row
-      const int row = (widx >> 2) & (kQPackRows - 1);
-      const int kg = (widx >> 7) & 3;
-      const int hf = widx >> 9;
-      const int h = row >> 2, digit = row & 3;
-      uint32_t word = 0;
+    // thread (hf, kg, h, j) = tid: the four digit rows of head h for dword j
+    // of channel half hf, lane group kg; each value is decomposed once and
+    // its digits go to the four rows' words (word index
+    // ((hf * 4 + kg) * kQPackRows + 4 h + digit) * 4 + j)
+    static_assert(2 * 4 * (kQPackRows / 4) * 4 == 256, "one thread per four-row word group");
+    {
+      const int j = tid & 3, h = (tid >> 2) & (kQPackRows / 4 - 1), kg = (tid >> 5) & 3, hf = tid >> 7;
+      uint32_t word[4] = {0u, 0u, 0u, 0u};
       if (h < GQ) {
         const float slot = j == 1 ? 0.25f : (j == 2 ? 0.0625f : (j == 3 ? 0.015625f : 1.f));
 #pragma unroll
@@ -150,11 +151,15 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
           const int q2 = (q1 - d1) >> 8;
           const int d2 = ((q2 + 128) & 255) - 128;
           const int d3 = (q2 - d2) >> 8;
-          const int dv = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
-          word |= static_cast<uint32_t>(dv & 255) << (8 * b2);
+          word[0] |= static_cast<uint32_t>(d0 & 255) << (8 * b2);
+          word[1] |= static_cast<uint32_t>(d1 & 255) << (8 * b2);
+          word[2] |= static_cast<uint32_t>(d2 & 255) << (8 * b2);
+          word[3] |= static_cast<uint32_t>(d3 & 255) << (8 * b2);
         }
       }
-      qpw[widx] = word;
+      const int base = ((hf * 4 + kg) * kQPackRows + 4 * h) * 4 + j;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) qpw[base + 4 * d] = word[d];
     }
   }
   if (tid >= GQ && tid < 8) {
