@@ -39,10 +39,12 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
             const int32_t* __restrict__ seq_lens, int batch, int target, int32_t* __restrict__ sched,
             int32_t* __restrict__ req, float lm_ratio, DemoteStep dm) {
   // Row 0 of the grid (dispatched first) holds the split scheduler; rows
-  // 1 .. B rotate the queries of request blockIdx.y - 1; rows B+1 .. 2B, when
-  // launched, demote the step's oldest recent token of request
-  // blockIdx.y - B - 1 (threads 0..127 the key, 128..255 the value), which
-  // touches nothing the other rows read.
+  // 1 .. B rotate the queries of request blockIdx.y - 1; the rows after
+  // them, when launched, demote the step's oldest recent token, which
+  // touches nothing the other rows read: rows B+1 .. 2B for request
+  // blockIdx.y - B - 1 (threads 0..127 the key, 128..255 the value), or, for
+  // small batches (3B+1 rows), rows B+1 .. 2B the key and 2B+1 .. 3B the
+  // value, each by all 256 threads.
   const int kvh = blockIdx.x, b = static_cast<int>(blockIdx.y) - 1;
   if (b < 0) {
     if (kvh == 0) schedule_splits(seq_lens, batch, kBf16Tokens, target, sched, req);
@@ -50,8 +52,13 @@ qrot_kernel(const uint16_t* __restrict__ q, const float* __restrict__ r_k, int h
   }
   if (b >= batch) {
     __shared__ QuantSmem<1> dsm[2];
-    const int half = threadIdx.x >> 7;
-    demote_unit_g(G, dm, kvh, b - batch, half != 0, threadIdx.x & 127, dsm[half]);
+    if (static_cast<int>(gridDim.y) > 1 + 2 * batch) {
+      const bool is_v = b >= 2 * batch;
+      demote_unit_g<256>(G, dm, kvh, b - (is_v ? 2 : 1) * batch, is_v, threadIdx.x, dsm[0]);
+    } else {
+      const int half = threadIdx.x >> 7;
+      demote_unit_g(G, dm, kvh, b - batch, half != 0, threadIdx.x & 127, dsm[half]);
+    }
     return;
   }
   const int tid = threadIdx.x;
@@ -787,7 +794,12 @@ struct QrotRun {
   static hipError_t run(const DecodeArgs& a, hipStream_t s) {
     const oscar_dims& d = *a.dims;
     const int batch = a.cache->batch;
-    const dim3 grid(d.num_kv_heads, 1 + batch + (a.demote != nullptr ? batch : 0));
+    // the demotion rows: one 256-thread workgroup each for the key and the
+    // value while the launch is small (batch 1 x 8 KV heads: 33.4/33.7 ->
+    // 33.0/33.1 us per step), the key and value halves of one workgroup
+    // otherwise (at 32 x 8 the doubled rows cost the step about 1 us)
+    const bool wide = batch * d.num_kv_heads <= 64;
+    const dim3 grid(d.num_kv_heads, 1 + batch + (a.demote != nullptr ? (wide ? 2 : 1) * batch : 0));
     qrot_kernel<GQ><<<grid, 256, 0, s>>>(
         a.q, a.rot->r_k, d.num_q_heads, d.num_kv_heads, d.group_size,
         reinterpret_cast<float*>(a.ws + a.lay.off_qrot), reinterpret_cast<float*>(a.ws + a.lay.off_qsum),

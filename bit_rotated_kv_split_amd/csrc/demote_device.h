@@ -26,7 +26,7 @@ struct QuantSmem {
   float xw[2][NT][2];          // per-wave (min, max) when a group spans both waves
   double xd[2][2][NT];         // per-wave float64 (sum, sum of squares), same case
   uint8_t code[NT][kDim];
-  double rp[4][kDim];          // demotion of one token: float64 partial rotations per row quarter
+  double rp[8][kDim];          // demotion of one token: float64 partial rotations per row group
 };
 
 // Sum over the G lanes of this thread's group, in float64: a butterfly
@@ -213,45 +213,52 @@ __device__ void store_tokens(const QuantSmem<NT>& sm, int nt, uint8_t* __restric
 }
 
 // Demotion of one (request, KV head, K or V) for a decode step, by one
-// 128-thread unit (thread k): the token at position L-257 leaves the recent
+// unit of NT = 128 or 256 threads (thread k): the token at position L-257 leaves the recent
 // ring for history index L-321, then the new token (if given) takes its
 // sink or recent slot.  Everything the unit reads is requested right after
 // the length, so the unit waits on memory about twice (the length, then
 // the token, its rotation column, the clip threshold, the page-table entry
 // and the new token together); the value word's other fifteen slots are
-// kept by an atomic AND/OR pair instead of a read-modify-write.
-template <int G>
-__device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int k, QuantSmem<1>& sm) {
+// kept by an atomic AND/OR pair instead of a read-modify-write.  With
+// 256 threads each thread sums half as many rows of R; both halves then
+// run the quantizer on the same values (identical LDS writes) and only the
+// first half stores.
+template <int G, int NT = kDim>
+__device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int kt, QuantSmem<1>& sm) {
+  static_assert(NT == kDim || NT == 2 * kDim, "one or two threads per channel");
   constexpr int NG = kDim / G;
+  constexpr int kRG = NT / 32, kRows = kDim / kRG;   // row groups, rows per group
+  const int k = kt & (kDim - 1);                     // channel
+  const bool writer = kt < kDim;                     // uniform per wave
   const DemoteArgs& a = is_v ? d.vv : d.kk;
   const int hkv = a.hkv;
   const int L = d.seq_lens[b];
   uint16_t* recent = (is_v ? d.recent_v : d.recent_k) + (static_cast<size_t>(b) * hkv + kvh) * kRecent * kDim;
   const uint16_t* src = is_v ? d.v_new : d.k_new;
   const bool append = src != nullptr && L >= 1;   // uniform across the workgroup
-  const uint16_t val = append ? src[(static_cast<size_t>(b) * hkv + kvh) * kDim + k] : uint16_t{0};
+  const uint16_t val = append && writer ? src[(static_cast<size_t>(b) * hkv + kvh) * kDim + k] : uint16_t{0};
   if (L > kBf16Tokens) {   // uniform across the workgroup
     const int j = L - kBf16Tokens - 1;            // history index of position L-257
     const int ring = (L - 1 - kSink) & (kRecent - 1);
-    // x . R: thread k sums rows 32 rg .. 32 rg + 31 (rg = k / 32) for
-    // channels 4 cq .. 4 cq + 3 (cq = k % 32), float64 products, 16-byte
-    // loads of R; the four row-quarter partials of channel k are added in a
-    // fixed order and rounded once to float32
-    const int cq = k & 31, rg = k >> 5;
+    // x . R: thread kt sums rows kRows rg .. kRows rg + kRows - 1
+    // (rg = kt / 32) for channels 4 cq .. 4 cq + 3 (cq = kt % 32), float64
+    // products, 16-byte loads of R; the row-group partials of channel k are
+    // added in a fixed order and rounded once to float32
+    const int cq = kt & 31, rg = kt >> 5;
     const float4* r4 = reinterpret_cast<const float4*>(a.r + static_cast<size_t>(kvh) * kDim * kDim);
     const uint16_t xk = recent[ring * kDim + k];
-    float4 rv[32];
+    float4 rv[kRows];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) rv[i] = r4[(32 * rg + i) * (kDim / 4) + cq];
+    for (int i = 0; i < kRows; ++i) rv[i] = r4[(kRows * rg + i) * (kDim / 4) + cq];
     const float c = a.clip[kvh * kDim + k];
     const int phys = a.page_table[static_cast<size_t>(b) * a.max_pages + (j >> 6)];
-    sm.x[0][k] = bf16_to_f32(xk);
+    if (writer) sm.x[0][k] = bf16_to_f32(xk);
     __syncthreads();
     {
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const double xi = static_cast<double>(sm.x[0][32 * rg + i]);
+      for (int i = 0; i < kRows; ++i) {
+        const double xi = static_cast<double>(sm.x[0][kRows * rg + i]);
         acc[0] = fma(xi, static_cast<double>(rv[i].x), acc[0]);
         acc[1] = fma(xi, static_cast<double>(rv[i].y), acc[1]);
         acc[2] = fma(xi, static_cast<double>(rv[i].z), acc[2]);
@@ -261,11 +268,14 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
       for (int e = 0; e < 4; ++e) sm.rp[rg][4 * cq + e] = acc[e];
     }
     __syncthreads();
-    const float yk = static_cast<float>((sm.rp[0][k] + sm.rp[1][k]) + (sm.rp[2][k] + sm.rp[3][k]));
+    double ys = (sm.rp[0][k] + sm.rp[1][k]) + (sm.rp[2][k] + sm.rp[3][k]);
+    if constexpr (kRG == 8) ys += (sm.rp[4][k] + sm.rp[5][k]) + (sm.rp[6][k] + sm.rp[7][k]);
+    const float yk = static_cast<float>(ys);
     float y[1] = {fminf(fmaxf(yk, -c), c)};
     quantize_rotated<G, 1>(sm, 1, y, k, a.codebook, a.thr);
     uint8_t* blk = a.pages + (static_cast<size_t>(phys) * hkv + kvh) * block_bytes(G);
     const int slot = j & 63;
+    if (!writer) return;   // the second half has no stores; nothing below waits
     uint32_t* words = reinterpret_cast<uint32_t*>(blk);
     if (!is_v) {
       if (k < 8) {   // key word d = k: channels 16k .. 16k+15 of this slot
@@ -289,7 +299,7 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
       e[1] = f32_to_bf16_rne(sm.zero[0][k]);
     }
   }
-  if (append) {
+  if (append && writer) {
     const int p = L - 1;
     if (p < kSink) {
       uint16_t* sink = (is_v ? d.sink_v : d.sink_k) + (static_cast<size_t>(b) * hkv + kvh) * kSink * kDim;
@@ -301,11 +311,12 @@ __device__ void demote_unit(const DemoteStep& d, int kvh, int b, bool is_v, int 
 }
 
 // Runtime-G dispatch of demote_unit.
+template <int NT = kDim>
 __device__ __forceinline__ void demote_unit_g(int group, const DemoteStep& d, int kvh, int b, bool is_v, int k,
                                               QuantSmem<1>& sm) {
-  if (group == 32) demote_unit<32>(d, kvh, b, is_v, k, sm);
-  else if (group == 64) demote_unit<64>(d, kvh, b, is_v, k, sm);
-  else demote_unit<128>(d, kvh, b, is_v, k, sm);
+  if (group == 32) demote_unit<32, NT>(d, kvh, b, is_v, k, sm);
+  else if (group == 64) demote_unit<64, NT>(d, kvh, b, is_v, k, sm);
+  else demote_unit<128, NT>(d, kvh, b, is_v, k, sm);
 }
 
 }  // namespace
