@@ -794,6 +794,19 @@ __device__ __forceinline__ void bf16_chunk_mfma(const Bf16Params& a, int gq, int
   }
 }
 
+// Issue priority of a wave by the quarter of its split's page groups it is
+// in: 3 in the first quarter down to 0 in the last.  Waves sharing a SIMD
+// otherwise issue oldest first, so of three equal splits started together
+// the youngest finishes last and runs alone, with few loads in flight; a
+// wave that gets ahead now yields to the ones behind it at each quarter.
+__device__ __forceinline__ void split_priority(int it, int groups) {
+  const int qtr = (4 * it) / groups;   // uniform
+  if (qtr == 0) __builtin_amdgcn_s_setprio(3);
+  else if (qtr == 1) __builtin_amdgcn_s_setprio(2);
+  else if (qtr == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Orders one page's P' row writes before the reads that follow (a wave
 // reads rows other lanes wrote).
 __device__ __forceinline__ void wave_lds_fence() {
@@ -1006,6 +1019,7 @@ hist_mfma_kernel(MfmaParams a) {
       const int groups = (p1 - p0 - 1) / BUF;
       int p = p0 + 1;
       for (int it = 0; it < groups; ++it, p += BUF) {
+        split_priority(it, groups);
 #pragma unroll
         for (int k = 0; k < BUF; ++k) {
           value_page<LM, NHB, G>(st, buf[k % BUF], lane, sm, (p + k - 1 - p0) & 1);
@@ -1036,6 +1050,7 @@ hist_mfma_kernel(MfmaParams a) {
       const int groups = (p1 - p0) / BUF;
       int p = p0;
       for (int it = 0; it < groups; ++it, p += BUF) {
+        split_priority(it, groups);
 #pragma unroll
         for (int k = 0; k < BUF; ++k) {
           load_page<G, WAVES == 1, kStreamSz>(buf[(k + BUF - 1) % BUF], page_ptr(min(p + k + BUF - 1, p_last)), lane);
@@ -1050,6 +1065,7 @@ hist_mfma_kernel(MfmaParams a) {
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- partial output of this split (rotated value domain)
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
