@@ -794,16 +794,17 @@ __device__ __forceinline__ void bf16_chunk_mfma(const Bf16Params& a, int gq, int
   }
 }
 
-// Issue priority of a wave by the quarter of its split's page groups it is
-// in: 3 in the first quarter down to 0 in the last.  Waves sharing a SIMD
-// otherwise issue oldest first, so of three equal splits started together
-// the youngest finishes last and runs alone, with few loads in flight; a
-// wave that gets ahead now yields to the ones behind it at each quarter.
-__device__ __forceinline__ void split_priority(int it, int groups) {
-  const int qtr = (4 * it) / groups;   // uniform
-  if (qtr == 0) __builtin_amdgcn_s_setprio(3);
-  else if (qtr == 1) __builtin_amdgcn_s_setprio(2);
-  else if (qtr == 2) __builtin_amdgcn_s_setprio(1);
+// Issue priority of a wave by how far through its split's page groups it
+// is: 3 in the first half, 2 to three quarters, 1 to seven eighths, 0 in
+// the last eighth.  Waves sharing a SIMD otherwise issue oldest first, so of
+// three equal splits started together the youngest finishes last and runs
+// alone, with few loads in flight; a wave that gets ahead now yields to the
+// ones behind it at each step, and the steps are closest together at the
+// end, where the spread left over is what the launch waits for.
+__device__ __forceinline__ void split_priority(int it, int groups) {   // uniform arguments
+  if (2 * it < groups) __builtin_amdgcn_s_setprio(3);
+  else if (4 * it < 3 * groups) __builtin_amdgcn_s_setprio(2);
+  else if (8 * it < 7 * groups) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
